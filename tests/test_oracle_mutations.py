@@ -1,0 +1,90 @@
+"""Plant plausible mistakes in a private copy of the oracle (CPU only) and check that the
+pins catch each one.  The copy is built from the oracle's source text with one edit; the
+real oracle module is never modified.
+"""
+import json
+import os
+import types
+
+import numpy as np
+import pytest
+
+from oracle import q4_oracle
+from synth import f64_to_bf16_bits
+
+SRC = open(q4_oracle.__file__).read()
+
+MUTATIONS = {
+    "scale denominator 16": ("dt(q_max - q_min)", "dt(q_max - q_min + 1)"),
+    "alpha not extended to 0": ("np.minimum(x.min(axis=-1), dt(0))", "x.min(axis=-1)"),
+    "zero-point sign": ("np.rint(dt(q_min) - ratio)", "np.rint(dt(q_min) + ratio)"),
+    "round after adding z": ("r = np.clip(np.rint(quot), dt(-2.0 ** 40), dt(2.0 ** 40)).astype(np.int64)\n    q = np.clip(r + z[..., None], q_min, q_max)",
+                             "q = np.clip(np.rint(quot + z[..., None]).astype(np.int64), q_min, q_max)"),
+    "no fp16 scale rounding": ("s = s16.astype(dt)", "s = np.minimum(scale.astype(np.float32), F16_MAX).astype(dt)"),
+    "nibble order swapped": ("(nib[:, 0::2] | (nib[:, 1::2] << 4))", "(nib[:, 1::2] | (nib[:, 0::2] << 4))"),
+    "unpack order swapped": ("codes[:, 0::2] = p & 0xF\n    codes[:, 1::2] = p >> 4",
+                             "codes[:, 1::2] = p & 0xF\n    codes[:, 0::2] = p >> 4"),
+    "sign extension off by one": ("codes - 16", "codes - 15"),
+    "dequant adds z": ("(qg - z[..., None])", "(qg + z[..., None])"),
+    "symmetric q_max 8": ('quantize_groups(x, -8, 7, "sym")', 'quantize_groups(x, -8, 8, "sym")'),
+    "group index off": ("s[..., None] * (qg - z[..., None])", "np.roll(s, 1, axis=-1)[..., None] * (qg - z[..., None])"),
+    "abs dropped in A": ("np.abs(X) @ np.abs(What).T", "X @ What.T"),
+}
+
+
+def _mutant(old, new):
+    assert SRC.count(old) == 1, old
+    mod = types.ModuleType("q4_oracle_mutant")
+    exec(compile(SRC.replace(old, new), "q4_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_pass(orc, golden_dir):
+    """The pins of test_oracle_pins / test_oracle_props in compact form; True if all hold."""
+    from tests.test_oracle_props import exact_group
+    try:
+        ex_all = json.load(open(os.path.join(golden_dir, "hand_examples.json")))
+        for mode in ("asym", "sym"):
+            ex = ex_all[mode]
+            W_bits = f64_to_bf16_bits(np.array([ex["x"]]))
+            packed, scales, zeros = orc.quantize_rtn_ref(W_bits, g=8, mode=mode)
+            if float(scales[0, 0]) != ex["scale"] or int(zeros[0, 0]) != ex["zero"]:
+                return False
+            if [f"0x{b:02X}" for b in packed[0]] != ex["packed_hex"]:
+                return False
+            if orc.unpack_codes_ref(packed, mode)[0].tolist() != ex["codes"]:
+                return False
+            if orc.dequantize_ref(packed, scales, zeros, 8, mode)[0].tolist() != ex["xhat"]:
+                return False
+        rng = np.random.default_rng(0)
+        groups = np.concatenate([rng.normal(0, 0.02, (48, 32)), np.abs(rng.normal(0, 1, (16, 32))) + 0.5])
+        for mode in ("asym", "sym"):
+            x = orc.bf16_bits_to_f32(f64_to_bf16_bits(groups))
+            qmin, qmax = (0, 15) if mode == "asym" else (-8, 7)
+            q, s16, z = orc.quantize_groups(x, qmin, qmax, mode)
+            for i in range(len(x)):
+                es, ez, eq = exact_group(x[i], mode)
+                if float(s16[i]) != float(es) or int(z[i]) != ez or q[i].tolist() != eq:
+                    return False
+        W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (4, 64)))
+        for mode in ("asym", "sym"):
+            packed, scales, zeros = orc.quantize_rtn_ref(W_bits, g=32, mode=mode)
+            Y, A = orc.matmul_ref(f64_to_bf16_bits(np.eye(64)), packed, scales, zeros, 32, mode)
+            if not np.array_equal(A, np.abs(Y)):
+                return False
+            x = orc.bf16_bits_to_f32(W_bits).astype(np.float64)
+            if np.abs(Y.T - x).max() > 0.6 * np.abs(x).max() / 7 + 1e-12:
+                return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unmutated_oracle_passes(golden_dir):
+    assert _pins_pass(q4_oracle, golden_dir)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, golden_dir):
+    old, new = MUTATIONS[name]
+    assert not _pins_pass(_mutant(old, new), golden_dir), f"pins missed: {name}"
