@@ -1,0 +1,137 @@
+/*
+ * q4.h — group-wise affine INT4 weight quantization (round to nearest) and the W4A16 matmul
+ * that consumes it, for AMD MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What is computed
+ * ----------------
+ * Quantization follows "DL S067 · Quantization — INT8, INT4, GPTQ, AWQ", §1 "The core math"
+ * (asymmetric: scale = (beta - alpha) / (q_max - q_min), z = round(q_min - alpha / scale),
+ * q = clip(round(x / scale) + z, q_min, q_max); symmetric: zero-point dropped and
+ * scale = max|x| / q_max) applied per group of g consecutive weights along K within each
+ * output row ("Model Quantization" §1 "Group-wise Quantization"; "DL S067" §2).  The matmul
+ * is W4A16 in the sense of "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 &
+ * INT4/INT8 Trade-offs", "The vocabulary": the 4-bit weights are dequantised inside the
+ * kernel and the product runs on 16-bit operands.
+ *
+ * Exact rules (the pages leave these open; this library fixes them):
+ *   - W is widened to fp32 (exact).  alpha = min(group, 0), beta = max(group, 0).
+ *   - asymmetric: codes in [0, 15], s32 = fl32(fl32(beta - alpha) / 15);
+ *     symmetric:  codes in [-8, 7],  s32 = fl32(max|x| / 7), z = 0.
+ *   - scale = fp16_rne(min(s32, 65504)); a scale that rounds to 0 is stored as 1.0.
+ *   - z = clamp(rint(-alpha / scale), 0, 15); q = clamp(rint(x / scale) + z, q_min, q_max),
+ *     rint = round half to even of the exact quotient (equal to rint of the IEEE fp32
+ *     quotient for every bf16 x and fp16 scale).
+ *   - dequantised weight: scale * (q - z).  Y = X * dequant(W)^T, fp32 accumulation,
+ *     Y rounded to bf16 (round to nearest even).
+ * NaN or Inf inputs are outside the method's domain: outputs are then unspecified.
+ *
+ * Layouts (all row-major, contiguous, little-endian)
+ *   W       bf16  [N, K]      weights, N output features, K input features
+ *   packed  uint8 [N, K/2]    codes, two per byte, even k in the low nibble; symmetric codes
+ *                             are 4-bit two's complement
+ *   scales  fp16  [N, K/g]
+ *   zeros   uint8 [N, K/g]    0 in symmetric mode
+ *   X       bf16  [M, K]      activations
+ *   Y       bf16  [M, N]
+ *
+ * Ownership, streams, errors
+ *   - Every pointer is device memory allocated by the caller.  The library never allocates,
+ *     frees or retains memory, and keeps no per-call state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and the
+ *     call returns without synchronizing.  Kernel faults surface at the caller's next
+ *     synchronization, as usual in HIP.  Calls are thread-safe.
+ *   - Arguments are validated before anything is enqueued; on error a negative status is
+ *     returned and nothing is launched.  A launch failure reported by the HIP runtime
+ *     returns Q4_ERR_HIP.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_VERSION 10000  /* 1.0.0 */
+
+typedef enum {
+    Q4_ASYM = 0,   /* uint4 codes [0, 15] with a uint8 zero-point per group */
+    Q4_SYM = 1     /* int4 codes [-8, 7], zero-point 0                      */
+} q4_mode_t;
+
+typedef enum {
+    Q4_KERNEL_AUTO = 0,   /* choose by M, N, K (see q4_select_kernel)                        */
+    Q4_KERNEL_GEMV = 1,   /* decode GEMV: fp32 dot products over exact 16-bit codes, M <= 2  */
+    Q4_KERNEL_GEMM = 2    /* bf16 MFMA GEMM on dequantised tiles, any M                       */
+} q4_kernel_t;
+
+enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = -1,      /* a required pointer is NULL                                    */
+    Q4_ERR_SHAPE = -2,     /* N < 1, K < 1, M < 0, or a size beyond 2^31 - 1                */
+    Q4_ERR_GROUP = -3,     /* g < 32, g % 32 != 0, or K % g != 0                             */
+    Q4_ERR_MODE = -4,      /* mode or kernel selector out of range                           */
+    Q4_ERR_ALIGN = -5,     /* W, X or packed not 16-byte aligned; scales or Y not 2-byte     */
+    Q4_ERR_HIP = -6,       /* the HIP runtime rejected a launch                              */
+    Q4_ERR_ALIAS = -7,     /* an output buffer overlaps an input or another output          */
+    Q4_ERR_UNSUPPORTED = -8 /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
+};
+
+/*
+ * Quantize W[N, K] (bf16) group-wise with round to nearest.
+ * Source: "DL S067 · Quantization — INT8, INT4, GPTQ, AWQ", §1 (formulas) and §2 (groups).
+ *
+ *   W       device, bf16 [N, K], 16-byte aligned
+ *   N, K    1 <= N, K <= 2^31 - 1
+ *   g       group size: multiple of 32, K % g == 0 (g = K gives one group per row)
+ *   mode    Q4_ASYM or Q4_SYM
+ *   packed  device, uint8 [N, K/2], 16-byte aligned (output)
+ *   scales  device, fp16  [N, K/g], 2-byte aligned (output)
+ *   zeros   device, uint8 [N, K/g] (output; all 0 in symmetric mode)
+ *   stream  hipStream_t or NULL
+ * Returns Q4_OK or a negative status.  Outputs are bit-exact with the rules above.
+ */
+int q4_quantize_rtn(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode,
+                    void* packed, void* scales, void* zeros, void* stream);
+
+/*
+ * Y[M, N] = X[M, K] * dequant(packed, scales, zeros)^T, bf16 out, fp32 accumulation.
+ * Source: W4A16 as defined in "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 &
+ * INT4/INT8 Trade-offs", "The vocabulary"; dequantisation x_hat = scale * (q - z) from
+ * "DL S067 · Quantization", §1.
+ *
+ *   X       device, bf16 [M, K], 16-byte aligned (may be NULL only when M == 0)
+ *   M       0 <= M <= 2^31 - 1 (M == 0 returns Q4_OK and launches nothing)
+ *   N, K, g, mode   as for q4_quantize_rtn; they must describe packed/scales/zeros
+ *   packed, scales  device inputs as produced by q4_quantize_rtn
+ *   zeros   device input; ignored and may be NULL in symmetric mode
+ *   Y       device, bf16 [M, N], 2-byte aligned (output; must not overlap any input)
+ * Accuracy: |Y - Y_exact| <= 8e-3 * sum_k |X[m,k] * x_hat[n,k]| + 1e-6 per element, where
+ * Y_exact is the fp64 product with the dequantised weights.
+ */
+int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+              const void* packed, const void* scales, const void* zeros, void* Y, void* stream);
+
+/* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
+ * M == 1 and K <= 16384, or M == 2 and K <= 4096, else Q4_ERR_UNSUPPORTED.  Both kernels satisfy the same
+ * accuracy bound; callers use this to pin a kernel. */
+int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+                     const void* packed, const void* scales, const void* zeros, void* Y,
+                     int32_t kernel, void* stream);
+
+/* The kernel Q4_KERNEL_AUTO picks for this shape (Q4_KERNEL_GEMV or Q4_KERNEL_GEMM), or a
+ * negative status for an invalid shape.  Pure host function, no HIP call. */
+int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* q4_status_string(int status);
+
+/* Q4_VERSION of the built library. */
+int q4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

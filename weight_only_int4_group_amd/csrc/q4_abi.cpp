@@ -1,0 +1,144 @@
+// C ABI of the q4 library: argument validation (no HIP call before it passes), kernel
+// selection and launch on the caller's stream.  See include/q4.h for the contract.
+#include "../../include/q4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "q4_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(int64_t N, int64_t K, int32_t g, int32_t mode) {
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return Q4_ERR_SHAPE;
+  if (g < 32 || g % 32 != 0 || K % g != 0) return Q4_ERR_GROUP;
+  if (mode != Q4_ASYM && mode != Q4_SYM) return Q4_ERR_MODE;
+  return Q4_OK;
+}
+
+// Compute units of the current device, cached per device id.
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool gemv_fits(int64_t M, int64_t K) {
+  return (M == 1 && K <= q4::kGemvMaxK) || (M == 2 && K <= q4::kGemvMaxK2);
+}
+
+int validate_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+                    const void* packed, const void* scales, const void* zeros, const void* Y) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (M < 0 || M > kMaxDim) return Q4_ERR_SHAPE;
+  if (M == 0) return Q4_OK;
+  if (!X || !packed || !scales || !Y || (mode == Q4_ASYM && !zeros)) return Q4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(Y, 2))
+    return Q4_ERR_ALIGN;
+  const int64_t G = K / g;
+  const Range y = range_of(Y, M * N * 2);
+  if (overlap(y, range_of(X, M * K * 2)) || overlap(y, range_of(packed, N * K / 2)) ||
+      overlap(y, range_of(scales, N * G * 2)) ||
+      (mode == Q4_ASYM && overlap(y, range_of(zeros, N * G))))
+    return Q4_ERR_ALIAS;
+  return Q4_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int q4_version(void) { return Q4_VERSION; }
+
+const char* q4_status_string(int status) {
+  switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "invalid shape: need N >= 1, K >= 1, M >= 0, all <= 2^31-1";
+    case Q4_ERR_GROUP: return "invalid group size: need g >= 32, g % 32 == 0 and K % g == 0";
+    case Q4_ERR_MODE: return "invalid mode or kernel selector";
+    case Q4_ERR_ALIGN: return "misaligned pointer: W, X, packed need 16 bytes; scales, Y need 2";
+    case Q4_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case Q4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case Q4_ERR_UNSUPPORTED: return "the chosen kernel does not support this shape";
+    default: return "unknown status";
+  }
+}
+
+int q4_quantize_rtn(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, void* packed,
+                    void* scales, void* zeros, void* stream) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (!W || !packed || !scales || !zeros) return Q4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return Q4_ERR_ALIGN;
+  const int64_t G = K / g;
+  const Range w = range_of(W, N * K * 2), p = range_of(packed, N * K / 2),
+              s = range_of(scales, N * G * 2), z = range_of(zeros, N * G);
+  if (overlap(w, p) || overlap(w, s) || overlap(w, z) || overlap(p, s) || overlap(p, z) ||
+      overlap(s, z))
+    return Q4_ERR_ALIAS;
+  return finish(q4::launch_quantize(W, N, K, g, mode == Q4_SYM, packed, scales, zeros, num_cus(),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
+  int st = check_shape(N, K, g, Q4_ASYM);
+  if (st != Q4_OK) return st;
+  if (M < 0 || M > kMaxDim) return Q4_ERR_SHAPE;
+  return gemv_fits(M, K) ? Q4_KERNEL_GEMV : Q4_KERNEL_GEMM;
+}
+
+int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+                     const void* packed, const void* scales, const void* zeros, void* Y,
+                     int32_t kernel, void* stream) {
+  if (kernel != Q4_KERNEL_AUTO && kernel != Q4_KERNEL_GEMV && kernel != Q4_KERNEL_GEMM)
+    return Q4_ERR_MODE;
+  int st = validate_matmul(X, M, N, K, g, mode, packed, scales, zeros, Y);
+  if (st != Q4_OK) return st;
+  if (M == 0) return Q4_OK;
+  if (kernel == Q4_KERNEL_AUTO) kernel = gemv_fits(M, K) ? Q4_KERNEL_GEMV : Q4_KERNEL_GEMM;
+  if (kernel == Q4_KERNEL_GEMV && !gemv_fits(M, K)) return Q4_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool sym = mode == Q4_SYM;
+  if (kernel == Q4_KERNEL_GEMV)
+    return finish(q4::launch_gemv(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+  return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+}
+
+int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+              const void* packed, const void* scales, const void* zeros, void* Y, void* stream) {
+  return q4_matmul_kernel(X, M, N, K, g, mode, packed, scales, zeros, Y, Q4_KERNEL_AUTO, stream);
+}
+
+}  // extern "C"

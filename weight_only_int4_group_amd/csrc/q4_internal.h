@@ -1,0 +1,25 @@
+// Kernel launchers behind the C ABI.  Arguments are already validated by q4_abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
+                           void* scales, void* zeros, int num_cus, hipStream_t stream);
+
+// Decode GEMV: M == 1 with K <= kGemvMaxK, or M == 2 with K <= kGemvMaxK2 (the lane's slice
+// of X stays in registers).
+constexpr int64_t kGemvMaxK = 16384;
+constexpr int64_t kGemvMaxK2 = 4096;
+hipError_t launch_gemv(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
+                       const void* packed, const void* scales, const void* zeros, void* Y,
+                       int num_cus, hipStream_t stream);
+
+// MFMA GEMM for any M >= 1.
+hipError_t launch_gemm(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
+                       const void* packed, const void* scales, const void* zeros, void* Y,
+                       int num_cus, hipStream_t stream);
+
+}  // namespace q4

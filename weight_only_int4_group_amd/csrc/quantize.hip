@@ -1,0 +1,251 @@
+// Group-wise INT4 round-to-nearest quantization and nibble packing (gfx950).
+//
+// Method: "DL S067 · Quantization — INT8, INT4, GPTQ, AWQ", §1 "The core math" (asymmetric
+// scale (beta - alpha) / (q_max - q_min), z = round(q_min - alpha / scale),
+// q = clip(round(x / scale) + z); symmetric scale max|x| / q_max), applied per group of g
+// consecutive weights along K ("DL S067" §2; "Model Quantization" §1 "Group-wise
+// Quantization").  The exact rules (fp32 arithmetic, fp16 scale, round half to even,
+// alpha/beta extended to include 0, nibble order) are those stated in include/q4.h.
+//
+// Bit-exactness without an IEEE divide per element.  For a bf16 x and an fp16 scale s the
+// exact quotient x / s is either exactly a half-integer or at least 2^-12 away from one, so
+// rint of the IEEE fp32 quotient equals rint of the exact quotient.  Each code is therefore
+// computed as t = x * r (r ~ 1/s), one residual correction t' = t + fl(x - t s) * r (two
+// fmas), and rint(t'): the corrected value is within 2^-40 of x / s, equals it exactly at
+// ties, and never crosses a half-integer the exact quotient does not cross.
+//
+// The per-group scale needs the IEEE quotient itself: fl32(d / 15) (or d / 7) is computed
+// as q0 = d * RN(1/15), r = fma(-q0, 15, d) (exact), fl = fma(r, RN(1/15), q0).  A quotient
+// by 15 or 7 is never a rounding midpoint and stays at least ulp/30 from one, while the
+// sequence is within 2^-24 ulp of it, so the rounding is the IEEE one.
+//
+// Layout: the weight matrix is processed as a flat array of 8-element chunks (16 bytes of
+// bf16 -> 4 bytes of nibbles).  Groups never straddle rows (K % g == 0), so the flat group
+// index is also the index into scales[N, K/g] and zeros[N, K/g].
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+struct GroupParams {
+  float sf;       // fp32 value of the stored fp16 scale
+  float rcp;      // ~1/sf (any value within 2^-22 relative works, see above)
+  float zf;       // zero-point as float (0 in symmetric mode)
+  uint16_t s16;   // stored scale bits
+};
+
+// alpha <= 0 <= beta already; returns the stored scale, its reciprocal and the zero-point.
+template <bool SYM>
+__device__ __forceinline__ GroupParams group_params(float alpha, float beta_or_absmax) {
+  float d, c, k;
+  if (SYM) {
+    d = fminf(beta_or_absmax, 1.0e6f);       // >= 65504 * 7 saturates either way
+    k = 7.0f;
+    c = 1.0f / 7.0f;
+  } else {
+    d = fminf(beta_or_absmax - alpha, 2.0e6f);   // one IEEE subtraction; cap keeps it finite
+    k = 15.0f;
+    c = 1.0f / 15.0f;
+  }
+  const float q0 = d * c;
+  const float r = __builtin_fmaf(-q0, k, d);
+  float s32 = __builtin_fmaf(r, c, q0);          // == fl32(d / k)
+  s32 = fminf(s32, 65504.0f);
+  _Float16 h = (_Float16)s32;                    // round to nearest even
+  if (h == (_Float16)0.0f) h = (_Float16)1.0f;
+  GroupParams p;
+  p.sf = (float)h;
+  p.s16 = __builtin_bit_cast(uint16_t, h);
+  p.rcp = __builtin_amdgcn_rcpf(p.sf);
+  if (SYM) {
+    p.zf = 0.0f;
+  } else {
+    const float t = alpha * p.rcp;
+    const float res = __builtin_fmaf(-t, p.sf, alpha);
+    const float tq = __builtin_fmaf(res, p.rcp, t);          // ~ alpha / s
+    p.zf = fminf(fmaxf(-rintf(tq), 0.0f), 15.0f);           // rint(0 - alpha/s), clamped
+  }
+  return p;
+}
+
+template <bool SYM>
+__device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
+  const float t = x * p.rcp;
+  const float res = __builtin_fmaf(-t, p.sf, x);
+  const float tq = __builtin_fmaf(res, p.rcp, t);            // ~ x / s
+  const float c = rintf(tq);
+  if (SYM) {
+    const float v = fminf(fmaxf(c, -8.0f), 7.0f);
+    return (uint32_t)(int)v & 0xFu;                           // 4-bit two's complement
+  } else {
+    const float v = fminf(fmaxf(c + p.zf, 0.0f), 15.0f);
+    return (uint32_t)v;
+  }
+}
+
+// Unpack a 16-byte chunk of 8 bf16 values.
+__device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(v[i]);
+    x[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
+
+template <bool SYM>
+__device__ __forceinline__ uint32_t pack8(const float x[8], const GroupParams& p) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= code_of<SYM>(x[i], p) << (4 * i);
+  return w;
+}
+
+template <int L>
+__device__ __forceinline__ float lanes_min(float v) {
+#pragma unroll
+  for (int o = 1; o < L; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float lanes_max(float v) {
+#pragma unroll
+  for (int o = 1; o < L; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// g in {32, 64, 128, 256, 512}: a group is L = g/8 consecutive lanes, each holding one chunk.
+// A wave covers 64 consecutive chunks (512 weights) per step; U steps are loaded together.
+template <int L, bool SYM, int U>
+__global__ __launch_bounds__(256) void quantize_lanes_kernel(
+    const u32x4* __restrict__ W, int64_t nchunks, uint32_t* __restrict__ packed,
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) / kWave;
+  for (int64_t base = wave * U; base * kWave < nchunks; base += nwaves * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = (base + u) * kWave + lane;
+      v[u] = c < nchunks ? __builtin_nontemporal_load(W + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = (base + u) * kWave + lane;
+      float x[8];
+      unpack8(v[u], x);
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (SYM) {
+          hi = fmaxf(hi, fabsf(x[i]));
+        } else {
+          lo = fminf(lo, x[i]);
+          hi = fmaxf(hi, x[i]);
+        }
+      }
+      if (!SYM) lo = lanes_min<L>(lo);
+      hi = lanes_max<L>(hi);
+      const GroupParams p = group_params<SYM>(lo, hi);
+      const uint32_t w = pack8<SYM>(x, p);
+      if (c < nchunks) {
+        packed[c] = w;
+        if ((lane & (L - 1)) == 0) {
+          const int64_t grp = c / L;
+          scales[grp] = p.s16;
+          zeros[grp] = (uint8_t)p.zf;
+        }
+      }
+    }
+  }
+}
+
+// Any g (multiple of 32): one wave per group, two passes over the group's chunks
+// (range, then codes); the second pass re-reads the group, normally from cache.
+template <bool SYM>
+__global__ __launch_bounds__(256) void quantize_wave_kernel(
+    const u32x4* __restrict__ W, int64_t ngroups, int cpg, uint32_t* __restrict__ packed,
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) / kWave;
+  for (int64_t grp = wave; grp < ngroups; grp += nwaves) {
+    const int64_t c0 = grp * cpg;
+    float lo = 0.0f, hi = 0.0f;
+    for (int j = lane; j < cpg; j += kWave) {
+      float x[8];
+      unpack8(W[c0 + j], x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (SYM) {
+          hi = fmaxf(hi, fabsf(x[i]));
+        } else {
+          lo = fminf(lo, x[i]);
+          hi = fmaxf(hi, x[i]);
+        }
+      }
+    }
+    if (!SYM) lo = lanes_min<kWave>(lo);
+    hi = lanes_max<kWave>(hi);
+    const GroupParams p = group_params<SYM>(lo, hi);
+    for (int j = lane; j < cpg; j += kWave) {
+      float x[8];
+      unpack8(W[c0 + j], x);
+      packed[c0 + j] = pack8<SYM>(x, p);
+    }
+    if (lane == 0) {
+      scales[grp] = p.s16;
+      zeros[grp] = (uint8_t)p.zf;
+    }
+  }
+}
+
+template <int L, bool SYM>
+hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scales, void* zeros,
+                        int num_cus, hipStream_t stream) {
+  constexpr int U = 4;
+  const int64_t steps = (nchunks + kWave * U - 1) / (kWave * U);   // wave-steps needed
+  const int64_t waves_wanted = steps;
+  int64_t blocks = (waves_wanted + 3) / 4;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((quantize_lanes_kernel<L, SYM, U>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, (const u32x4*)W, nchunks, (uint32_t*)packed, (uint16_t*)scales,
+                     (uint8_t*)zeros);
+  return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed, void* scales,
+                       void* zeros, int num_cus, hipStream_t stream) {
+  const int64_t nchunks = N * K / 8;
+  switch (g) {
+    case 32: return launch_lanes<4, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    case 64: return launch_lanes<8, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    case 128: return launch_lanes<16, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    case 256: return launch_lanes<32, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    case 512: return launch_lanes<64, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    default: {
+      const int64_t ngroups = N * (K / g);
+      int64_t blocks = (ngroups + 3) / 4;
+      const int64_t cap = (int64_t)num_cus * 8;
+      if (blocks > cap) blocks = cap;
+      hipLaunchKernelGGL((quantize_wave_kernel<SYM>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const u32x4*)W, ngroups, g / 8, (uint32_t*)packed, (uint16_t*)scales,
+                         (uint8_t*)zeros);
+      return hipGetLastError();
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
+                           void* scales, void* zeros, int num_cus, hipStream_t stream) {
+  return sym ? launch_mode<true>(W, N, K, g, packed, scales, zeros, num_cus, stream)
+             : launch_mode<false>(W, N, K, g, packed, scales, zeros, num_cus, stream);
+}
+
+}  // namespace q4
