@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+One step is one pass of the whole path over synthetic inputs resident in HBM:
+  1. quantize  -- group-wise INT4 RTN of the 70B-shaped MLP weight W[28672, 8192] (asym, g=128)
+  2. decode    -- W4A16 GEMV, M = 1, through L layers of that shape (L distinct quantized weight
+                  copies, 6 by default, 740 MB in total, so the 256 MB Infinity Cache cannot
+                  serve the weights); the copy quantized in step 1 is read last
+  3. prefill   -- W4A16 GEMM, M = 2048, W[8192, 8192] (asym, g=128 and g=32)
+The headline value is the decode GEMV's HBM throughput: algorithmic bytes (packed codes +
+fp16 scales + uint8 zeros + X + Y) per launch / measured launch time, HIP events on the
+launch stream.  Parity against the CPU oracle is asserted on sampled outputs before timing.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR   (writes the traffic summary)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; GEMM TFLOP/s at M=2048"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_70b_mlp_m1_traffic.md")
+GEMV_SRC = os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", "gemv.hip")
+
+
+def weight_bytes(N, K, g, mode):
+    G = K // g
+    return N * K // 2 + 2 * N * G + (N * G if mode == "asym" else 0)
+
+
+def matmul_bytes(M, N, K, g, mode):
+    return weight_bytes(N, K, g, mode) + 2 * M * K + 2 * M * N
+
+
+def quantize_bytes(N, K, g):
+    return 2 * N * K + N * K // 2 + 3 * N * (K // g)
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Traffic per GEMV launch from the committed counter summary, if it matches the source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    try:
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        d = json.loads(blob)
+    except (IndexError, ValueError):
+        return None
+    if d.get("gemv_src_sha") != src_sha(GEMV_SRC):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--layers", type=int, default=6, help="distinct decode weight copies per step")
+    p.add_argument("--no-check", action="store_true", help="skip the parity assertion")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also launch one plain 512 MiB device copy (counter calibration)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    return p.parse_args(argv)
+
+
+# --------------------------------------------------------------------------- counters
+def _counter_rows(d):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMV, scaled by a plain copy's."""
+    def per_kernel(d, counter):
+        out = {}
+        for r in _counter_rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+        return out
+
+    def pick(d, key):
+        hits = [v for k, v in d.items() if key(k)]
+        if not hits:
+            return None
+        vals = [x for h in hits for x in h]
+        return sum(vals) / len(vals), len(vals)
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    is_gemv = lambda k: "gemv_kernel" in k
+    is_copy = lambda k: ("copy" in k.lower() or "elementwise" in k.lower()) and "q4" not in k
+    gf, gw, cf, cw = pick(fetch, is_gemv), pick(write, is_gemv), pick(fetch, is_copy), pick(write, is_copy)
+    copy_bytes = 512 * 2 ** 20
+    res = {
+        "gemv_src_sha": src_sha(GEMV_SRC),
+        "gemv_fetch_kib_per_dispatch": gf[0] if gf else None,
+        "gemv_write_kib_per_dispatch": gw[0] if gw else None,
+        "gemv_dispatches": gf[1] if gf else 0,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf[0] if cf else None,
+        "copy_write_kib": cw[0] if cw else None,
+    }
+    if gf and gw and cf and cw:
+        ff = copy_bytes / (cf[0] * 1024)
+        fw = copy_bytes / (cw[0] * 1024)
+        res["copy_factor_fetch"] = ff
+        res["copy_factor_write"] = fw
+        res["traffic_bytes_per_launch"] = gf[0] * 1024 * ff + gw[0] * 1024 * fw
+    else:
+        res["traffic_bytes_per_launch"] = None
+    return res
+
+
+# --------------------------------------------------------------------------- workload
+def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, block=4096):
+    """The CPU oracle's W4A16 matmul (M=1), over row blocks of the 70B-shaped layer.
+
+    The oracle quantizes each block first (not timed); matmul_ref is then timed over the
+    blocks, cycling through the layer until about budget_s seconds of CPU work are spent.
+    """
+    import numpy as np
+    from oracle import q4_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    N, K = W_bits.shape
+    blocks = [orc.quantize_rtn_ref(W_bits[r:r + block], g, mode) for r in range(0, N, block)]
+    done_rows, spent, passes = 0, 0.0, 0
+    while spent < budget_s:
+        for p, s, z in blocks:
+            t = time.perf_counter()
+            orc.matmul_ref(X_bits, p, s, z, g, mode)
+            spent += time.perf_counter() - t
+            done_rows += p.shape[0]
+        passes += 1
+    nbytes = matmul_bytes(X_bits.shape[0], done_rows, K, g, mode)
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle matmul_ref (fp64 dequantisation + BLAS), M=1, the whole {N}x{K} "
+                      f"layer in row blocks of {block}, {passes} passes, {spent:.1f} s"}
+
+
+def check_parity(q4, torch, W4_bits, X4_bits, sets, Y4, W5_bits, X5_host, X5_dev, w5, Y5):
+    """Sampled parity of every timed kernel against the oracle (asserts)."""
+    import numpy as np
+    from oracle import q4_oracle as orc
+    rng = np.random.default_rng(7)
+    # quantize: sampled rows bit-exact
+    rows = np.sort(rng.choice(W4_bits.shape[0], 256, replace=False))
+    rp, rs, rz = orc.quantize_rtn_ref(W4_bits[rows], 128, "asym")
+    p, s, z = sets[0]
+    assert np.array_equal(p[rows].cpu().numpy(), rp), "quantize: packed differs"
+    assert np.array_equal(s[rows].cpu().view(torch.int16).numpy().view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(z[rows].cpu().numpy(), rz), "quantize: zeros differ"
+    # decode GEMV on copy 0 (bit-identical to the oracle's weights on the sampled rows)
+    q4.matmul_into(torch.from_numpy(X4_bits.view(np.int16)).view(torch.bfloat16).cuda(), p, s, z,
+                   128, "asym", Y4)
+    torch.cuda.synchronize()
+    Y = Y4.float().cpu().numpy().astype(np.float64)
+    Yr, A = orc.matmul_ref(X4_bits, rp, rs, rz, 128, "asym")
+    ok, u1 = orc.check_matmul(Y[:, rows], Yr, A)
+    assert ok, f"GEMV outside tolerance (usage {u1})"
+    # GEMM: sampled entries, weights re-quantized by the oracle on the sampled rows
+    usages = [u1]
+    for g, (p5, s5, z5) in w5.items():
+        q4.matmul_into(X5_dev, p5, s5, z5, g, "asym", Y5)
+        torch.cuda.synchronize()
+        n_idx = np.sort(rng.choice(W5_bits.shape[0], 64, replace=False))
+        m_idx = rng.choice(X5_host.shape[0], 64, replace=False)
+        rp5, rs5, rz5 = orc.quantize_rtn_ref(W5_bits[n_idx], g, "asym")
+        assert np.array_equal(p5[n_idx].cpu().numpy(), rp5)
+        Yr5, A5 = orc.matmul_ref(X5_host[m_idx], rp5, rs5, rz5, g, "asym")
+        Yg = Y5[m_idx][:, n_idx].float().cpu().numpy().astype(np.float64)
+        ok, u = orc.check_matmul(Yg, Yr5, A5)
+        assert ok, f"GEMM g={g} outside tolerance (usage {u})"
+        usages.append(u)
+    return max(usages)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters)
+        print(json.dumps(res, indent=1))
+        return 0
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path is single-GPU; sharding is "
+              "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import weight_only_int4_group_amd as q4
+    from synth import CONFIGS, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    c4, c5 = CONFIGS[3], CONFIGS[4]
+    N4, K4, g4 = c4.N, c4.K, c4.g
+    W4_bits, X4_bits = make_layer(c4, M=1)
+    W5_bits, X5_bits = make_layer(c5)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    W4, X4 = up(W4_bits), up(X4_bits)
+    W5, X5 = up(W5_bits), up(X5_bits)
+    G4 = K4 // g4
+    L = args.layers
+    sets = [(torch.empty((N4, K4 // 2), dtype=torch.uint8, device=dev),
+             torch.empty((N4, G4), dtype=torch.float16, device=dev),
+             torch.empty((N4, G4), dtype=torch.uint8, device=dev)) for _ in range(L)]
+    for s in sets:
+        q4.quantize_rtn_into(W4, g4, "asym", *s)
+    w5 = {g: q4.quantize_rtn(W5, g, "asym") for g in (128, 32)}
+    Y4 = torch.empty((1, N4), dtype=torch.bfloat16, device=dev)
+    Y5 = torch.empty((X5.shape[0], c5.N), dtype=torch.bfloat16, device=dev)
+    copy_src = copy_dst = None
+    if args.copy_calibration:
+        copy_src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        copy_dst = torch.empty_like(copy_src)
+    torch.cuda.synchronize()
+
+    max_usage = None
+    if not args.no_check:
+        max_usage = check_parity(q4, torch, W4_bits, X4_bits, sets, Y4, W5_bits, X5_bits, X5, w5, Y5)
+
+    n_ev = 5
+    def step(t, ev):
+        ev[0].record()
+        q4.quantize_rtn_into(W4, g4, "asym", *sets[t % L])
+        ev[1].record()
+        for i in range(L):
+            p, s, z = sets[(t + 1 + i) % L]
+            q4.matmul_into(X4, p, s, z, g4, "asym", Y4)
+        ev[2].record()
+        q4.matmul_into(X5, *w5[128], 128, "asym", Y5)
+        ev[3].record()
+        q4.matmul_into(X5, *w5[32], 32, "asym", Y5)
+        ev[4].record()
+
+    warm = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(max(args.warmup, 0))]
+    for t in range(args.warmup):
+        step(t, warm[t])
+    if copy_dst is not None:
+        copy_dst.copy_(copy_src)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        step(args.warmup + t, evs[t])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def mean_ms(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs)
+
+    q_ms = mean_ms(0, 1)
+    gemv_ms = mean_ms(1, 2) / L
+    g128_ms = mean_ms(2, 3)
+    g32_ms = mean_ms(3, 4)
+
+    gemv_bytes = matmul_bytes(1, N4, K4, g4, "asym")
+    gemv_gbs = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    flops = 2.0 * X5.shape[0] * c5.N * c5.K
+    g128_tf = flops / (g128_ms * 1e-3) / 1e12
+    g32_tf = flops / (g32_ms * 1e-3) / 1e12
+    q_bytes = quantize_bytes(N4, K4, g4)
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"70B-shaped MLP decode: W4A16 GEMV M=1, W[{N4},{K4}] asym g={g4}, "
+                         f"{L} weight copies per step; plus RTN quantize of that W and prefill "
+                         f"GEMM M={X5.shape[0]} W[{c5.N},{c5.K}] g=128 and g=32"),
+            "M": 1, "N": N4, "K": K4, "g": g4, "mode": "asym", "layers_per_step": L,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "kernel": "gemv_kernel", "bytes_per_launch": gemv_bytes,
+            "ms_per_launch": round(gemv_ms, 5),
+        },
+        "gemm": {
+            "M": int(X5.shape[0]), "N": c5.N, "K": c5.K,
+            "g128": {"tflops": round(g128_tf, 2), "ms": round(g128_ms, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(g128_tf, 2),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(g128_tf / BF16_PEAK_TFLOPS, 4)}},
+            "g32": {"tflops": round(g32_tf, 2), "ms": round(g32_ms, 4),
+                    "roofline": {"bound": "mfma", "achieved": round(g32_tf, 2),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(g32_tf / BF16_PEAK_TFLOPS, 4)}},
+        },
+        "quantize": {"GB/s": round(q_gbs, 2), "ms": round(q_ms, 4), "bytes": q_bytes,
+                     "roofline": {"bound": "hbm", "achieved": round(q_gbs, 2), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4)}},
+        "parity_max_tolerance_usage": max_usage,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
