@@ -61,9 +61,10 @@ typedef enum {
 } q4_mode_t;
 
 typedef enum {
-    Q4_KERNEL_AUTO = 0,   /* choose by M, N, K (see q4_select_kernel)                        */
-    Q4_KERNEL_GEMV = 1,   /* decode GEMV: fp32 dot products over exact 16-bit codes, M <= 2  */
-    Q4_KERNEL_GEMM = 2    /* bf16 MFMA GEMM on dequantised tiles, any M                       */
+    Q4_KERNEL_AUTO = 0,    /* choose by M, N, K, g (see q4_select_kernel)                           */
+    Q4_KERNEL_GEMV = 1,    /* decode GEMV, M <= 2: fp32 wave reduction of exact fp16 (q - z) dots  */
+    Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M                      */
+    Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z), fp32 per-group scaling  */
 } q4_kernel_t;
 
 enum {
@@ -114,8 +115,10 @@ int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t
               const void* packed, const void* scales, const void* zeros, void* Y, void* stream);
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
- * M == 1 and K <= 16384, or M == 2 and K <= 4096, else Q4_ERR_UNSUPPORTED.  Both kernels satisfy the same
- * accuracy bound; callers use this to pin a kernel. */
+ * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,
+ * g in {32, 64} or g % 128 == 0, and X staged in at most 160 KiB of LDS:
+ * 2 M K + 64 K / min(g, 128) bytes.  Otherwise Q4_ERR_UNSUPPORTED.  Every kernel
+ * satisfies the same accuracy bound; callers use this to pin a kernel. */
 int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int32_t kernel, void* stream);

@@ -73,6 +73,10 @@ def test_quantize_validation(kw, status):
     (dict(Y=A16), -7), (dict(Y=B16 + 16), -7), (dict(Y=C16), -7), (dict(Y=D16), -7),
     (dict(M=2, K=8192, g=128, kernel=1), -8), (dict(M=3, kernel=1), -8),
     (dict(M=1, K=32768, g=128, kernel=1), -8),
+    (dict(M=17, K=128, g=32, kernel=3), -8), (dict(M=4, K=96, g=96, kernel=3), -8),
+    (dict(M=4, K=480, g=160, kernel=3), -8), (dict(M=16, K=8192, g=128, kernel=3), -8),
+    (dict(M=16, K=8192, g=32, kernel=3), -8),
+    (dict(kernel=4), -4), (dict(kernel=-1), -4),
 ])
 def test_matmul_validation(kw, status):
     assert _mm(**kw) == status
@@ -89,11 +93,19 @@ def test_matmul_m0_and_sym_zeros_null_are_accepted_without_launch():
 def test_select_kernel():
     assert q4.select_kernel(1, 28672, 8192, 128) == "gemv"
     assert q4.select_kernel(1, 11008, 4096, 128) == "gemv"
-    assert q4.select_kernel(2, 4096, 4096, 128) == "gemv"
-    assert q4.select_kernel(2, 4096, 8192, 128) == "gemm"
-    assert q4.select_kernel(1, 4096, 32768, 128) == "gemm"
-    for M in (3, 4, 8, 16, 2048):
-        assert q4.select_kernel(M, 8192, 8192, 128) == "gemm"
+    assert q4.select_kernel(1, 4096, 16384, 128) == "gemv"
+    assert q4.select_kernel(1, 4096, 32768, 128) == "decode"
+    assert q4.select_kernel(1, 4096, 131072, 128) == "gemm"      # X would not fit in LDS
+    for M in (2, 3, 4, 8):
+        assert q4.select_kernel(M, 28672, 8192, 128) == "decode"
+    assert q4.select_kernel(16, 4096, 4096, 128) == "decode"
+    assert q4.select_kernel(16, 8192, 8192, 128) == "gemm"      # X would not fit in LDS
+    assert q4.select_kernel(2, 100, 96, 32) == "decode"
+    assert q4.select_kernel(4, 100, 96, 32) == "decode"
+    assert q4.select_kernel(4, 100, 480, 160) == "gemm"         # group straddles a 128 tile
+    assert q4.select_kernel(4, 100, 480, 96) == "gemm"
+    assert q4.select_kernel(17, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel(2048, 8192, 8192, 128) == "gemm"
     with pytest.raises(q4.Q4Error):
         q4.select_kernel(1, 8192, 8192, 48)
 

@@ -19,6 +19,17 @@ def _gpu():
     require_gpu()
 
 
+def kernels_for(M, N, K, g):
+    """Every kernel that can run this shape (mirrors the rules stated in include/q4.h)."""
+    ks = ["auto", "gemm"]
+    if (M == 1 and K <= 16384) or (M == 2 and K <= 4096):
+        ks.append("gemv")
+    lds = 2 * M * K + 64 * (K // min(g, 128))
+    if 1 <= M <= 16 and (g in (32, 64) or g % 128 == 0) and lds <= 160 * 1024:
+        ks.append("decode")
+    return tuple(ks)
+
+
 def _upload(packed, scales, zeros):
     from tests.gpu_util import dev
     return dev(packed), dev(scales.view(np.uint16)).view(__import__("torch").float16), dev(zeros)
@@ -52,7 +63,7 @@ def _check_full(X_bits, W_bits, g, mode, label, kernels=("auto",), quant=None):
 def test_configs_full(idx):
     cfg = CONFIGS[idx]
     W_bits, X_bits = make_layer(cfg)
-    kernels = ("auto", "gemm") if X_bits.shape[0] <= 2 else ("auto",)
+    kernels = kernels_for(X_bits.shape[0], cfg.N, cfg.K, cfg.g)
     _check_full(X_bits, W_bits, cfg.g, cfg.mode, cfg.name, kernels)
 
 
@@ -83,7 +94,8 @@ def layer70b():
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_70b_mlp_decode(layer70b, M):
     cfg, X_bits, qw = layer70b
-    _check_sampled(X_bits[:M], qw, cfg.g, cfg.mode, cfg.name, n_samples=3000)
+    for kernel in kernels_for(M, cfg.N, cfg.K, cfg.g):
+        _check_sampled(X_bits[:M], qw, cfg.g, cfg.mode, cfg.name, n_samples=3000, kernel=kernel)
 
 
 @pytest.mark.parametrize("g", [128, 32])
@@ -94,15 +106,15 @@ def test_prefill(g):
     _check_sampled(X_bits, qw, g, cfg.mode, cfg.name, n_samples=4096)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 16, 17, 33, 64, 65, 129, 257])
-@pytest.mark.parametrize("N,K,g", [(100, 96, 32), (37, 256, 64), (128, 4096, 128), (1, 32, 32)])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 33, 64, 65, 129, 257])
+@pytest.mark.parametrize("N,K,g", [(100, 96, 32), (37, 256, 64), (128, 4096, 128), (1, 32, 32),
+                                   (50, 640, 128), (33, 1024, 256), (20, 8192, 8192)])
 def test_ragged(M, N, K, g):
     rng = np.random.default_rng(M * 131 + N * 7 + K)
     W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
     X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
     for mode in ("asym", "sym"):
-        kernels = ("auto", "gemm") if M <= 2 and (M == 1 or K <= 4096) else ("auto",)
-        _check_full(X_bits, W_bits, g, mode, "ragged", kernels)
+        _check_full(X_bits, W_bits, g, mode, "ragged", kernels_for(M, N, K, g))
 
 
 def test_special_values():
@@ -123,8 +135,7 @@ def test_special_values():
     X_bits = f64_to_bf16_bits(X)
     for mode in ("asym", "sym"):
         for M in (1, 2, 6):
-            kernels = ("auto", "gemm") if M <= 2 else ("auto",)
-            Y = _check_full(X_bits[:M], W_bits, g, mode, "special", kernels)
+            Y = _check_full(X_bits[:M], W_bits, g, mode, "special", kernels_for(M, N, K, g))
             assert np.all(Y[:, 0] == 0.0)
 
 
@@ -143,9 +154,10 @@ def test_on_grid_weights_match_exact_product():
     X = orc.bf16_bits_to_f32(X_bits).astype(np.float64)
     exact = X @ W.T
     A = np.abs(X) @ np.abs(W).T
-    for M in (1, 20):
-        Y = _gpu_matmul(X_bits[:M], _upload(packed, scales, zeros), g, "asym")
-        assert np.all(np.abs(Y - exact[:M]) <= orc.tol_ref(A[:M]))
+    for M in (1, 2, 7, 16, 20):
+        for kernel in kernels_for(M, N, K, g):
+            Y = _gpu_matmul(X_bits[:M], _upload(packed, scales, zeros), g, "asym", kernel)
+            assert np.all(np.abs(Y - exact[:M]) <= orc.tol_ref(A[:M])), kernel
 
 
 def test_m0_is_noop_and_nondefault_stream():

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libq4.so")
 
 MODES = {"asym": 0, "sym": 1}
-KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
+KERNELS = {"auto": 0, "gemv": 1, "gemm": 2, "decode": 3}
 _KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
 _lock = threading.Lock()

@@ -1,0 +1,247 @@
+// W4A16 decode for 1 <= M <= 16 on the fp16 matrix cores of gfx950
+// (v_mfma_f32_16x16x32_f16).
+//
+// W4A16: 4-bit weights dequantised inside the kernel, products on 16-bit operands
+// ("LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
+// "The vocabulary"); decode reads every weight once and is bound by HBM ("Overview").
+// Dequantisation x_hat = scale * (q - z) ("DL S067 · Quantization", §1).
+//
+// Arithmetic (exact up to fp32 summation and the final bf16 rounding):
+//   * (q - z) is formed exactly in fp16 (nibble OR-ed into the mantissa of 1024.0, minus
+//     1024 + z; nibbles in bits 4..7 give 16 (q - z));
+//   * X is converted to fp16 exactly after scaling each (row m, k tile) by a power of two 2^e
+//     that puts its largest |x| in [2^14, 2^15); the positions that meet a 16 (q - z) weight
+//     carry 2^(e-4);
+//   * the MFMA sums the products of one tile (exact products, fp32 accumulation); each tile's
+//     partial is multiplied by scale * 2^-e in fp32 and accumulated.
+//
+// Roles: D[m][n] = sum_k X[m][k] W[n][k], A = X (rows m, zero beyond M), B = dequantised W
+// (16 rows n).  A tile is TK = min(g, 128) weights wide along K, so it never straddles a group.
+// In tile t, lane (j, q) = (lane % 16, lane / 16) owns the TK/4 weights that start at
+// k = t TK + q TK/4 in row n0 + j (TK/32 dwords); slice u of the tile is the u-th dword of every
+// lane, i.e. one MFMA.  K inside a tile is permuted identically for both operands.
+//
+// Work split.  One wave streams one block of 16 output rows over the whole of K, keeping 32 dwords
+// of packed weights per lane (with their scales and zero-points) in flight in registers; every lane's
+// accumulators are the final sums of one output column, so there is no cross-wave reduction
+// and no barrier after X has been staged.  Blocks hold just enough waves to cover N with one
+// block per compute unit.
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMaxWaves = 8;        // waves per block at most (2 per SIMD)
+
+// Four 32-bit registers of fp16 pairs (q - z) (x16 for odd positions) from 8 nibbles.
+template <bool SYM>
+__device__ __forceinline__ f16x8 dequant_q_minus_z(uint32_t dw, uint32_t bias, f16x2 b1, f16x2 b16) {
+  if (SYM) dw ^= 0x88888888u;                         // two's complement nibble -> q + 8
+  const uint32_t d8 = dw >> 8;
+  const f16x2 h0 = as_f16x2((dw & 0x000F000Fu) | bias) - b1;    // k0, k4
+  const f16x2 h1 = as_f16x2((dw & 0x00F000F0u) | bias) - b16;   // k1, k5 (x16)
+  const f16x2 h2 = as_f16x2((d8 & 0x000F000Fu) | bias) - b1;    // k2, k6
+  const f16x2 h3 = as_f16x2((d8 & 0x00F000F0u) | bias) - b16;   // k3, k7 (x16)
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+template <int DPT>
+__device__ __forceinline__ void load_dwords(uint32_t (&d)[DPT], const uint8_t* p) {
+  if constexpr (DPT == 4) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+  } else if constexpr (DPT == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    d[0] = v[0]; d[1] = v[1];
+  } else {
+    d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+}
+
+size_t lds_bytes(int64_t M, int64_t K, int g) {
+  const int64_t TK = g < 128 ? g : 128;
+  return (size_t)(2 * M * K + 64 * (K / TK));
+}
+
+template <int DPT, bool SYM, bool FULLT>
+__global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
+    const uint16_t* __restrict__ X, int M, int N, int K, int g,
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y) {
+  constexpr int TK = 32 * DPT;
+  constexpr int P = 32 / DPT;                   // tiles in flight per wave (32 dwords per lane)
+  extern __shared__ u32x4 lds4[];
+  const int T = K / TK;                         // tiles along K
+  const int G = K / g;
+  const int TPG = g / TK;                       // tiles per group
+  const int MP = M;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int lane = tid & (kWave - 1);
+  const int wpb = nthreads / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int j = lane & 15, q = lane >> 4;
+  const int NB = (N + 15) >> 4;
+
+  u32x4* xs = lds4;                                                       // [T][DPT][4][MP]
+  float* fx = reinterpret_cast<float*>(lds4 + (size_t)T * DPT * 4 * MP);  // [T][16]
+
+  // ---- X -> LDS: TK/8 threads per (m, tile), one octet of 8 values each ----
+  constexpr int OPT = TK / 8;                 // octets per tile
+  for (int u0 = tid; u0 < 16 * T * OPT; u0 += nthreads) {
+    const int o = u0 & (OPT - 1);             // octet o = q DPT + u covers k = t TK + 8 o
+    const int mt = u0 / OPT;
+    const int m = mt / T, t = mt - m * T;
+    if (m >= MP) {                            // rows 4 q + r past M get the factor 0
+      if (o == 0) fx[t * 16 + m] = 0.0f;
+      continue;
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)t * TK + 8 * o);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+#pragma unroll
+    for (int s = 1; s < OPT; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s));   // aligned lanes
+    int e = 0;
+    if (amax > 0.0f) {
+      int E;
+      frexpf(amax, &E);
+      e = min(15 - E, 100);                   // amax * 2^e in [2^14, 2^15)
+    }
+    const f16x2 p0 = {(_Float16)ldexpf(bf16_lo(v[0]), e), (_Float16)ldexpf(bf16_lo(v[2]), e)};
+    const f16x2 p1 = {(_Float16)ldexpf(bf16_hi(v[0]), e - 4), (_Float16)ldexpf(bf16_hi(v[2]), e - 4)};
+    const f16x2 p2 = {(_Float16)ldexpf(bf16_lo(v[1]), e), (_Float16)ldexpf(bf16_lo(v[3]), e)};
+    const f16x2 p3 = {(_Float16)ldexpf(bf16_hi(v[1]), e - 4), (_Float16)ldexpf(bf16_hi(v[3]), e - 4)};
+    const int kq = o / DPT, u = o - kq * DPT;
+    xs[((size_t)(t * DPT + u) * 4 + kq) * MP + m] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
+    if (o == 0) fx[t * 16 + m] = ldexpf(1.0f, -e);
+  }
+  __syncthreads();
+
+  uint32_t bias = 0x64006400u;
+  asm volatile("" : "+v"(bias));   // keep in a VGPR: (x & mask) | bias -> one v_and_or_b32
+  const int jx = min(j, MP - 1);
+
+  const size_t rowbytes = (size_t)K >> 1;
+  for (int nb = blockIdx.x * wpb + w; nb < NB; nb += gridDim.x * wpb) {   // wave-uniform
+    // Rows past N (ragged last block) read row N - 1; their outputs are not stored.
+    const int n = min(nb * 16 + j, N - 1);
+    const uint8_t* pr = packed + (size_t)n * rowbytes + q * (TK / 8);
+    const uint16_t* sr = scales + (size_t)n * G;
+    const uint8_t* zr = zeros + (size_t)n * G;
+
+    // Ring of P tiles.  Loads are unconditional, from clamped tiles (t <= T - 1): a load under
+    // a branch would make the compiler wait for every load in flight before the next use.
+    uint32_t wb[P][DPT];
+    uint32_t sb[P], zb[P];
+    int lt = 0, lg = 0, lgi = 0;              // next tile to load, its group, tile inside group
+    auto load_next = [&](int i) {
+      const int t = min(lt, T - 1);
+      const int gg = lt < T ? lg : G - 1;
+      load_dwords<DPT>(wb[i], pr + (size_t)t * (TK / 2));
+      sb[i] = sr[gg];
+      if (!SYM) zb[i] = zr[gg];
+      ++lt;
+      if (++lgi == TPG) { lgi = 0; ++lg; }
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) load_next(i);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < T; t0 += P) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int t = t0 + i;
+        if (FULLT || t < T) {                 // wave-uniform; FULLT: T is a multiple of P
+          const uint32_t z = SYM ? 8u : zb[i];
+          const f16x2 b1 = as_f16x2((0x6400u + z) * 0x00010001u);
+          const f16x2 b16 = as_f16x2((0x6400u + 16u * z) * 0x00010001u);
+          f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < DPT; ++u) {
+            const f16x8 bw = dequant_q_minus_z<SYM>(wb[i][u], bias, b1, b16);
+            // rows j >= M read row M - 1: their results land in rows that are never stored
+            const f16x8 ax = __builtin_bit_cast(f16x8, xs[((size_t)(t * DPT + u) * 4 + q) * MP + jx]);
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, part, 0, 0, 0);
+          }
+          const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[i]);
+          const f32x4 f = *reinterpret_cast<const f32x4*>(fx + t * 16 + 4 * q);   // 2^-e, rows 4q..4q+3
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(part[r], s * f[r], acc[r]);
+        }
+        load_next(i);
+      }
+    }
+    // lane (j, q): rows m = 4 q + r of output column n0 + j
+    const int ncol = nb * 16 + j;
+    if (ncol < N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * q + r;
+        if (m < MP) Y[(size_t)m * N + ncol] = f32_to_bf16_bits(acc[r]);
+      }
+    }
+  }
+}
+
+template <int DPT, bool SYM>
+hipError_t launch_cfg(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
+                      const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
+  const size_t lds = lds_bytes(M, K, g);
+  // More than 64 KiB of dynamic LDS has to be enabled per kernel (thread-safe one-time init).
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
+          ? hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)
+          : hipErrorInvalidValue;
+  if (attr != hipSuccess) return attr;
+  const int64_t NB = (N + 15) / 16;
+  // Enough waves per block that one block per compute unit covers all blocks of rows.
+  int64_t wpb = (NB + num_cus - 1) / num_cus;
+  if (wpb > kMaxWaves) wpb = kMaxWaves;
+  if (wpb < 1) wpb = 1;
+  int64_t blocks = (NB + wpb - 1) / wpb;
+  if (blocks > num_cus) blocks = num_cus;
+  const int64_t T = K / (32 * DPT);
+  if (T % (32 / DPT) == 0)
+    hipLaunchKernelGGL((decode_kernel<DPT, SYM, true>), dim3((unsigned)blocks), dim3((unsigned)(wpb * kWave)),
+                       lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,
+                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
+  else
+    hipLaunchKernelGGL((decode_kernel<DPT, SYM, false>), dim3((unsigned)blocks), dim3((unsigned)(wpb * kWave)),
+                       lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,
+                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
+  return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t launch_mode(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
+                       const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
+  if (g == 32) return launch_cfg<1, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+  if (g == 64) return launch_cfg<2, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+  return launch_cfg<4, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+}
+
+}  // namespace
+
+size_t decode_lds_bytes(int64_t M, int64_t K, int g) { return lds_bytes(M, K, g); }
+
+bool decode_fits(int64_t M, int64_t N, int64_t K, int g) {
+  (void)N;
+  if (M < 1 || M > 16) return false;
+  if (!(g == 32 || g == 64 || g % 128 == 0)) return false;
+  return decode_lds_bytes(M, K, g) <= 160 * 1024;
+}
+
+hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
+                         const void* packed, const void* scales, const void* zeros, void* Y,
+                         int num_cus, hipStream_t stream) {
+  return sym ? launch_mode<true>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream)
+             : launch_mode<false>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+}
+
+}  // namespace q4

@@ -6,199 +6,234 @@
 // token reads every weight).  Dequantisation is x_hat = scale * (q - z) ("DL S067 ·
 // Quantization", §1).
 //
-// Arithmetic.  Y[m, n] = sum_groups scale * sum_{k in group} x[m, k] * (q[n, k] - z), with
-//   * (q - z) formed exactly in fp16: a nibble n is OR-ed into the mantissa of 1024.0
-//     (0x6400 | n == 1024 + n) and (1024 + z) is subtracted, two weights per instruction;
-//     nibbles in bits 4..7 of a byte give 1024 + 16 n and use 1024 + 16 z;
-//   * x converted to fp16 exactly, per (row of X, 32-weight chunk), after scaling by a power
-//     of two that puts the chunk's largest |x| in [2^14, 2^15) (positions that carry the
-//     factor 16 of the weight use the scale / 16);
-//   * products x * (q - z) are exact (11 x 11 bits); they are summed with v_dot2 into fp32,
-//     then each chunk sum is multiplied by scale * 2^-e in fp32 and accumulated per lane;
-//   * lanes are combined by an fp32 wave reduction, and Y is rounded to bf16 once.
-// The only approximations are fp32 summation and the final bf16 rounding (x elements
-// smaller than 2^-27 of their chunk's maximum lose low bits in fp16; their contribution
-// error is below 2^-39 of that maximum times |x_hat|).
+// Arithmetic.  Y[m, n] = sum_chunks scale * (sum_{k in chunk} x[m, k] q[n, k] - z sum_k x[m, k]),
+// chunks of 32 weights never straddling a group, with
+//   * the codes q used as exact fp16 subnormals: a nibble masked into the low bits of a 16-bit
+//     half is the fp16 value q * 2^-24 (a nibble in bits 4..7 gives 16 q * 2^-24), two weights
+//     per instruction and no bias to remove;
+//   * x converted to fp16 exactly, per (row of X, chunk), after scaling by a power of two 2^e
+//     that puts the chunk's largest |x| in [2^14, 2^15) (positions that meet a 16 q weight carry
+//     2^(e-4)); the chunk sums of the scaled x are precomputed once per block;
+//   * products x q are exact; v_dot2 sums them in fp32; the zero-point enters as one fma per
+//     chunk (sum x q - z sum x), the chunk result is multiplied by 2^24, 2^-e and the scale in
+//     fp32 and accumulated per lane; lanes are combined by an fp32 wave reduction and Y is rounded to
+//     bf16 once.
+// Beyond fp32 summation and the bf16 output, the rounding of the two chunk sums adds at most
+// about 2^-24 * 30 * scale * sum|x| per chunk (the q and z terms are each at most 15 sum|x|);
+// x elements smaller than 2^-27 of their chunk's maximum lose low bits in fp16.
 //
 // Work split.  A wave owns one output row n at a time; lane l owns the 16-byte packed chunks
 // c = l + 64 j (32 weights each), so one load instruction reads 1 KiB of a row contiguously.
-// The lane's slice of X is fixed for every row, so after a block-wide conversion through LDS
-// it stays in registers.  Rows are grid-strided over a persistent grid, and the next row's
-// packed chunks, scales and zeros are loaded before the current row is reduced.
+// One persistent block of 16 waves per compute unit converts X once into LDS (laid out in
+// four planes so that a lane's 16-byte reads of consecutive chunks hit distinct banks).
+// Each wave keeps three rows in flight: the loads of rows n + nw and n + 2 nw are issued
+// before row n is computed, and the first three rows are requested before the conversion of
+// X, so HBM latency overlaps it.  Row sums are reduced with DPP row operations and lane reads.
 #include "q4_device.h"
 #include "q4_internal.h"
 
 namespace q4 {
 namespace {
 
-constexpr int kBlock = 512;
+// Sum over the 64 lanes of a wave, returned uniformly.
+__device__ __forceinline__ float dpp_row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)); // row_mirror
+  return v;   // every lane of a 16-lane row holds that row's sum
+}
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_row_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
 
-template <int MT, int J, bool SYM>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(
+// Loaded values stay untouched until use, so the loads of later rows remain in flight.
+template <int J>
+struct RowBuf {
+  u32x4 w[J];
+  uint32_t s[J];      // fp16 scale bits
+  uint32_t z[J];      // zero-point
+};
+
+template <int MT, int J, bool SYM, int BLOCK, bool FULL>
+__global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y) {
-  extern __shared__ uint32_t lds[];
+  extern __shared__ u32x4 lds4[];
   const int C = K >> 5;                       // 32-weight chunks per row
   const int G = K / g;
   const int cpg = g >> 5;                     // chunks per group
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wpb = BLOCK / kWave;
+  const int64_t nw = (int64_t)gridDim.x * wpb;
+  const int64_t n0 = (int64_t)blockIdx.x * wpb +
+                    __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // wave-uniform
 
-  // ---- X -> fp16 pairs, 16 dwords per (m, chunk), plus 2^-e per (m, chunk) ----
-  uint32_t* xs = lds;
-  float* fs = reinterpret_cast<float*>(lds + (size_t)M * C * 16);
-  for (int idx = threadIdx.x; idx < M * C; idx += blockDim.x) {
+  int goff[J];
+  bool cval[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = lane + kWave * j;
+    cval[j] = FULL || c < C;
+    goff[j] = (cval[j] ? c : C - 1) / cpg;
+  }
+
+  // Loads are unconditional, from clamped (always valid) chunks and rows: a load under a branch
+  // makes the compiler wait for every load in flight, prefetched rows included, before the
+  // next use.  Chunks past the row end are skipped when computed; rows past N are not stored.
+  auto load = [&](RowBuf<J>& b, int64_t row) {
+    const u32x4* pr = packed + (size_t)row * C;
+    const size_t gb = (size_t)row * G;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+      b.w[j] = __builtin_nontemporal_load(pr + c);
+      b.s[j] = scales[gb + goff[j]];
+      if (!SYM) b.z[j] = zeros[gb + goff[j]];
+    }
+  };
+
+  RowBuf<J> b0, b1, b2;
+  const int64_t nlast = N - 1;
+  load(b0, n0 < nlast ? n0 : nlast);
+  load(b1, n0 + nw < nlast ? n0 + nw : nlast);
+  load(b2, n0 + 2 * nw < nlast ? n0 + 2 * nw : nlast);
+
+  // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, chunk), four planes of 16 bytes ----
+  // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t;
+  // fs holds 2^-e and sx the chunk sum of the scaled x times 2^-24.
+  u32x4* xs = lds4;                                           // [M][4][C]
+  float* fs = reinterpret_cast<float*>(lds4 + (size_t)M * 4 * C);   // [M][C]
+  float* sx = fs + (size_t)M * C;                                   // [M][C]
+  for (int idx = threadIdx.x; idx < M * C; idx += BLOCK) {
     const int m = idx / C;
     const int c = idx - m * C;
     const u32x4* xp = reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)c * 32);
-    float x[32];
+    u32x4 v[4];
 #pragma unroll
-    for (int o = 0; o < 4; ++o) {
-      const u32x4 v = xp[o];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[8 * o + 2 * i] = bf16_lo(v[i]);
-        x[8 * o + 2 * i + 1] = bf16_hi(v[i]);
-      }
-    }
+    for (int o = 0; o < 4; ++o) v[o] = xp[o];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[o][i])), fabsf(bf16_hi(v[o][i]))));
     int e = 0;
     if (amax > 0.0f) {
       int E;
       frexpf(amax, &E);                       // amax = f * 2^E, f in [0.5, 1)
-      e = min(15 - E, 100);
+      e = min(15 - E, 100);                   // amax * 2^e in [2^14, 2^15)
     }
+    float sum = 0.0f;
 #pragma unroll
     for (int o = 0; o < 4; ++o) {
-      const float* y = x + 8 * o;
-      f16x2 p0 = {(_Float16)ldexpf(y[0], e), (_Float16)ldexpf(y[4], e)};
-      f16x2 p1 = {(_Float16)ldexpf(y[1], e - 4), (_Float16)ldexpf(y[5], e - 4)};
-      f16x2 p2 = {(_Float16)ldexpf(y[2], e), (_Float16)ldexpf(y[6], e)};
-      f16x2 p3 = {(_Float16)ldexpf(y[3], e - 4), (_Float16)ldexpf(y[7], e - 4)};
-      uint32_t* dst = xs + (size_t)idx * 16 + 4 * o;
-      dst[0] = as_u32(p0);
-      dst[1] = as_u32(p1);
-      dst[2] = as_u32(p2);
-      dst[3] = as_u32(p3);
+      // octet o: x0..x7 = lo/hi halves of v[o][0..3]
+      const u32x4 q = v[o];
+      const f16x2 p0 = {(_Float16)ldexpf(bf16_lo(q[0]), e), (_Float16)ldexpf(bf16_lo(q[2]), e)};
+      const f16x2 p1 = {(_Float16)ldexpf(bf16_hi(q[0]), e - 4), (_Float16)ldexpf(bf16_hi(q[2]), e - 4)};
+      const f16x2 p2 = {(_Float16)ldexpf(bf16_lo(q[1]), e), (_Float16)ldexpf(bf16_lo(q[3]), e)};
+      const f16x2 p3 = {(_Float16)ldexpf(bf16_hi(q[1]), e - 4), (_Float16)ldexpf(bf16_hi(q[3]), e - 4)};
+      xs[((size_t)m * 4 + o) * C + c] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
+      // sum of the scaled x as the dot products see them (the x16 positions count 16 times)
+      sum += (float)p0[0] + (float)p0[1] + (float)p2[0] + (float)p2[1] +
+             16.0f * ((float)p1[0] + (float)p1[1] + (float)p3[0] + (float)p3[1]);
     }
     fs[idx] = ldexpf(1.0f, -e);
+    sx[idx] = ldexpf(sum, -24);
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t xr[MT][J][16];
-  float fr[MT][J];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + kWave * j;
-      const bool ok = m < M && c < C;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) xr[m][j][t] = ok ? xs[((size_t)m * C + c) * 16 + t] : 0u;
-      fr[m][j] = ok ? fs[(size_t)m * C + c] : 0.0f;
-    }
-  }
-
-  const int64_t waves_per_block = blockDim.x / kWave;
-  const int64_t nw = (int64_t)gridDim.x * waves_per_block;
-  int64_t n = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x / kWave);
-
-  u32x4 wc[J];
-  uint16_t sc[J];
-  uint8_t zc[J];
-  auto load_row = [&](int64_t row, u32x4 (&w)[J], uint16_t (&s)[J], uint8_t (&z)[J]) {
-    const u32x4* pr = packed + (size_t)row * C;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + kWave * j;
-      if (c < C) {
-        w[j] = __builtin_nontemporal_load(pr + c);
-        const size_t gi = (size_t)row * G + c / cpg;
-        s[j] = scales[gi];
-        z[j] = SYM ? (uint8_t)8 : zeros[gi];
-      } else {
-        w[j] = u32x4{0u, 0u, 0u, 0u};
-        s[j] = 0;
-        z[j] = 0;
-      }
-    }
-  };
-  if (n < N) load_row(n, wc, sc, zc);
-
-  for (; n < N; n += nw) {
-    u32x4 wn[J];
-    uint16_t sn[J];
-    uint8_t zn[J];
-    const int64_t nn = n + nw;
-    if (nn < N) load_row(nn, wn, sn, zn);
-
+  auto process = [&](const RowBuf<J>& b, int64_t row) {
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const uint32_t z = zc[j];
-      const f16x2 b1 = as_f16x2((0x6400u + z) * 0x00010001u);        // (1024 + z) x2
-      const f16x2 b16 = as_f16x2((0x6400u + 16u * z) * 0x00010001u); // (1024 + 16 z) x2
-      float d[MT];
+      if (cval[j]) {
+        const int c = lane + kWave * j;
+        const float zf = SYM ? 8.0f : (float)b.z[j];
+        // four independent partial sums per row of X (one per dword) keep the dot2 chains short
+        float d[MT][4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) d[m] = 0.0f;
+        for (int o = 0; o < 4; ++o) {
+          uint32_t dw = b.w[j][o];
+          if (SYM) dw ^= 0x88888888u;          // two's complement nibble -> q + 8
+          const uint32_t d8 = dw >> 8;
+          const f16x2 h0 = as_f16x2(dw & 0x000F000Fu);   // q k0, k4   (x 2^-24)
+          const f16x2 h1 = as_f16x2(dw & 0x00F000F0u);   // 16 q k1, k5
+          const f16x2 h2 = as_f16x2(d8 & 0x000F000Fu);   // q k2, k6
+          const f16x2 h3 = as_f16x2(d8 & 0x00F000F0u);   // 16 q k3, k7
 #pragma unroll
-      for (int o = 0; o < 4; ++o) {
-        uint32_t dw = wc[j][o];
-        if (SYM) dw ^= 0x88888888u;          // two's complement nibble -> q + 8
-        const uint32_t d8 = dw >> 8;
-        const f16x2 h0 = as_f16x2((dw & 0x000F000Fu) | 0x64006400u) - b1;   // k0, k4
-        const f16x2 h1 = as_f16x2((dw & 0x00F000F0u) | 0x64006400u) - b16;  // k1, k5 (x16)
-        const f16x2 h2 = as_f16x2((d8 & 0x000F000Fu) | 0x64006400u) - b1;   // k2, k6
-        const f16x2 h3 = as_f16x2((d8 & 0x00F000F0u) | 0x64006400u) - b16;  // k3, k7 (x16)
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 xv = xs[((size_t)m * 4 + o) * C + c];
+            float t = __builtin_amdgcn_fdot2(h0, as_f16x2(xv[0]), 0.0f, false);
+            t = __builtin_amdgcn_fdot2(h1, as_f16x2(xv[1]), t, false);
+            t = __builtin_amdgcn_fdot2(h2, as_f16x2(xv[2]), t, false);
+            d[m][o] = __builtin_amdgcn_fdot2(h3, as_f16x2(xv[3]), t, false);
+          }
+        }
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)b.s[j]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          d[m] = __builtin_amdgcn_fdot2(h0, as_f16x2(xr[m][j][4 * o + 0]), d[m], false);
-          d[m] = __builtin_amdgcn_fdot2(h1, as_f16x2(xr[m][j][4 * o + 1]), d[m], false);
-          d[m] = __builtin_amdgcn_fdot2(h2, as_f16x2(xr[m][j][4 * o + 2]), d[m], false);
-          d[m] = __builtin_amdgcn_fdot2(h3, as_f16x2(xr[m][j][4 * o + 3]), d[m], false);
+          const float r = __builtin_fmaf(-zf, sx[m * C + c], (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]));
+          // 2^24 and 2^-e applied as two exact power-of-two products: no overflow unless the
+          // chunk's dot product itself overflows
+          acc[m] = __builtin_fmaf((r * 16777216.0f) * fs[m * C + c], s, acc[m]);
         }
       }
-      const float s = (float)__builtin_bit_cast(_Float16, sc[j]);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = __builtin_fmaf(d[m], s * fr[m][j], acc[m]);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const float tot = wave_sum(acc[m]);
-      if (lane == m && m < M) Y[(size_t)m * N + n] = f32_to_bf16_bits(tot);
+      const float tot = wave_total(acc[m]);
+      if (lane == m && m < M) Y[(size_t)m * N + row] = f32_to_bf16_bits(tot);
     }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      wc[j] = wn[j];
-      sc[j] = sn[j];
-      zc[j] = zn[j];
-    }
+  };
+
+  // sched_barrier keeps the compiler from hoisting one row's work into another's, which would
+  // keep more than three rows of registers live.
+  // Three rows in flight per wave; past the end the loads repeat row N - 1 (never used).
+  for (int64_t n = n0; n < N; n += 3 * nw) {
+    process(b0, n);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, n + 3 * nw < nlast ? n + 3 * nw : nlast);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + nw < N) process(b1, n + nw);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b1, n + 4 * nw < nlast ? n + 4 * nw : nlast);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 2 * nw < N) process(b2, n + 2 * nw);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b2, n + 5 * nw < nlast ? n + 5 * nw : nlast);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int MT, int J>
+template <int MT, int J, int BLOCK>
 hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                       const void* packed, const void* scales, const void* zeros, void* Y,
                       int num_cus, hipStream_t stream) {
   const int C = (int)(K >> 5);
-  const size_t lds = (size_t)M * C * 16 * 4 + (size_t)M * C * 4;
-  const int64_t waves_per_block = kBlock / kWave;
-  int64_t blocks = (N + waves_per_block - 1) / waves_per_block;
-  const int64_t cap = (int64_t)num_cus * 2;
+  const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 8;
+  const int64_t wpb = BLOCK / kWave;
+  int64_t blocks = (N + wpb - 1) / wpb;
+  const int64_t cap = (int64_t)num_cus * (BLOCK >= 768 ? 1 : 2);
   if (blocks > cap) blocks = cap;
+  const bool full = C == kWave * J;
+#define Q4_GEMV_LAUNCH(SYMV, FULLV)                                                              \
+  hipLaunchKernelGGL((gemv_kernel<MT, J, SYMV, BLOCK, FULLV>), dim3((unsigned)blocks), dim3(BLOCK), \
+                     lds, stream, (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,     \
+                     (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y)
   if (sym) {
-    hipLaunchKernelGGL((gemv_kernel<MT, J, true>), dim3((unsigned)blocks), dim3(kBlock), lds, stream,
-                       (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
+    if (full) Q4_GEMV_LAUNCH(true, true); else Q4_GEMV_LAUNCH(true, false);
   } else {
-    hipLaunchKernelGGL((gemv_kernel<MT, J, false>), dim3((unsigned)blocks), dim3(kBlock), lds, stream,
-                       (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
+    if (full) Q4_GEMV_LAUNCH(false, true); else Q4_GEMV_LAUNCH(false, false);
   }
+#undef Q4_GEMV_LAUNCH
   return hipGetLastError();
 }
 
@@ -206,11 +241,11 @@ template <int MT>
 hipError_t launch_mt(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int num_cus, hipStream_t stream) {
-  if (K <= 2048) return launch_mtj<MT, 1>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
-  if (K <= 4096) return launch_mtj<MT, 2>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+  if (K <= 2048) return launch_mtj<MT, 1, 1024>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+  if (K <= 4096) return launch_mtj<MT, 2, (MT == 1 ? 1024 : 768)>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   if constexpr (MT == 1) {
-    if (K <= 8192) return launch_mtj<1, 4>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
-    if (K <= 16384) return launch_mtj<1, 8>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+    if (K <= 8192) return launch_mtj<1, 4, 768>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+    if (K <= 16384) return launch_mtj<1, 8, 512>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -55,6 +55,14 @@ bool gemv_fits(int64_t M, int64_t K) {
   return (M == 1 && K <= q4::kGemvMaxK) || (M == 2 && K <= q4::kGemvMaxK2);
 }
 
+// Q4_KERNEL_AUTO: the decode kernels for small M, the GEMM otherwise.
+int auto_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
+  if (M == 1 && gemv_fits(M, K)) return Q4_KERNEL_GEMV;
+  if (q4::decode_fits(M, N, K, g)) return Q4_KERNEL_DECODE;
+  if (gemv_fits(M, K)) return Q4_KERNEL_GEMV;
+  return Q4_KERNEL_GEMM;
+}
+
 int validate_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
                     const void* packed, const void* scales, const void* zeros, const void* Y) {
   int st = check_shape(N, K, g, mode);
@@ -116,23 +124,26 @@ int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
   int st = check_shape(N, K, g, Q4_ASYM);
   if (st != Q4_OK) return st;
   if (M < 0 || M > kMaxDim) return Q4_ERR_SHAPE;
-  return gemv_fits(M, K) ? Q4_KERNEL_GEMV : Q4_KERNEL_GEMM;
+  if (M == 0) return Q4_KERNEL_GEMM;
+  return auto_kernel(M, N, K, g);
 }
 
 int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int32_t kernel, void* stream) {
-  if (kernel != Q4_KERNEL_AUTO && kernel != Q4_KERNEL_GEMV && kernel != Q4_KERNEL_GEMM)
-    return Q4_ERR_MODE;
+  if (kernel < Q4_KERNEL_AUTO || kernel > Q4_KERNEL_DECODE) return Q4_ERR_MODE;
   int st = validate_matmul(X, M, N, K, g, mode, packed, scales, zeros, Y);
   if (st != Q4_OK) return st;
   if (M == 0) return Q4_OK;
-  if (kernel == Q4_KERNEL_AUTO) kernel = gemv_fits(M, K) ? Q4_KERNEL_GEMV : Q4_KERNEL_GEMM;
+  if (kernel == Q4_KERNEL_AUTO) kernel = auto_kernel(M, N, K, g);
   if (kernel == Q4_KERNEL_GEMV && !gemv_fits(M, K)) return Q4_ERR_UNSUPPORTED;
+  if (kernel == Q4_KERNEL_DECODE && !q4::decode_fits(M, N, K, g)) return Q4_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool sym = mode == Q4_SYM;
   if (kernel == Q4_KERNEL_GEMV)
     return finish(q4::launch_gemv(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+  if (kernel == Q4_KERNEL_DECODE)
+    return finish(q4::launch_decode(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
 }
 

@@ -17,6 +17,14 @@ hipError_t launch_gemv(const void* X, int M, int64_t N, int64_t K, int g, bool s
                        const void* packed, const void* scales, const void* zeros, void* Y,
                        int num_cus, hipStream_t stream);
 
+// Decode on fp16 MFMA for 1 <= M <= 16 (K <= 8192, g in {32, 64} or a multiple of 128, X staged
+// in LDS).
+size_t decode_lds_bytes(int64_t M, int64_t K, int g);
+bool decode_fits(int64_t M, int64_t N, int64_t K, int g);
+hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
+                         const void* packed, const void* scales, const void* zeros, void* Y,
+                         int num_cus, hipStream_t stream);
+
 // MFMA GEMM for any M >= 1.
 hipError_t launch_gemm(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
                        const void* packed, const void* scales, const void* zeros, void* Y,
