@@ -106,6 +106,17 @@ def test_prefill(g):
     _check_sampled(X_bits, qw, g, cfg.mode, cfg.name, n_samples=4096)
 
 
+@pytest.mark.parametrize("M,N,K,g", [(512, 64, 128, 128), (513, 300, 256, 32), (640, 256, 384, 128),
+                                     (1000, 520, 512, 64), (700, 1030, 1024, 256), (777, 136, 640, 128)])
+def test_prefill_ragged(M, N, K, g):
+    """Large-M shapes on the LDS-staged GEMM: ragged M and N tiles, odd step counts, every g."""
+    rng = np.random.default_rng(M + 3 * N + 7 * K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full(X_bits, W_bits, g, mode, "prefill-ragged", ("auto", "gemm"))
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 33, 64, 65, 129, 257])
 @pytest.mark.parametrize("N,K,g", [(100, 96, 32), (37, 256, 64), (128, 4096, 128), (1, 32, 32),
                                    (50, 640, 128), (33, 1024, 256), (20, 8192, 8192)])

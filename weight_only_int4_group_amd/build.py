@@ -28,6 +28,7 @@ SOURCES = {
     "quantize.hip": ["-ffp-contract=off", "-fno-fast-math"],
     "gemv.hip": [],
     "gemm.hip": [],
+    "prefill.hip": [],
     "decode.hip": [],
     "q4_abi.cpp": [],
 }
