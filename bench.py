@@ -93,41 +93,48 @@ def _counter_rows(d):
 
 
 def summarize_counters(fetch_dir, write_dir):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMV, scaled by a plain copy's."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMV, scaled by a plain copy's.
+
+    The calibration copy is the one device-to-device copy of 512 MiB that
+    ``--copy-calibration`` launches: the copy dispatch whose WRITE_SIZE is closest to 512 MiB
+    (its FETCH_SIZE is taken from the same dispatch index of the other run).
+    """
     def per_kernel(d, counter):
         out = {}
         for r in _counter_rows(d):
             if r.get("Counter_Name") != counter:
                 continue
-            name = r.get("Kernel_Name", "")
-            out.setdefault(name, []).append(float(r["Counter_Value"]))
+            out.setdefault(r.get("Kernel_Name", ""), []).append(float(r["Counter_Value"]))
         return out
 
-    def pick(d, key):
-        hits = [v for k, v in d.items() if key(k)]
-        if not hits:
-            return None
-        vals = [x for h in hits for x in h]
-        return sum(vals) / len(vals), len(vals)
+    def mean_of(d, key):
+        vals = [x for k, v in d.items() if key(k) for x in v]
+        return (sum(vals) / len(vals), len(vals)) if vals else None
 
+    copy_bytes = 512 * 2 ** 20
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
     is_gemv = lambda k: "gemv_kernel" in k
-    is_copy = lambda k: ("copy" in k.lower() or "elementwise" in k.lower()) and "q4" not in k
-    gf, gw, cf, cw = pick(fetch, is_gemv), pick(write, is_gemv), pick(fetch, is_copy), pick(write, is_copy)
-    copy_bytes = 512 * 2 ** 20
+    is_copy = lambda k: "copyBuffer" in k
+    gf, gw = mean_of(fetch, is_gemv), mean_of(write, is_gemv)
+    cw_all = [x for k, v in write.items() if is_copy(k) for x in v]
+    cf_all = [x for k, v in fetch.items() if is_copy(k) for x in v]
+    cw = cf = None
+    if cw_all and cf_all and len(cw_all) == len(cf_all):
+        i = min(range(len(cw_all)), key=lambda j: abs(cw_all[j] * 1024 - copy_bytes))
+        cw, cf = cw_all[i], cf_all[i]
     res = {
         "gemv_src_sha": src_sha(GEMV_SRC),
         "gemv_fetch_kib_per_dispatch": gf[0] if gf else None,
         "gemv_write_kib_per_dispatch": gw[0] if gw else None,
         "gemv_dispatches": gf[1] if gf else 0,
         "copy_bytes": copy_bytes,
-        "copy_fetch_kib": cf[0] if cf else None,
-        "copy_write_kib": cw[0] if cw else None,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
     }
     if gf and gw and cf and cw:
-        ff = copy_bytes / (cf[0] * 1024)
-        fw = copy_bytes / (cw[0] * 1024)
+        ff = copy_bytes / (cf * 1024)
+        fw = copy_bytes / (cw * 1024)
         res["copy_factor_fetch"] = ff
         res["copy_factor_write"] = fw
         res["traffic_bytes_per_launch"] = gf[0] * 1024 * ff + gw[0] * 1024 * fw
