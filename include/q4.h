@@ -63,7 +63,9 @@ typedef enum {
 typedef enum {
     Q4_KERNEL_AUTO = 0,    /* choose by M, N, K, g (see q4_select_kernel)                           */
     Q4_KERNEL_GEMV = 1,    /* decode GEMV, M <= 2: fp32 wave reduction of exact fp16 (q - z) dots  */
-    Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M                      */
+    Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M (M >= 512 with K % 128
+                              == 0 and a power-of-two g: X staged in LDS, W dequantised in
+                              registers; otherwise W dequantised into LDS)                        */
     Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z), fp32 per-group scaling  */
 } q4_kernel_t;
 
@@ -123,8 +125,9 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int32_t kernel, void* stream);
 
-/* The kernel Q4_KERNEL_AUTO picks for this shape (Q4_KERNEL_GEMV or Q4_KERNEL_GEMM), or a
- * negative status for an invalid shape.  Pure host function, no HIP call. */
+/* The kernel Q4_KERNEL_AUTO picks for this shape (Q4_KERNEL_GEMV, Q4_KERNEL_DECODE or
+ * Q4_KERNEL_GEMM), or a negative status for an invalid shape.  Pure host function, no HIP
+ * call. */
 int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
