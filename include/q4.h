@@ -119,7 +119,7 @@ int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
  * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,
  * g in {32, 64} or g % 128 == 0, and X staged in at most 160 KiB of LDS:
- * 2 M K + 64 K / min(g, 128) bytes.  Otherwise Q4_ERR_UNSUPPORTED.  Every kernel
+ * 2 M K + 64 K / min(g, 128) + 8192 bytes.  Otherwise Q4_ERR_UNSUPPORTED.  Every kernel
  * satisfies the same accuracy bound; callers use this to pin a kernel. */
 int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
                      const void* packed, const void* scales, const void* zeros, void* Y,

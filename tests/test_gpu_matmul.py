@@ -24,7 +24,7 @@ def kernels_for(M, N, K, g):
     ks = ["auto", "gemm"]
     if (M == 1 and K <= 16384) or (M == 2 and K <= 4096):
         ks.append("gemv")
-    lds = 2 * M * K + 64 * (K // min(g, 128))
+    lds = 2 * M * K + 64 * (K // min(g, 128)) + 8192
     if 1 <= M <= 16 and (g in (32, 64) or g % 128 == 0) and lds <= 160 * 1024:
         ks.append("decode")
     return tuple(ks)
