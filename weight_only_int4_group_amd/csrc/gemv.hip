@@ -53,14 +53,18 @@ __device__ __forceinline__ float wave_total(float v) {
 }
 
 // Loaded values stay untouched until use, so the loads of later rows remain in flight.
-template <int J>
+// SHARE (a row has at most 64 groups): lane l loads the scale and zero of group l only, and a
+// lane reads the values of its chunks' groups from the owning lanes (ds_bpermute), i.e. two
+// coalesced loads per row instead of two per chunk.  The rows of a wave are processed with all
+// 64 lanes active, so every source lane of the exchange holds its value.
+template <int J, bool SHARE>
 struct RowBuf {
   u32x4 w[J];
-  uint32_t s[J];      // fp16 scale bits
-  uint32_t z[J];      // zero-point
+  uint32_t s[SHARE ? 1 : J];      // fp16 scale bits
+  uint32_t z[SHARE ? 1 : J];      // zero-point
 };
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE>
 __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -87,19 +91,26 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   // Loads are unconditional, from clamped (always valid) chunks and rows: a load under a branch
   // makes the compiler wait for every load in flight, prefetched rows included, before the
   // next use.  Chunks past the row end are skipped when computed; rows past N are not stored.
-  auto load = [&](RowBuf<J>& b, int64_t row) {
+  const int gown = min(lane, G - 1);           // SHARE: the group this lane loads
+  auto load = [&](RowBuf<J, SHARE>& b, int64_t row) {
     const u32x4* pr = packed + (size_t)row * C;
     const size_t gb = (size_t)row * G;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
       b.w[j] = __builtin_nontemporal_load(pr + c);
-      b.s[j] = scales[gb + goff[j]];
-      if (!SYM) b.z[j] = zeros[gb + goff[j]];
+      if (!SHARE) {
+        b.s[j] = scales[gb + goff[j]];
+        if (!SYM) b.z[j] = zeros[gb + goff[j]];
+      }
+    }
+    if (SHARE) {
+      b.s[0] = scales[gb + gown];
+      if (!SYM) b.z[0] = zeros[gb + gown];
     }
   };
 
-  RowBuf<J> b0, b1, b2;
+  RowBuf<J, SHARE> b0, b1, b2;
   const int64_t nlast = N - 1;
   load(b0, n0 < nlast ? n0 : nlast);
   load(b1, n0 + nw < nlast ? n0 + nw : nlast);
@@ -148,15 +159,30 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   }
   __syncthreads();
 
-  auto process = [&](const RowBuf<J>& b, int64_t row) {
+  auto process = [&](const RowBuf<J, SHARE>& b, int64_t row) {
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    // SHARE: every lane takes part in the exchange (all 64 lanes active), before any branch.
+    uint32_t shared[SHARE ? J : 1];
+    if (SHARE) {
+      const uint32_t sz = SYM ? b.s[0] : (b.s[0] | (b.z[0] << 16));   // one word per group
+#pragma unroll
+      for (int j = 0; j < J; ++j) shared[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * goff[j], (int)sz);
+    }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (cval[j]) {
         const int c = lane + kWave * j;
-        const float zf = SYM ? 8.0f : (float)b.z[j];
+        uint32_t sbits, zbits;
+        if (SHARE) {
+          sbits = shared[j] & 0xffffu;
+          zbits = shared[j] >> 16;
+        } else {
+          sbits = b.s[j];
+          zbits = SYM ? 8u : b.z[j];
+        }
+        const float zf = SYM ? 8.0f : (float)zbits;
         // four independent partial sums per row of X (one per dword) keep the dot2 chains short
         float d[MT][4];
 #pragma unroll
@@ -177,7 +203,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
             d[m][o] = __builtin_amdgcn_fdot2(h3, as_f16x2(xv[3]), t, false);
           }
         }
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)b.s[j]);
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const float r = __builtin_fmaf(-zf, sx[m * C + c], (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]));
@@ -224,15 +250,20 @@ hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sy
   const int64_t cap = (int64_t)num_cus * (BLOCK >= 768 ? 1 : 2);
   if (blocks > cap) blocks = cap;
   const bool full = C == kWave * J;
-#define Q4_GEMV_LAUNCH(SYMV, FULLV)                                                              \
-  hipLaunchKernelGGL((gemv_kernel<MT, J, SYMV, BLOCK, FULLV>), dim3((unsigned)blocks), dim3(BLOCK), \
-                     lds, stream, (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,     \
-                     (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y)
+  const bool share = K / g <= kWave;
+#define Q4_GEMV_LAUNCH(SYMV, FULLV, SHAREV)                                                      \
+  hipLaunchKernelGGL((gemv_kernel<MT, J, SYMV, BLOCK, FULLV, SHAREV>), dim3((unsigned)blocks),   \
+                     dim3(BLOCK), lds, stream, (const uint16_t*)X, M, N, (int)K, g,              \
+                     (const u32x4*)packed, (const uint16_t*)scales, (const uint8_t*)zeros,       \
+                     (uint16_t*)Y)
+#define Q4_GEMV_SHARE(SYMV, FULLV)                                                               \
+  if (share) Q4_GEMV_LAUNCH(SYMV, FULLV, true); else Q4_GEMV_LAUNCH(SYMV, FULLV, false)
   if (sym) {
-    if (full) Q4_GEMV_LAUNCH(true, true); else Q4_GEMV_LAUNCH(true, false);
+    if (full) { Q4_GEMV_SHARE(true, true); } else { Q4_GEMV_SHARE(true, false); }
   } else {
-    if (full) Q4_GEMV_LAUNCH(false, true); else Q4_GEMV_LAUNCH(false, false);
+    if (full) { Q4_GEMV_SHARE(false, true); } else { Q4_GEMV_SHARE(false, false); }
   }
+#undef Q4_GEMV_SHARE
 #undef Q4_GEMV_LAUNCH
   return hipGetLastError();
 }
@@ -244,7 +275,17 @@ hipError_t launch_mt(const void* X, int M, int64_t N, int64_t K, int g, bool sym
   if (K <= 2048) return launch_mtj<MT, 1, 1024>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   if (K <= 4096) return launch_mtj<MT, 2, (MT == 1 ? 1024 : 768)>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   if constexpr (MT == 1) {
-    if (K <= 8192) return launch_mtj<1, 4, 768>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+    if (K <= 8192) {
+      // Whole rows per wave: pick the block size (8, 12 or 16 waves per compute unit) that
+      // minimises (rows of the busiest wave) x (waves sharing a compute unit).
+      auto cost = [&](int64_t w) { return ((N + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w)) * w; };
+      const int64_t c8 = cost(8), c12 = cost(12), c16 = cost(16);
+      if (c16 <= c12 && c16 <= c8)
+        return launch_mtj<1, 4, 1024>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+      if (c8 < c12)
+        return launch_mtj<1, 4, 512>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+      return launch_mtj<1, 4, 768>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+    }
     if (K <= 16384) return launch_mtj<1, 8, 512>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   }
   return hipErrorInvalidValue;
