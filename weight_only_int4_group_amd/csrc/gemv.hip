@@ -32,6 +32,8 @@
 #include "q4_device.h"
 #include "q4_internal.h"
 
+#include <atomic>
+
 namespace q4 {
 namespace {
 
@@ -64,7 +66,7 @@ struct RowBuf {
   uint32_t z[SHARE ? 1 : J];      // zero-point
 };
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
 __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -88,33 +90,37 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     goff[j] = (cval[j] ? c : C - 1) / cpg;
   }
 
-  // Loads are unconditional, from clamped (always valid) chunks and rows: a load under a branch
-  // makes the compiler wait for every load in flight, prefetched rows included, before the
-  // next use.  Chunks past the row end are skipped when computed; rows past N are not stored.
+  // Loads are unconditional, from clamped (always valid) chunks: a load under a branch makes the
+  // compiler wait for every load in flight, prefetched rows included, before the next use.  A
+  // row past the end gets an empty buffer resource, so its loads read no memory and return 0;
+  // chunks past the row end are skipped when computed and rows past N are not stored.
   const int gown = min(lane, G - 1);           // SHARE: the group this lane loads
   auto load = [&](RowBuf<J, SHARE>& b, int64_t row) {
-    const u32x4* pr = packed + (size_t)row * C;
-    const size_t gb = (size_t)row * G;
+    const bool live = row < N;                  // wave-uniform
+    const size_t r = live ? (size_t)row : 0;
+    const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + r * C, live ? (uint32_t)C * 16u : 0u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_over(scales + r * G, live ? (uint32_t)G * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rz = buffer_over(zeros + r * G, live ? (uint32_t)G : 0u);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
-      b.w[j] = __builtin_nontemporal_load(pr + c);
+      b.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * c, 0, kBufferNT));
       if (!SHARE) {
-        b.s[j] = scales[gb + goff[j]];
-        if (!SYM) b.z[j] = zeros[gb + goff[j]];
+        b.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * goff[j], 0, 0);
+        if (!SYM) b.z[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, goff[j], 0, 0);
       }
     }
     if (SHARE) {
-      b.s[0] = scales[gb + gown];
-      if (!SYM) b.z[0] = zeros[gb + gown];
+      b.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * gown, 0, 0);
+      if (!SYM) b.z[0] = __builtin_amdgcn_raw_buffer_load_b8(rz, gown, 0, 0);
     }
   };
 
+  static_assert(RING == 2 || RING == 3, "two or three rows in flight");
   RowBuf<J, SHARE> b0, b1, b2;
-  const int64_t nlast = N - 1;
-  load(b0, n0 < nlast ? n0 : nlast);
-  load(b1, n0 + nw < nlast ? n0 + nw : nlast);
-  load(b2, n0 + 2 * nw < nlast ? n0 + 2 * nw : nlast);
+  load(b0, n0);
+  load(b1, n0 + nw);
+  if constexpr (RING == 3) load(b2, n0 + 2 * nw);
 
   // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, chunk), four planes of 16 bytes ----
   // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t;
@@ -159,6 +165,22 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   }
   __syncthreads();
 
+  // XREG (one row of X): a lane meets the same J chunks of X in every row of W, so it copies
+  // them, with their factors, from LDS into registers once and reads no LDS per row.
+  constexpr bool XREG = MT == 1 && (J <= 2 || (J == 4 && (BLOCK <= 768 || RING <= 2)));   // register budget
+  u32x4 xr[XREG ? J : 1][4];
+  float xf[XREG ? J : 1], xsum[XREG ? J : 1];
+  if constexpr (XREG) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+#pragma unroll
+      for (int o = 0; o < 4; ++o) xr[j][o] = xs[(size_t)o * C + c];
+      xf[j] = fs[c];
+      xsum[j] = sx[c];
+    }
+  }
+
   auto process = [&](const RowBuf<J, SHARE>& b, int64_t row) {
     float acc[MT];
 #pragma unroll
@@ -196,7 +218,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
           const f16x2 h3 = as_f16x2(d8 & 0x00F000F0u);   // 16 q k3, k7
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = xs[((size_t)m * 4 + o) * C + c];
+            const u32x4 xv = XREG ? xr[XREG ? j : 0][o] : xs[((size_t)m * 4 + o) * C + c];
             float t = __builtin_amdgcn_fdot2(h0, as_f16x2(xv[0]), 0.0f, false);
             t = __builtin_amdgcn_fdot2(h1, as_f16x2(xv[1]), t, false);
             t = __builtin_amdgcn_fdot2(h2, as_f16x2(xv[2]), t, false);
@@ -206,10 +228,12 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const float r = __builtin_fmaf(-zf, sx[m * C + c], (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]));
+          const float sxv = XREG ? xsum[XREG ? j : 0] : sx[m * C + c];
+          const float fsv = XREG ? xf[XREG ? j : 0] : fs[m * C + c];
+          const float r = __builtin_fmaf(-zf, sxv, (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]));
           // 2^24 and 2^-e applied as two exact power-of-two products: no overflow unless the
           // chunk's dot product itself overflows
-          acc[m] = __builtin_fmaf((r * 16777216.0f) * fs[m * C + c], s, acc[m]);
+          acc[m] = __builtin_fmaf((r * 16777216.0f) * fsv, s, acc[m]);
         }
       }
     }
@@ -221,72 +245,100 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   };
 
   // sched_barrier keeps the compiler from hoisting one row's work into another's, which would
-  // keep more than three rows of registers live.
-  // Three rows in flight per wave; past the end the loads repeat row N - 1 (never used).
-  for (int64_t n = n0; n < N; n += 3 * nw) {
+  // keep more than RING rows of registers live.  The slots are named, not an array: indexed
+  // slots made the compiler wait for a later row's loads before computing an earlier one.
+  const int64_t step = RING * nw;
+  for (int64_t n = n0; n < N; n += step) {
     process(b0, n);
     __builtin_amdgcn_sched_barrier(0);
-    load(b0, n + 3 * nw < nlast ? n + 3 * nw : nlast);
+    load(b0, n + step);
     __builtin_amdgcn_sched_barrier(0);
     if (n + nw < N) process(b1, n + nw);
     __builtin_amdgcn_sched_barrier(0);
-    load(b1, n + 4 * nw < nlast ? n + 4 * nw : nlast);
+    load(b1, n + nw + step);
     __builtin_amdgcn_sched_barrier(0);
-    if (n + 2 * nw < N) process(b2, n + 2 * nw);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b2, n + 5 * nw < nlast ? n + 5 * nw : nlast);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RING == 3) {
+      if (n + 2 * nw < N) process(b2, n + 2 * nw);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b2, n + 2 * nw + step);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
-template <int MT, int J, int BLOCK>
-hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
-                      const void* packed, const void* scales, const void* zeros, void* Y,
-                      int num_cus, hipStream_t stream) {
-  const int C = (int)(K >> 5);
+// Blocks of one kernel that fit on a compute unit at once (from its register and LDS use),
+// remembered per LDS size: the grid of a persistent kernel is sized to what is resident.
+template <typename Kernel>
+int64_t resident_blocks(Kernel kernel, int block, size_t lds, std::atomic<uint64_t>& memo) {
+  const uint64_t m = memo.load(std::memory_order_relaxed);
+  if (m != 0 && (m >> 8) == lds) return (int64_t)(m & 0xff);
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, block, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    nb = 1;
+  }
+  nb = nb < 1 ? 1 : (nb > 255 ? 255 : nb);
+  memo.store(((uint64_t)lds << 8) | (uint64_t)nb, std::memory_order_relaxed);
+  return nb;
+}
+
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
+hipError_t launch_one(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
+                      const void* scales, const void* zeros, void* Y, int num_cus,
+                      hipStream_t stream) {
+  static std::atomic<uint64_t> memo{0};
+  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING>;
+  const int64_t C = K >> 5;
   const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 8;
   const int64_t wpb = BLOCK / kWave;
   int64_t blocks = (N + wpb - 1) / wpb;
-  const int64_t cap = (int64_t)num_cus * (BLOCK >= 768 ? 1 : 2);
+  const int64_t cap = (int64_t)num_cus * resident_blocks(kernel, BLOCK, lds, memo);
   if (blocks > cap) blocks = cap;
-  const bool full = C == kWave * J;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(BLOCK), lds, stream,
+                     (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,
+                     (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
+  return hipGetLastError();
+}
+
+template <int MT, int J, int BLOCK, int RING>
+hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
+                      const void* packed, const void* scales, const void* zeros, void* Y,
+                      int num_cus, hipStream_t stream) {
+  const bool full = (K >> 5) == kWave * J;
   const bool share = K / g <= kWave;
-#define Q4_GEMV_LAUNCH(SYMV, FULLV, SHAREV)                                                      \
-  hipLaunchKernelGGL((gemv_kernel<MT, J, SYMV, BLOCK, FULLV, SHAREV>), dim3((unsigned)blocks),   \
-                     dim3(BLOCK), lds, stream, (const uint16_t*)X, M, N, (int)K, g,              \
-                     (const u32x4*)packed, (const uint16_t*)scales, (const uint8_t*)zeros,       \
-                     (uint16_t*)Y)
-#define Q4_GEMV_SHARE(SYMV, FULLV)                                                               \
-  if (share) Q4_GEMV_LAUNCH(SYMV, FULLV, true); else Q4_GEMV_LAUNCH(SYMV, FULLV, false)
+#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                     \
+  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING>(X, M, N, K, g, packed, scales, \
+                                                             zeros, Y, num_cus, stream)
+#define Q4_GEMV_SHARE(SYMV, FULLV)                                                           \
+  if (share) { Q4_GEMV_ONE(SYMV, FULLV, true); } else { Q4_GEMV_ONE(SYMV, FULLV, false); }
   if (sym) {
     if (full) { Q4_GEMV_SHARE(true, true); } else { Q4_GEMV_SHARE(true, false); }
   } else {
     if (full) { Q4_GEMV_SHARE(false, true); } else { Q4_GEMV_SHARE(false, false); }
   }
 #undef Q4_GEMV_SHARE
-#undef Q4_GEMV_LAUNCH
-  return hipGetLastError();
+#undef Q4_GEMV_ONE
 }
 
 template <int MT>
 hipError_t launch_mt(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int num_cus, hipStream_t stream) {
-  if (K <= 2048) return launch_mtj<MT, 1, 1024>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
-  if (K <= 4096) return launch_mtj<MT, 2, (MT == 1 ? 1024 : 768)>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+  if (K <= 2048) return launch_mtj<MT, 1, 1024, 3>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+  if (K <= 4096) return launch_mtj<MT, 2, (MT == 1 ? 1024 : 768), 3>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   if constexpr (MT == 1) {
     if (K <= 8192) {
-      // Whole rows per wave: pick the block size (8, 12 or 16 waves per compute unit) that
-      // minimises (rows of the busiest wave) x (waves sharing a compute unit).
+      // Whole rows per wave, X held in registers: 12 waves per compute unit with three rows in
+      // flight, or 16 waves with two when that spreads the rows more evenly (it minimises
+      // (rows of the busiest wave) x (waves per unit)).  The 16-wave form fits its registers
+      // only with shared scale loads (at most 64 groups) on full 8192-wide rows.
       auto cost = [&](int64_t w) { return ((N + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w)) * w; };
-      const int64_t c8 = cost(8), c12 = cost(12), c16 = cost(16);
-      if (c16 <= c12 && c16 <= c8)
-        return launch_mtj<1, 4, 1024>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
-      if (c8 < c12)
-        return launch_mtj<1, 4, 512>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
-      return launch_mtj<1, 4, 768>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+      const bool lean = K == 8192 && K / g <= kWave;
+      if (lean && cost(16) < cost(12))
+        return launch_mtj<1, 4, 1024, 2>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+      return launch_mtj<1, 4, 768, 3>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
     }
-    if (K <= 16384) return launch_mtj<1, 8, 512>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
+    if (K <= 16384) return launch_mtj<1, 8, 512, 3>(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus, stream);
   }
   return hipErrorInvalidValue;
 }

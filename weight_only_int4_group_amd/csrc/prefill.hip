@@ -61,12 +61,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float c1, float 
   return u32x4{pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5), pack_bf16x2(w6, w7)};
 }
 
-// Raw-buffer resource over [base, base + bytes): loads at offsets >= bytes return 0.
-constexpr int kBufferFlags = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
-}
-
 // 16 bytes per lane, global -> LDS: lane i writes LDS bytes [lds + 16 i, lds + 16 i + 16).
 // `base` and `lds` are wave-uniform; the instruction has no register result.
 __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t lds) {

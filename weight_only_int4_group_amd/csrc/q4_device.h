@@ -42,4 +42,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Raw-buffer resource over [base, base + bytes): loads at offsets >= bytes read no memory and
+// return 0.  kBufferNT marks a load non-temporal (streamed once, not kept in the caches).
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kBufferNT = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
 }  // namespace q4
