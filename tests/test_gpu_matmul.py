@@ -117,6 +117,23 @@ def test_prefill_ragged(M, N, K, g):
         _check_full(X_bits, W_bits, g, mode, "prefill-ragged", ("auto", "gemm"))
 
 
+@pytest.mark.parametrize("M,N,K,g", [(589, 22000, 384, 128), (512, 32768, 256, 32),
+                                     (1024, 16384, 512, 256), (600, 21800, 640, 64)])
+def test_prefill_large_tiles(M, N, K, g):
+    """Shapes with at least as many 256 x 256 tiles as a 256-CU device has compute units, so
+    the GEMM takes its 256-row tile: ragged M and N, odd and even step counts, every g."""
+    import torch
+    from tests.gpu_util import log
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // 256) * -(-N // 256)
+    log(f"large-tile case M={M} N={N} K={K} g={g}: {tiles} tiles on {cus} compute units")
+    rng = np.random.default_rng(M + N + K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full(X_bits, W_bits, g, mode, "prefill-large", ("auto",))
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 33, 64, 65, 129, 257])
 @pytest.mark.parametrize("N,K,g", [(100, 96, 32), (37, 256, 64), (128, 4096, 128), (1, 32, 32),
                                    (50, 640, 128), (33, 1024, 256), (20, 8192, 8192)])

@@ -21,6 +21,7 @@
 // one m, written as one 8-byte store into row-major Y.  Blocks are numbered so the tiles that
 // share X rows land on one XCD (one L2).
 #include <type_traits>
+#include <utility>
 
 #include "q4_device.h"
 #include "q4_internal.h"
@@ -29,36 +30,62 @@ namespace q4 {
 namespace {
 
 constexpr int kStepK = 128;                            // k per step
-constexpr int kTileM = 128;                            // X rows per block
 constexpr int kTileN = 256;                            // W rows per block (64 per wave)
 constexpr uint32_t kRowBytes = kStepK * 2;             // one X row of a step in LDS
-constexpr uint32_t kStageBytes = kTileM * kRowBytes;   // 32 KiB
-constexpr uint32_t kWaveDma = kStageBytes / 4;         // bytes each wave copies per step
-constexpr int kDmaOps = kWaveDma / 1024;               // 1 KiB copy instructions per wave
 constexpr uint32_t kSzStage = 4 * (512 + 256);          // scale / zero words per stage
+// X rows per block (TM): 128 (two blocks per compute unit) or 256 (one block; every
+// dequantised weight then serves twice the X rows).
+constexpr int kTileMSmall = 128, kTileMLarge = 256;
 
 // Dequantise 8 codes (one dword, code k in bits 4k..4k+3) into 8 bf16 MFMA operand values.
 // A nibble at bits 0..3 OR-ed into fp16 1024.0 (0x6400) reads as 1024 + q; a nibble at bits
 // 4..7 OR-ed into fp16 64.0 (0x5400, ulp 1/16) reads as 64 + q.  With c1 = -s (1024 + z) and
 // c64 = -s (64 + z), fma(1024 + q, s, c1) = fma(64 + q, s, c64) = s (q - z) exactly in fp32
 // (fp16 scale x 5-bit integer), then rounded once to bf16.
+// The work is split so that it can be spread between matrix instructions: deq_prep forms the
+// four biased fp16 pairs of a dword, deq_pair(i) the i-th packed bf16 pair of the result
+// (k = 2i, 2i + 1 in the permuted order k0 k1 | k2 k3 | k4 k5 | k6 k7).
+struct Biased {
+  f16x2 q0, q1, q2, q3;    // (k0, k4) and (k2, k6) as 1024 + q; (k1, k5) and (k3, k7) as 64 + q
+};
+// (x & mask) | bias as one v_and_or_b32: the compiler otherwise emits an AND and an OR, each
+// with a literal, for every biased pair.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bias) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bias));
+  return r;
+}
 template <bool SYM>
-__device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float c1, float c64) {
+__device__ __forceinline__ Biased deq_prep(uint32_t dw) {
   if (SYM) dw ^= 0x88888888u;                     // two's complement nibble -> q + 8, z = 8
   const uint32_t d8 = dw >> 8;
-  const f16x2 q0 = as_f16x2((dw & 0x000F000Fu) | 0x64006400u);   // k0, k4
-  const f16x2 q1 = as_f16x2((dw & 0x00F000F0u) | 0x54005400u);   // k1, k5
-  const f16x2 q2 = as_f16x2((d8 & 0x000F000Fu) | 0x64006400u);   // k2, k6
-  const f16x2 q3 = as_f16x2((d8 & 0x00F000F0u) | 0x54005400u);   // k3, k7
-  const float w0 = __builtin_fmaf((float)q0[0], s, c1);
-  const float w4 = __builtin_fmaf((float)q0[1], s, c1);
-  const float w1 = __builtin_fmaf((float)q1[0], s, c64);
-  const float w5 = __builtin_fmaf((float)q1[1], s, c64);
-  const float w2 = __builtin_fmaf((float)q2[0], s, c1);
-  const float w6 = __builtin_fmaf((float)q2[1], s, c1);
-  const float w3 = __builtin_fmaf((float)q3[0], s, c64);
-  const float w7 = __builtin_fmaf((float)q3[1], s, c64);
-  return u32x4{pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5), pack_bf16x2(w6, w7)};
+  return Biased{as_f16x2(and_or(dw, 0x000F000Fu, 0x64006400u)), as_f16x2(and_or(dw, 0x00F000F0u, 0x54005400u)),
+                as_f16x2(and_or(d8, 0x000F000Fu, 0x64006400u)), as_f16x2(and_or(d8, 0x00F000F0u, 0x54005400u))};
+}
+__device__ __forceinline__ uint32_t deq_pair(const Biased& b, int i, float s, float c1, float c64) {
+  const f16x2 lo = (i & 1) ? b.q2 : b.q0;
+  const f16x2 hi = (i & 1) ? b.q3 : b.q1;
+  const int h = i >> 1;
+  return pack_bf16x2(__builtin_fmaf((float)lo[h], s, c1), __builtin_fmaf((float)hi[h], s, c64));
+}
+template <bool SYM>
+__device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float c1, float c64) {
+  const Biased b = deq_prep<SYM>(dw);
+  return u32x4{deq_pair(b, 0, s, c1, c64), deq_pair(b, 1, s, c1, c64), deq_pair(b, 2, s, c1, c64),
+               deq_pair(b, 3, s, c1, c64)};
+}
+
+// acc += a b on the matrix core with the accumulator tied to its AGPRs, so that a wave's 256
+// accumulators stay in place (the builtin lets the register allocator move them between
+// AGPRs and VGPRs around every MFMA).  The compiler does not look inside the asm, so the
+// caller owns the hazards: the vector instruction that writes a (or b) must come at least
+// three instructions before the MFMA that reads it, the accumulator must not be rewritten by
+// anything but this MFMA, and drain_mfma() must run before the accumulators are read.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void drain_mfma() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // 16 bytes per lane, global -> LDS: lane i writes LDS bytes [lds + 16 i, lds + 16 i + 16).
@@ -92,19 +119,30 @@ __device__ __forceinline__ void step_barrier() {
 template <int R>
 using Slot = std::integral_constant<int, R>;
 
+// f(0), f(1), ..., f(N - 1) with compile-time arguments: straight-line code that does not
+// depend on the unroller's size limits.
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
 // EDGE = false: every tile of the launch is full (256 W rows, 128 X rows in range), so the
 // per-lane parts of all addresses are the same for every row group and the rest is
 // wave-uniform.  EDGE = true: the last row and / or column of tiles of a ragged shape; X rows
 // past M are clamped to row M - 1 and W rows past N read as 0 (their outputs are dropped).
-template <bool SYM, bool EDGE>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+template <int TM, bool SYM, bool EDGE>
+__global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, int lg,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y, int tiles_m, int tiles_n,
     int edge_row, int vec_store) {
-  constexpr int MB = kTileM / 16;    // 16-row blocks of X
-  constexpr int NB = 4;              // 16-row blocks of W per wave
-  constexpr int RW = kTileM / 4;     // X rows each wave copies per step
+  static_assert(TM == kTileMSmall || TM == kTileMLarge, "tile of 128 or 256 X rows");
+  constexpr int MB = TM / 16;                          // 16-row blocks of X
+  constexpr int NB = 4;                                // 16-row blocks of W per wave
+  constexpr int RW = TM / 4;                           // X rows each wave copies per step
+  constexpr uint32_t kStageBytes = TM * kRowBytes;     // 32 or 64 KiB
+  constexpr uint32_t kWaveDma = kStageBytes / 4;       // bytes each wave copies per step
+  constexpr int kDmaOps = kWaveDma / 1024;             // 1 KiB copy instructions per wave
 
   // Two X stages, then (full tiles) two stages of the scale and zero-point words of the
   // block's W rows: per stage and wave, 64 rows x 8 bytes of scales and 64 rows x 4 bytes of
@@ -131,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     bm = t / tiles_n;
     bn = t - bm * tiles_n;
   }
-  const int m0 = bm * kTileM, n0 = bn * kTileN;
+  const int m0 = bm * TM, n0 = bn * kTileN;
   const int KT = K / kStepK;
   const int G = K >> lg;
   const uint32_t xrow_bytes = (uint32_t)K * 2u;
@@ -205,6 +243,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       if (EDGE) copy_to_lds(src, dma_off[i], dst + 1024u * i);
       else copy_to_lds(src + (size_t)(RW * wave + 4 * i) * K, dma_off[0] ^ (64u * (i & 3)), dst + 1024u * i);
     }
+  };
+  auto copy_x_piece = [&](int buf, int kt, int i) {
+    const uint16_t* src = xblk + (size_t)min(kt, KT - 1) * kStepK;
+    const uint32_t dst = lds_wave + (uint32_t)buf * kStageBytes;
+    if (EDGE) copy_to_lds(src, dma_off[i], dst + 1024u * i);
+    else copy_to_lds(src + (size_t)(RW * wave + 4 * i) * K, dma_off[0] ^ (64u * (i & 3)), dst + 1024u * i);
   };
   auto copy_sz = [&](int buf, int kt) {
     const uint32_t gs = (uint32_t)((min(kt, KT - 1) * kStepK) >> lg);
@@ -297,23 +341,129 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     step_barrier();
   };
 
-  copy_x(0, 0);
-  if (!EDGE) copy_sz(0, 0);
-  load_w(Slot<0>{}, 0);
-  asm volatile("" ::"v"(wq[0][0]), "v"(wq[0][1]), "v"(wq[0][2]), "v"(wq[0][3]));
-  if (EDGE) {
-    asm volatile("" ::"v"(ws[0][0]), "v"(ws[0][1]), "v"(ws[0][2]), "v"(ws[0][3]));
-    if (!SYM) asm volatile("" ::"v"(wz[0][0]), "v"(wz[0][1]), "v"(wz[0][2]), "v"(wz[0][3]));
-  }
-  step_barrier();
+  if constexpr (TM == kTileMSmall) {
+    copy_x(0, 0);
+    if (!EDGE) copy_sz(0, 0);
+    load_w(Slot<0>{}, 0);
+    asm volatile("" ::"v"(wq[0][0]), "v"(wq[0][1]), "v"(wq[0][2]), "v"(wq[0][3]));
+    if (EDGE) {
+      asm volatile("" ::"v"(ws[0][0]), "v"(ws[0][1]), "v"(ws[0][2]), "v"(ws[0][3]));
+      if (!SYM) asm volatile("" ::"v"(wz[0][0]), "v"(wz[0][1]), "v"(wz[0][2]), "v"(wz[0][3]));
+    }
+    step_barrier();
 
-  // Straight-line body of two steps (one per buffer / register slot); an odd last step follows.
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(Slot<0>{}, kt);
-    step(Slot<1>{}, kt + 1);
+    // Straight-line body of two steps (one per buffer / register slot); an odd last step follows.
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      step(Slot<0>{}, kt);
+      step(Slot<1>{}, kt + 1);
+    }
+    if (kt < KT) step(Slot<0>{}, kt);
+  } else {
+    // One wave per SIMD.  A step is 64 groups g = (ks, mb), each four MFMAs (X rows 16 mb..
+    // x the wave's 64 W rows, sub-step ks) followed by a quarter of a dequantisation for the
+    // next sub-step (for ks = 3: sub-step 0 of the next step, whose codes and scales this wave
+    // loaded itself) and the LDS read of the X fragment two groups ahead.  sched_barrier keeps
+    // the groups in order, which is what makes the MFMA asm safe: an operand written in group
+    // g is first read in group g + 1 or later, behind at least three MFMAs, and every
+    // accumulator is rewritten only by its own MFMA, 16 groups later.
+    u32x4 a[2][NB];                          // operands of sub-step ks (slot ks & 1)
+    float sc[2][NB], cc1[2][NB], cc64[2][NB];   // per step slot: scale, -s (1024 + z), -s (64 + z)
+
+    auto prep_scales = [&](auto S, int kt) {
+      constexpr int R = decltype(S)::value;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t sbits, zbits;
+        if (EDGE) {
+          sbits = ws[R][nb];
+          zbits = wz[R][nb];
+        } else {
+          const uint32_t gs = (uint32_t)((kt * kStepK) >> lg);
+          const uint32_t par = rg_r + gs;
+          const uint8_t* st = xl + 2u * kStageBytes + (uint32_t)R * kSzStage;
+          sbits = *reinterpret_cast<const uint16_t*>(st + (uint32_t)wave * 512u + (uint32_t)li * 8u + 2u * gl +
+                                                     2u * (par & 1u) + 128u * nb);
+          zbits = SYM ? 8u : (uint32_t)st[2048u + (uint32_t)wave * 256u + (uint32_t)li * 4u + gl + (par & 3u) + 64u * nb];
+        }
+        sc[R][nb] = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+        const float zf = (float)zbits;
+        cc1[R][nb] = -sc[R][nb] * (1024.0f + zf);
+        cc64[R][nb] = -sc[R][nb] * (64.0f + zf);
+      }
+    };
+    // Wait for this wave's loads of the step in slot R (codes; everything issued before them).
+    auto wait_codes = [&wq, &ws, &wz](auto S) {
+      constexpr int R = decltype(S)::value;
+      asm volatile("" ::"v"(wq[R][0]), "v"(wq[R][1]), "v"(wq[R][2]), "v"(wq[R][3]));
+      if (EDGE) {
+        asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
+        if (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
+      }
+    };
+
+    auto step_large = [&](auto S, int kt) {
+      constexpr int R = decltype(S)::value;
+      const uint8_t* xs = xl + (uint32_t)R * kStageBytes;
+      constexpr int NG = 4 * MB;          // groups per step
+      constexpr int XA = 2;               // X fragments read this many groups ahead
+      auto xfrag = [&](int g) {
+        return *reinterpret_cast<const bf16x8*>(xs + (g % MB) * 16 * kRowBytes + (rd_off ^ (16u * (g / MB))));
+      };
+      bf16x8 bx[XA + 1];
+#pragma unroll
+      for (int g = 0; g < XA; ++g) bx[g] = xfrag(g);
+      Biased bq;
+      for_each_index([&](auto GC) {
+        constexpr int g = decltype(GC)::value;
+        constexpr int ks = g / MB, mb = g % MB;
+        // The next step's loads, spread over the first groups so that the wave never stalls
+        // on a long run of memory instructions: codes first (needed soonest), then one X
+        // copy per group, then the scale / zero words.
+        if constexpr (g == 0) load_w(Slot<R ^ 1>{}, kt + 1);
+        if constexpr (g < kDmaOps) copy_x_piece(R ^ 1, kt + 1, g);
+        if constexpr (g == kDmaOps) { if (!EDGE) copy_sz(R ^ 1, kt + 1); }
+        if constexpr (g + XA < NG) bx[(g + XA) % (XA + 1)] = xfrag(g + XA);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mfma_acc(acc[nb][mb], a[ks & 1][nb], bx[g % (XA + 1)]);
+        constexpr int nbw = mb >> 2, piece = mb & 3;
+        if constexpr (ks < 3) {
+          if constexpr (piece == 0) bq = deq_prep<SYM>(wq[R][nbw][ks + 1]);
+          a[(ks + 1) & 1][nbw][piece] = deq_pair(bq, piece, sc[R][nbw], cc1[R][nbw], cc64[R][nbw]);
+        } else {
+          if constexpr (piece == 0) bq = deq_prep<SYM>(wq[R ^ 1][nbw][0]);
+          a[0][nbw][piece] = deq_pair(bq, piece, sc[R ^ 1][nbw], cc1[R ^ 1][nbw], cc64[R ^ 1][nbw]);
+        }
+        if constexpr (ks == 2 && mb == MB - 1) {
+          wait_codes(Slot<R ^ 1>{});
+          prep_scales(Slot<R ^ 1>{}, kt + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, NG>{});
+      step_barrier();
+    };
+
+    copy_x(0, 0);
+    if (!EDGE) copy_sz(0, 0);
+    load_w(Slot<0>{}, 0);
+    wait_codes(Slot<0>{});
+    prep_scales(Slot<0>{}, 0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a[0][nb] = dequant8<SYM>(wq[0][nb][0], sc[0][nb], cc1[0][nb], cc64[0][nb]);
+    step_barrier();
+
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      step_large(Slot<0>{}, kt);
+      step_large(Slot<1>{}, kt + 1);
+    }
+    if (kt < KT) step_large(Slot<0>{}, kt);
+    drain_mfma();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+a"(acc[nb][mb]));
   }
-  if (kt < KT) step(Slot<0>{}, kt);
 
   // D[n][m]: lane (li, lq) holds n = 4 lq + e (e = 0..3) of column m = li.
 #pragma unroll
@@ -337,17 +487,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
 }
 
-template <bool SYM>
-hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
-                      const void* scales, const void* zeros, void* Y, hipStream_t stream) {
-  const int full_m = (int)(M / kTileM), full_n = (int)(N / kTileN);
-  const int tiles_m = (int)((M + kTileM - 1) / kTileM);
+template <int TM, bool SYM>
+hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
+                     const void* scales, const void* zeros, void* Y, hipStream_t stream) {
+  const int full_m = (int)(M / TM), full_n = (int)(N / kTileN);
+  const int tiles_m = (int)((M + TM - 1) / TM);
   const int tiles_n = (int)((N + kTileN - 1) / kTileN);
   const int vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 7) == 0);
   const int64_t full_blocks = (int64_t)full_m * full_n;
   if ((int64_t)tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
   if (full_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<SYM, false>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, SYM, false>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, full_m, full_n, 0, vec);
     const hipError_t e = hipGetLastError();
@@ -358,13 +508,23 @@ hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, co
   const int edge_row = tiles_m != full_m;
   const int64_t edge_blocks = (edge_row ? tiles_n : 0) + (tiles_n != full_n ? full_m : 0);
   if (edge_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<SYM, true>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, SYM, true>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, tiles_m, tiles_n,
                        edge_row, vec);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <bool SYM>
+hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
+                      const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
+  // The 256-row tile runs one block per compute unit: take it when its tiles fill every unit.
+  const int64_t large_tiles = ((M + kTileMLarge - 1) / kTileMLarge) * ((N + kTileN - 1) / kTileN);
+  if (large_tiles >= num_cus)
+    return launch_tm<kTileMLarge, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  return launch_tm<kTileMSmall, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
 }
 
 }  // namespace
@@ -374,16 +534,16 @@ bool prefill_fits(int64_t M, int64_t N, int64_t K, int g) {
   // must span < 2 GiB.
   const int64_t lim = int64_t(1) << 31;
   return M >= kPrefillMinM && K % kStepK == 0 && g >= 32 && (g & (g - 1)) == 0 &&
-         (int64_t)kTileM * K * 2 < lim && N * (K / 2) < lim && N * (K / g) * 2 < lim;
+         (int64_t)kTileMLarge * K * 2 < lim && N * (K / 2) < lim && N * (K / g) * 2 < lim;
 }
 
 hipError_t launch_prefill(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
                           const void* packed, const void* scales, const void* zeros, void* Y,
-                          hipStream_t stream) {
+                          int num_cus, hipStream_t stream) {
   int lg = 0;
   while ((1 << lg) < g) ++lg;
-  return sym ? launch_sym<true>(X, M, N, K, lg, packed, scales, zeros, Y, stream)
-             : launch_sym<false>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  return sym ? launch_sym<true>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream)
+             : launch_sym<false>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream);
 }
 
 }  // namespace q4

@@ -145,7 +145,7 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
   if (kernel == Q4_KERNEL_DECODE)
     return finish(q4::launch_decode(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   if (q4::prefill_fits(M, N, K, g))
-    return finish(q4::launch_prefill(X, M, N, K, g, sym, packed, scales, zeros, Y, s));
+    return finish(q4::launch_prefill(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
 }
 

@@ -30,7 +30,7 @@ hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool
 constexpr int64_t kPrefillMinM = 512;
 bool prefill_fits(int64_t M, int64_t N, int64_t K, int g);
 hipError_t launch_prefill(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
-                          const void* packed, const void* scales, const void* zeros, void* Y,
+                          const void* packed, const void* scales, const void* zeros, void* Y, int num_cus,
                           hipStream_t stream);
 
 // MFMA GEMM for any M >= 1.
