@@ -62,11 +62,18 @@ __device__ __forceinline__ Biased deq_prep(uint32_t dw) {
   return Biased{as_f16x2(and_or(dw, 0x000F000Fu, 0x64006400u)), as_f16x2(and_or(dw, 0x00F000F0u, 0x54005400u)),
                 as_f16x2(and_or(d8, 0x000F000Fu, 0x64006400u)), as_f16x2(and_or(d8, 0x00F000F0u, 0x54005400u))};
 }
-__device__ __forceinline__ uint32_t deq_pair(const Biased& b, int i, float s, float c1, float c64) {
+// The two fp32 values of pair i (exact), then the pair packed to bf16.
+__device__ __forceinline__ void deq_fmas(const Biased& b, int i, float s, float c1, float c64, float& w0, float& w1) {
   const f16x2 lo = (i & 1) ? b.q2 : b.q0;
   const f16x2 hi = (i & 1) ? b.q3 : b.q1;
   const int h = i >> 1;
-  return pack_bf16x2(__builtin_fmaf((float)lo[h], s, c1), __builtin_fmaf((float)hi[h], s, c64));
+  w0 = __builtin_fmaf((float)lo[h], s, c1);
+  w1 = __builtin_fmaf((float)hi[h], s, c64);
+}
+__device__ __forceinline__ uint32_t deq_pair(const Biased& b, int i, float s, float c1, float c64) {
+  float w0, w1;
+  deq_fmas(b, i, s, c1, c64, w0, w1);
+  return pack_bf16x2(w0, w1);
 }
 template <bool SYM>
 __device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float c1, float c64) {
@@ -417,23 +424,38 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       for_each_index([&](auto GC) {
         constexpr int g = decltype(GC)::value;
         constexpr int ks = g / MB, mb = g % MB;
-        // The next step's loads, spread over the first groups so that the wave never stalls
-        // on a long run of memory instructions: codes first (needed soonest), then one X
-        // copy per group, then the scale / zero words.
+        constexpr int nbw = mb >> 2, piece = mb & 3;
+        constexpr bool next = ks == 3;                 // dequantising sub-step 0 of the next step
+        constexpr int dst = next ? 0 : (ks + 1) & 1;
+        constexpr int S2 = next ? (R ^ 1) : R;         // step slot of the codes and scales
+        const bf16x8 b = bx[g % (XA + 1)];
+        // Four slots, each one MFMA and then a little other work, so that the wave issues the
+        // other work while the MFMA executes.  Slot 0: this group's LDS read two groups ahead
+        // and, in the first groups, one of the next step's loads (codes first, then one X
+        // copy per group, then the scale / zero words).
+        mfma_acc(acc[0][mb], a[ks & 1][0], b);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (g + XA < NG) bx[(g + XA) % (XA + 1)] = xfrag(g + XA);
         if constexpr (g == 0) load_w(Slot<R ^ 1>{}, kt + 1);
         if constexpr (g < kDmaOps) copy_x_piece(R ^ 1, kt + 1, g);
         if constexpr (g == kDmaOps) { if (!EDGE) copy_sz(R ^ 1, kt + 1); }
-        if constexpr (g + XA < NG) bx[(g + XA) % (XA + 1)] = xfrag(g + XA);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) mfma_acc(acc[nb][mb], a[ks & 1][nb], bx[g % (XA + 1)]);
-        constexpr int nbw = mb >> 2, piece = mb & 3;
-        if constexpr (ks < 3) {
-          if constexpr (piece == 0) bq = deq_prep<SYM>(wq[R][nbw][ks + 1]);
-          a[(ks + 1) & 1][nbw][piece] = deq_pair(bq, piece, sc[R][nbw], cc1[R][nbw], cc64[R][nbw]);
-        } else {
-          if constexpr (piece == 0) bq = deq_prep<SYM>(wq[R ^ 1][nbw][0]);
-          a[0][nbw][piece] = deq_pair(bq, piece, sc[R ^ 1][nbw], cc1[R ^ 1][nbw], cc64[R ^ 1][nbw]);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Slot 1: the biased fp16 pairs of a new code dword.
+        mfma_acc(acc[1][mb], a[ks & 1][1], b);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (piece == 0) bq = deq_prep<SYM>(next ? wq[R ^ 1][nbw][0] : wq[R][nbw][ks + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        // Slot 2: the two exact products of this group's pair.
+        mfma_acc(acc[2][mb], a[ks & 1][2], b);
+        __builtin_amdgcn_sched_barrier(0);
+        float w0, w1;
+        deq_fmas(bq, piece, sc[S2][nbw], cc1[S2][nbw], cc64[S2][nbw], w0, w1);
+        __builtin_amdgcn_sched_barrier(0);
+        // Slot 3: the pair packed into the operand; before sub-step 3, this wave's next codes
+        // are waited for and the next step's scales formed.
+        mfma_acc(acc[3][mb], a[ks & 1][3], b);
+        __builtin_amdgcn_sched_barrier(0);
+        a[dst][nbw][piece] = pack_bf16x2(w0, w1);
         if constexpr (ks == 2 && mb == MB - 1) {
           wait_codes(Slot<R ^ 1>{});
           prep_scales(Slot<R ^ 1>{}, kt + 1);
