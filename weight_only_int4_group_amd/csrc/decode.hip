@@ -99,6 +99,81 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
   float* fx = reinterpret_cast<float*>(lds4 + (size_t)T * DPT * 4 * MP);  // [T][16]: 2^-e
   f32x4* red = reinterpret_cast<f32x4*>(fx + (size_t)T * 16);             // [waves][64]
 
+  // This wave: row-block slot r of each group of RB row blocks, tiles [t_beg, t_end) of K.
+  const int r = w / KS, part = w - r * KS;
+  const int TPP = (T + KS - 1) / KS;
+  const int t_beg = min(part * TPP, T), t_end = min(t_beg + TPP, T);
+  const int NT = t_end - t_beg;
+  const int NGR = (NB + RB - 1) / RB;
+  const size_t rowbytes = (size_t)K >> 1;
+
+  // Ring of P tiles.  Loads are unconditional, from clamped tiles (t <= t_end - 1): a load
+  // under a branch would make the compiler wait for every load in flight before the next use.
+  uint32_t wb[P][DPT];
+  uint32_t sb[P], zb[P];
+  const uint8_t* pr = packed;
+  const uint16_t* sr = scales;
+  const uint8_t* zr = zeros;
+  int lt = 0, lg = 0, lgi = 0;
+  auto load_next = [&](int i) {
+    const int t = min(lt, t_end - 1);
+    load_dwords<DPT>(wb[i], pr + (size_t)t * (TK / 2));
+    if (!WIN) {
+      const int gg = lt < t_end ? lg : (t_end - 1) / TPG;
+      sb[i] = sr[gg];
+      if (!SYM) zb[i] = zr[gg];
+    }
+    ++lt;
+    if (++lgi == TPG) { lgi = 0; ++lg; }
+  };
+  // Windows (WIN): the scales / zeros of the P tiles (= P groups) of one chunk; the next
+  // chunk's window is loaded at the start of the current one.
+  constexpr int SW = WIN ? P / 2 : 1, ZW = WIN ? P / 4 : 1;
+  uint32_t cs[SW], cz[ZW], ns[SW], nz[ZW];
+  auto load_window = [&](uint32_t (&ds)[SW], uint32_t (&dz)[ZW], int c) {
+    const int t = min(t_beg + c * P, t_end - P);
+    const uint32_t* s4 = reinterpret_cast<const uint32_t*>(sr + t);
+#pragma unroll
+    for (int v = 0; v < SW; v += 4) {
+      const u32x4 x4 = *reinterpret_cast<const u32x4*>(s4 + v);
+      ds[v] = x4[0]; ds[v + 1] = x4[1]; ds[v + 2] = x4[2]; ds[v + 3] = x4[3];
+    }
+    if (!SYM) {
+      const uint32_t* z4 = reinterpret_cast<const uint32_t*>(zr + t);
+      if constexpr (ZW == 2) {
+        const u32x2 x2 = *reinterpret_cast<const u32x2*>(z4);
+        dz[0] = x2[0]; dz[1] = x2[1];
+      } else {
+#pragma unroll
+        for (int v = 0; v < ZW; v += 4) {
+          const u32x4 x4 = *reinterpret_cast<const u32x4*>(z4 + v);
+          dz[v] = x4[0]; dz[v + 1] = x4[1]; dz[v + 2] = x4[2]; dz[v + 3] = x4[3];
+        }
+      }
+    }
+  };
+  // Point the ring at row block nb = gi RB + r and request its first P tiles (wave-uniform).
+  auto begin_group = [&](int gi) {
+    const int nb = gi * RB + r;
+    if (nb < NB && NT > 0) {
+      // Rows past N (ragged last block) read row N - 1; their outputs are not stored.
+      const int n = min(nb * 16 + j, N - 1);
+      pr = packed + (size_t)n * rowbytes + q * (TK / 8);
+      sr = scales + (size_t)n * G;
+      zr = zeros + (size_t)n * G;
+      lt = t_beg;
+      lg = t_beg / TPG;
+      lgi = t_beg - lg * TPG;
+      if (WIN) load_window(cs, cz, 0);
+#pragma unroll
+      for (int i = 0; i < P; ++i) load_next(i);
+    }
+  };
+
+  // The first group's weights are requested before X is staged, so that HBM latency overlaps
+  // the staging.
+  if (blockIdx.x < NGR) begin_group(blockIdx.x);
+
   // ---- X -> LDS: TK/8 threads per (m, tile) of the M rows, one octet of 8 values each, four
   // octets per thread in flight; rows M..15 get the factor 0. ----
   constexpr int OPT = TK / 8;                 // octets per tile
@@ -151,71 +226,11 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
   asm volatile("" : "+v"(bias));   // keep in a VGPR: (x & mask) | bias -> one v_and_or_b32
   const int jx = min(j, MP - 1);
 
-  // This wave: row-block slot r of each group of RB row blocks, tiles [t_beg, t_end) of K.
-  const int r = w / KS, part = w - r * KS;
-  const int TPP = (T + KS - 1) / KS;
-  const int t_beg = min(part * TPP, T), t_end = min(t_beg + TPP, T);
-  const int NT = t_end - t_beg;
-  const int NGR = (NB + RB - 1) / RB;
-  const size_t rowbytes = (size_t)K >> 1;
-
   for (int gi = blockIdx.x; gi < NGR; gi += gridDim.x) {            // block-uniform
+    if (gi != (int)blockIdx.x) begin_group(gi);
     const int nb = gi * RB + r;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (nb < NB && NT > 0) {                                          // wave-uniform
-      // Rows past N (ragged last block) read row N - 1; their outputs are not stored.
-      const int n = min(nb * 16 + j, N - 1);
-      const uint8_t* pr = packed + (size_t)n * rowbytes + q * (TK / 8);
-      const uint16_t* sr = scales + (size_t)n * G;
-      const uint8_t* zr = zeros + (size_t)n * G;
-
-      // Ring of P tiles.  Loads are unconditional, from clamped tiles (t <= t_end - 1): a load
-      // under a branch would make the compiler wait for every load in flight before the next
-      // use.
-      uint32_t wb[P][DPT];
-      uint32_t sb[P], zb[P];
-      int lt = t_beg, lg = t_beg / TPG, lgi = t_beg - (t_beg / TPG) * TPG;
-      auto load_next = [&](int i) {
-        const int t = min(lt, t_end - 1);
-        load_dwords<DPT>(wb[i], pr + (size_t)t * (TK / 2));
-        if (!WIN) {
-          const int gg = lt < t_end ? lg : (t_end - 1) / TPG;
-          sb[i] = sr[gg];
-          if (!SYM) zb[i] = zr[gg];
-        }
-        ++lt;
-        if (++lgi == TPG) { lgi = 0; ++lg; }
-      };
-      // Windows (WIN): the scales / zeros of the P tiles (= P groups) of one chunk; the
-      // next chunk's window is loaded at the start of the current one.
-      constexpr int SW = WIN ? P / 2 : 1, ZW = WIN ? P / 4 : 1;
-      uint32_t cs[SW], cz[ZW], ns[SW], nz[ZW];
-      auto load_window = [&](uint32_t (&ds)[SW], uint32_t (&dz)[ZW], int c) {
-        const int t = min(t_beg + c * P, t_end - P);
-        const uint32_t* s4 = reinterpret_cast<const uint32_t*>(sr + t);
-#pragma unroll
-        for (int v = 0; v < SW; v += 4) {
-          const u32x4 x4 = *reinterpret_cast<const u32x4*>(s4 + v);
-          ds[v] = x4[0]; ds[v + 1] = x4[1]; ds[v + 2] = x4[2]; ds[v + 3] = x4[3];
-        }
-        if (!SYM) {
-          const uint32_t* z4 = reinterpret_cast<const uint32_t*>(zr + t);
-          if constexpr (ZW == 2) {
-            const u32x2 x2 = *reinterpret_cast<const u32x2*>(z4);
-            dz[0] = x2[0]; dz[1] = x2[1];
-          } else {
-#pragma unroll
-            for (int v = 0; v < ZW; v += 4) {
-              const u32x4 x4 = *reinterpret_cast<const u32x4*>(z4 + v);
-              dz[v] = x4[0]; dz[v + 1] = x4[1]; dz[v + 2] = x4[2]; dz[v + 3] = x4[3];
-            }
-          }
-        }
-      };
-      if (WIN) load_window(cs, cz, 0);
-#pragma unroll
-      for (int i = 0; i < P; ++i) load_next(i);
-
       for (int t0 = 0; t0 < NT; t0 += P) {
         if (WIN) load_window(ns, nz, t0 / P + 1);
 #pragma unroll
