@@ -53,16 +53,30 @@ __device__ __forceinline__ f16x8 dequant_q_minus_z(uint32_t dw, uint32_t bias, f
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
+// Maximum over each aligned group of L lanes (L = 4, 8 or 16, inside one 16-lane DPP row),
+// returned to every lane of the group: DPP moves, no LDS round trips.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(L == 4 || L == 8 || L == 16, "4, 8 or 16 lanes");
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  if (L >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  if (L >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  return v;
+}
+
+// The weights are read 64 bytes per row at a time, the rest of each line one tile later:
+// plain loads keep the line in the cache for that second half.
 template <int DPT>
 __device__ __forceinline__ void load_dwords(uint32_t (&d)[DPT], const uint8_t* p) {
   if constexpr (DPT == 4) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
     d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
   } else if constexpr (DPT == 2) {
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
     d[0] = v[0]; d[1] = v[1];
   } else {
-    d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    d[0] = *reinterpret_cast<const uint32_t*>(p);
   }
 }
 
@@ -199,9 +213,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][c])), fabsf(bf16_hi(v[i][c]))));
-#pragma unroll
-      for (int sh = 1; sh < OPT; sh <<= 1)    // aligned groups of OPT lanes = one (m, tile)
-        amax = fmaxf(amax, __shfl_xor(amax, sh));
+      amax = group_max<OPT>(amax);            // aligned groups of OPT lanes = one (m, tile)
       int e = 0;
       if (amax > 0.0f) {
         int E;
