@@ -35,7 +35,9 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kMaxWaves = 8;        // waves per block at most (2 per SIMD)
+constexpr int kMaxWaves = 8;        // waves sharing one row block at most (K split), and
+                                    // LDS slots for their partial sums
+constexpr int kWideWaves = 16;      // waves per block of the lean (window) variant
 
 // Four 32-bit registers of fp16 pairs (q - z) (x16 for odd positions) from 8 nibbles: a
 // nibble OR-ed into the mantissa of fp16 1024.0 reads 1024 + q, and subtracting 1024 + z
@@ -90,8 +92,9 @@ size_t lds_tail(int64_t K, int g) {
 }
 
 // WIN: one group per tile, window loads of scales / zeros (needs aligned windows, see launch).
-template <int DPT, bool SYM, bool WIN>
-__global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
+// MAXW: waves per block at most (the lean WIN variant fits 16 waves' registers).
+template <int DPT, bool SYM, bool WIN, int MAXW>
+__global__ __launch_bounds__(MAXW * kWave) void decode_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, int g,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y, int RB, int KS) {
@@ -283,11 +286,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
       }
     }
     if (KS > 1) {                                                     // block-uniform
-      red[w * kWave + lane] = acc;
+      // Parts 1..KS-1 of row-block slot r leave their sums in slots r (KS - 1) + part - 1
+      // (RB (KS - 1) <= kMaxWaves of them); part 0 adds them in part order.
+      if (part > 0) red[(r * (KS - 1) + part - 1) * kWave + lane] = acc;
       __syncthreads();
       if (part == 0) {
 #pragma unroll 1
-        for (int pp = 1; pp < KS; ++pp) acc += red[(w + pp) * kWave + lane];
+        for (int pp = 1; pp < KS; ++pp) acc += red[(r * (KS - 1) + pp - 1) * kWave + lane];
       }
       __syncthreads();
     }
@@ -309,42 +314,55 @@ hipError_t launch_cfg(const void* X, int M, int64_t N, int64_t K, int g, const v
   constexpr int TK = 32 * DPT, P = 32 / DPT;
   const size_t lds = lds_bytes(M, K, g);
   // More than 64 KiB of dynamic LDS has to be enabled per kernel (thread-safe one-time init).
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
-          ? hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)
-          : hipErrorInvalidValue;
+  static const hipError_t attr = [] {
+    const void* kernels[] = {reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true, kWideWaves>),
+                             reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true, kMaxWaves>),
+                             reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, false, kMaxWaves>)};
+    for (const void* k : kernels) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
   if (attr != hipSuccess) return attr;
   const int64_t NB = (N + 15) / 16;
   const int64_t T = K / TK;
-  // Row blocks per resident block; with fewer than 8, the spare waves split K.
-  int64_t rb = (NB + num_cus - 1) / num_cus;
-  int RB, KS;
-  if (rb >= kMaxWaves) {
-    RB = kMaxWaves;
-    KS = 1;
-  } else {
+  const int64_t G = K / g;
+  // Row blocks per resident block (RB) and waves splitting each one's K (KS), for a block of at
+  // most maxw waves: with fewer row blocks than waves, the spare waves split K, at most
+  // kMaxWaves ways, with at most kMaxWaves partial sums in LDS.
+  auto split = [&](int maxw, int& RB, int& KS) {
+    const int64_t rb = (NB + num_cus - 1) / num_cus;
+    if (rb >= maxw) {
+      RB = maxw;
+      KS = 1;
+      return;
+    }
     RB = (int)rb;
-    KS = kMaxWaves / RB;
-    while (KS > 1 && (T % KS != 0 || T / KS < 2)) --KS;
-  }
+    KS = min(maxw / RB, kMaxWaves);
+    while (KS > 1 && (T % KS != 0 || T / KS < 2 || RB * (KS - 1) > kMaxWaves)) --KS;
+  };
+  // Window loads: one group per tile, every wave's tile range a whole number of windows, and
+  // 4-byte-aligned windows of scales and zeros in every row.
+  auto windows = [&](int KS) {
+    return (g == TK) && ((T / KS) % P == 0) && (T % KS == 0) && (G % (P < 16 ? P : 16) == 0);
+  };
+  int RB, KS;
+  split(kWideWaves, RB, KS);
+  const bool wide = windows(KS);
+  if (!wide) split(kMaxWaves, RB, KS);
+  const bool win = wide || windows(KS);
   const int64_t groups = (NB + RB - 1) / RB;
   const int64_t blocks = groups < num_cus ? groups : num_cus;
   const int threads = RB * KS * kWave;
-  // Window loads: one group per tile, every wave's tile range a whole number of windows, and
-  // 4-byte-aligned windows of scales and zeros in every row.
-  const int64_t G = K / g;
-  const bool win = (g == TK) && ((T / KS) % P == 0) && (T % KS == 0) &&
-                   (G % (P < 16 ? P : 16) == 0);
-  if (win)
-    hipLaunchKernelGGL((decode_kernel<DPT, SYM, true>), dim3((unsigned)blocks), dim3((unsigned)threads),
-                       lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, RB, KS);
-  else
-    hipLaunchKernelGGL((decode_kernel<DPT, SYM, false>), dim3((unsigned)blocks), dim3((unsigned)threads),
-                       lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, RB, KS);
+#define Q4_DECODE_LAUNCH(WINV, MAXWV)                                                              \
+  hipLaunchKernelGGL((decode_kernel<DPT, SYM, WINV, MAXWV>), dim3((unsigned)blocks), dim3((unsigned)threads), \
+                     lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,          \
+                     (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, RB, KS)
+  if (wide) Q4_DECODE_LAUNCH(true, kWideWaves);
+  else if (win) Q4_DECODE_LAUNCH(true, kMaxWaves);
+  else Q4_DECODE_LAUNCH(false, kMaxWaves);
+#undef Q4_DECODE_LAUNCH
   return hipGetLastError();
 }
 
