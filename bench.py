@@ -77,10 +77,43 @@ def parse_args(argv=None):
     p.add_argument("--layers", type=int, default=6, help="distinct decode weight copies per step")
     p.add_argument("--no-check", action="store_true", help="skip the parity assertion")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the practical-ceiling measurements reported as context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 512 MiB device copy (counter calibration)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args(argv)
+
+
+# --------------------------------------------------------------------------- context
+def measure_context(torch, sets, X5, W5, reps=10):
+    """Practical ceilings on this GPU, measured after the timed steps and reported beside the
+    kernels (not targets): a plain streaming read of the same decode weight bytes (torch
+    reduction over the packed codes of the weight copies, rotating as the GEMV does) and the
+    vendor bf16 GEMM (torch.matmul, hipBLASLt) on the prefill shape with unquantized bf16
+    weights."""
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    views = [s[0].view(torch.int32) for s in sets]
+    read_bytes = views[0].numel() * 4
+    read_ms = timed(lambda i: views[i % len(views)].sum(), reps * len(views))
+    flops = 2.0 * X5.shape[0] * W5.shape[0] * X5.shape[1]
+    mm_ms = timed(lambda i: torch.matmul(X5, W5.t()), reps)
+    return {
+        "stream_read": {"GB/s": round(read_bytes / (read_ms * 1e-3) / 1e9, 1), "bytes": read_bytes,
+                        "how": "torch.sum over the int32 view of one decode weight's packed codes, rotating over the copies"},
+        "vendor_bf16_gemm": {"TFLOP/s": round(flops / (mm_ms * 1e-3) / 1e12, 1), "ms": round(mm_ms, 4),
+                             "how": "torch.matmul (hipBLASLt) X[2048,8192] @ W[8192,8192]^T in bf16, unquantized W"},
+    }
 
 
 # --------------------------------------------------------------------------- counters
@@ -349,6 +382,8 @@ def main(argv=None):
                                   "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4)}},
         "parity_max_tolerance_usage": max_usage,
     }
+    if not args.no_context:
+        out["context"] = measure_context(torch, sets, X5, W5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
     print(json.dumps(out), flush=True)
