@@ -38,6 +38,9 @@ R5  z = clamp(rint(0 - fl32(alpha / scale)), q_min, q_max); symmetric mode store
 R6  codes are stored two per byte, even k in the low nibble; symmetric codes are stored as
     4-bit two's complement.
 R7  x_hat = fp64(scale_fp16) * (q - z)  (exact in fp64).
+R8  the standalone dequantisation returns x_hat rounded once to bf16 or fp16, round half
+    to even (R3); an fp16 result beyond the fp16 range becomes +-inf as IEEE rounding
+    says.  x_hat has at most 15 significant bits and lies in bf16's normal range (or is 0).
 """
 from __future__ import annotations
 
@@ -45,7 +48,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_groups", "quantize_rtn_ref", "unpack_codes_ref",
-    "dequantize_ref", "matmul_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
+    "dequantize_ref", "round_to_bf16_bits_ref", "dequantize_rounded_ref", "matmul_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
     "bits_per_weight", "weight_bytes", "format_math_row",
 ]
 
@@ -171,6 +174,40 @@ def dequantize_ref(packed, scales, zeros, g: int, mode: str) -> np.ndarray:
         raise ValueError("scales/zeros shape does not match packed and g")
     qg = q.reshape(N, K // g, g)
     return (s[..., None] * (qg - z[..., None])).reshape(N, K)
+
+
+BF16_MIN_NORMAL = 2.0 ** -126
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_to_bf16_bits_ref(x) -> np.ndarray:
+    """fp64 -> bf16 bit patterns (uint16), rounding the exact value half to even (R3).
+
+    bf16 keeps 8 significant bits: write x = m * 2**e with 0.5 <= |m| < 1, round m * 2**8 to
+    an integer (ties to even) and scale back.  Defined for 0 and for results in bf16's
+    normal range, which covers every dequantised weight (R8); anything else raises.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    a = np.abs(r)
+    if not np.all((a == 0) | ((a >= BF16_MIN_NORMAL) & (a <= BF16_MAX))):
+        raise ValueError("value outside the range this rounding is defined for")
+    # r has at most 8 significant bits and a normal exponent: exact in fp32, and its bf16
+    # pattern is the top half of the fp32 pattern.
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def dequantize_rounded_ref(packed, scales, zeros, g: int, mode: str, out: str = "bf16"):
+    """x_hat (R7) rounded once to the output format (R8): bf16 bit patterns (uint16) for
+    out="bf16", a float16 array for out="f16"."""
+    xhat = dequantize_ref(packed, scales, zeros, g, mode)
+    if out == "bf16":
+        return round_to_bf16_bits_ref(xhat)
+    if out == "f16":
+        with np.errstate(over="ignore"):
+            return xhat.astype(np.float16)       # numpy rounds fp64 -> fp16 half to even
+    raise ValueError(f"unknown output format {out!r}")
 
 
 def matmul_ref(X_bits, packed, scales, zeros, g: int, mode: str):

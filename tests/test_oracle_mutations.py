@@ -29,6 +29,9 @@ MUTATIONS = {
     "symmetric q_max 8": ('quantize_groups(x, -8, 7, "sym")', 'quantize_groups(x, -8, 8, "sym")'),
     "group index off": ("s[..., None] * (qg - z[..., None])", "np.roll(s, 1, axis=-1)[..., None] * (qg - z[..., None])"),
     "abs dropped in A": ("np.abs(X) @ np.abs(What).T", "X @ What.T"),
+    "bf16 ties away from zero": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m))"),
+    "bf16 7 significant bits": ("np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)", "np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)"),
+    "bf16 truncation": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
 }
 
 
@@ -75,6 +78,9 @@ def _pins_pass(orc, golden_dir):
             x = orc.bf16_bits_to_f32(W_bits).astype(np.float64)
             if np.abs(Y.T - x).max() > 0.6 * np.abs(x).max() / 7 + 1e-12:
                 return False
+        from tests.test_oracle_pins import rounding_pins_hold
+        if not rounding_pins_hold(orc):
+            return False
     except Exception:
         return False
     return True

@@ -181,3 +181,90 @@ def test_one_hot_reads_back_single_weights():
                 zz = 0 if mode == "sym" else int(zeros[n, k // 32])
                 assert Y[k, n] == float(scales[n, k // 32]) * (codes[n, k] - zz)
                 assert A[k, n] == abs(Y[k, n])
+
+
+# --------------------------------------------------------------------------- rounded dequantisation
+BF16_HAND_CASES = {
+        1.0 + 2.0 ** -8: 0x3F80,                  # half an ulp above 1: tie -> even (1.0)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,              # 1.5 ulp: tie -> 1 + 2^-6 (even)
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,     # just above the tie -> up
+        -(1.0 + 2.0 ** -8): 0xBF80,
+        0.0: 0x0000,
+        255.5: 0x4380,                            # 255.5 -> 256 (9 significant bits needed)
+        3.0 * 2.0 ** -24: 0x3440,                 # smallest fp16 scale times 3: exact
+        65504.0 * 15: 0x4970,                     # largest |x_hat|: 982560 -> 983040
+}
+
+
+def _torch_bf16_cases():
+    import torch
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(100000) * np.exp2(rng.uniform(-100, 100, 100000))).astype(np.float32)
+    ties = (rng.integers(1, 2 ** 16, 20000) * 2 + 1).astype(np.float64) * 2.0 ** -9   # odd/2^9: many ties
+    x = np.concatenate([x, ties.astype(np.float32)])
+    return x, torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def rounding_pins_hold(o) -> bool:
+    """The bf16 rounding pins below in compact form (used by the mutation tests)."""
+    got = o.round_to_bf16_bits_ref(np.array(list(BF16_HAND_CASES)))
+    if [int(v) for v in got] != list(BF16_HAND_CASES.values()):
+        return False
+    x, want = _torch_bf16_cases()
+    return bool(np.array_equal(o.round_to_bf16_bits_ref(x.astype(np.float64)), want))
+
+
+def test_bf16_rounding_hand_values():
+    """bf16 keeps 8 significant bits; ties go to the even neighbour (ulp at 1 is 2^-7)."""
+    got = orc.round_to_bf16_bits_ref(np.array(list(BF16_HAND_CASES)))
+    assert [int(v) for v in got] == list(BF16_HAND_CASES.values())
+
+
+def test_bf16_rounding_matches_torch_conversion():
+    """Against an independent routine: torch's fp32 -> bf16 conversion (round to nearest
+    even) on values exact in fp32 across bf16's normal exponent range."""
+    x, want = _torch_bf16_cases()
+    assert np.array_equal(orc.round_to_bf16_bits_ref(x.astype(np.float64)), want)
+
+
+def test_bf16_rounding_rejects_out_of_range():
+    for v in (2.0 ** -130, 1e39, np.inf, np.nan):
+        with pytest.raises(ValueError):
+            orc.round_to_bf16_bits_ref(np.array([v]))
+
+
+@pytest.mark.parametrize("mode", ["asym", "sym"])
+def test_dequantize_rounded_exact_when_representable(mode):
+    """Power-of-two scales make every x_hat = 2^e (q - z) exact in bf16 and fp16 (|q - z| <= 15
+    needs 4 significant bits), so the rounded output must equal x_hat itself."""
+    rng = np.random.default_rng(5)
+    N, K, g = 6, 256, 64
+    q = rng.integers(0, 16, (N, K))
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.exp2(rng.integers(-20, 10, (N, K // g))).astype(np.float16)
+    zeros = rng.integers(0, 16, (N, K // g)).astype(np.uint8)
+    codes = q if mode == "asym" else np.where(q >= 8, q - 16, q)
+    z = zeros.astype(np.int64) if mode == "asym" else np.zeros_like(zeros, dtype=np.int64)
+    xhat = scales.astype(np.float64).repeat(g, axis=1) * (codes - z.repeat(g, axis=1))
+    b = orc.dequantize_rounded_ref(packed, scales, zeros, g, mode, "bf16")
+    assert np.array_equal(orc.bf16_bits_to_f32(b).astype(np.float64), xhat)
+    h = orc.dequantize_rounded_ref(packed, scales, zeros, g, mode, "f16")
+    assert h.dtype == np.float16 and np.array_equal(h.astype(np.float64), xhat)
+
+
+def test_dequantize_rounded_f16_matches_torch_and_overflows():
+    """fp16 output against torch's conversion of the (fp32-exact) products; products beyond
+    65504 (plus half an ulp) become inf."""
+    import torch
+    rng = np.random.default_rng(9)
+    N, K, g = 4, 128, 32
+    packed = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    scales = np.array(rng.uniform(0.5, 30000, (N, K // g)), dtype=np.float16)
+    scales[0, 0] = 65504.0
+    zeros = rng.integers(0, 16, (N, K // g)).astype(np.uint8)
+    for mode in ("asym", "sym"):
+        xhat = orc.dequantize_ref(packed, scales, zeros, g, mode)
+        want = torch.from_numpy(xhat.astype(np.float32)).to(torch.float16).numpy()
+        got = orc.dequantize_rounded_ref(packed, scales, zeros, g, mode, "f16")
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+        assert np.array_equal(np.isinf(got), np.abs(xhat) >= 65520.0)
