@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4_VERSION 10000  /* 1.0.0 */
+#define Q4_VERSION 10100  /* 1.1.0 */
 
 typedef enum {
     Q4_ASYM = 0,   /* uint4 codes [0, 15] with a uint8 zero-point per group */
@@ -69,13 +69,19 @@ typedef enum {
     Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z), fp32 per-group scaling  */
 } q4_kernel_t;
 
+typedef enum {
+    Q4_DTYPE_BF16 = 0,     /* bfloat16 output */
+    Q4_DTYPE_F16 = 1       /* IEEE binary16 output */
+} q4_dtype_t;
+
 enum {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,      /* a required pointer is NULL                                    */
     Q4_ERR_SHAPE = -2,     /* N < 1, K < 1, M < 0, or a size beyond 2^31 - 1                */
     Q4_ERR_GROUP = -3,     /* g < 32, g % 32 != 0, or K % g != 0                             */
-    Q4_ERR_MODE = -4,      /* mode or kernel selector out of range                           */
-    Q4_ERR_ALIGN = -5,     /* W, X or packed not 16-byte aligned; scales or Y not 2-byte     */
+    Q4_ERR_MODE = -4,      /* mode, kernel selector or output type out of range              */
+    Q4_ERR_ALIGN = -5,     /* W, X, packed or a dequantize output not 16-byte aligned; scales
+                              or Y not 2-byte                                                 */
     Q4_ERR_HIP = -6,       /* the HIP runtime rejected a launch                              */
     Q4_ERR_ALIAS = -7,     /* an output buffer overlaps an input or another output          */
     Q4_ERR_UNSUPPORTED = -8 /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
@@ -115,6 +121,25 @@ int q4_quantize_rtn(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode
  */
 int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
               const void* packed, const void* scales, const void* zeros, void* Y, void* stream);
+
+/*
+ * out[N, K] = scale * (q - z) for every weight, rounded once (to nearest even) to bf16 or fp16:
+ * the dequantisation of "DL S067 · Quantization — INT8, INT4, GPTQ, AWQ", §1 "The core math"
+ * (x_hat = scale * (q - z)) with the per-group parameters of "Model Quantization" §1
+ * "Group-wise Quantization".  For callers that feed the dequantised weights to another
+ * library's GEMM.  The value before rounding is exact (an fp16 scale times an integer in
+ * [-15, 15]), so the output is bit-exact; with Q4_DTYPE_F16 a product beyond the fp16 range
+ * becomes +-Inf.
+ *
+ *   N, K, g, mode   as for q4_quantize_rtn; they must describe packed/scales/zeros
+ *   packed, scales  device inputs as produced by q4_quantize_rtn (packed 16-byte aligned)
+ *   zeros   device input; ignored and may be NULL in symmetric mode
+ *   out     device, [N, K] of out_dtype, 16-byte aligned (output; must not overlap an input)
+ *   out_dtype  Q4_DTYPE_BF16 or Q4_DTYPE_F16
+ */
+int q4_dequantize(int64_t N, int64_t K, int32_t g, int32_t mode, const void* packed,
+                  const void* scales, const void* zeros, void* out, int32_t out_dtype,
+                  void* stream);
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
  * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,

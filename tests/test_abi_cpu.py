@@ -26,15 +26,15 @@ def declared_functions():
 def test_library_exports_all_declared_symbols():
     lib = q4.library()
     names = declared_functions()
-    assert names == sorted(["q4_matmul", "q4_matmul_kernel", "q4_quantize_rtn", "q4_select_kernel",
-                            "q4_status_string", "q4_version"])
+    assert names == sorted(["q4_dequantize", "q4_matmul", "q4_matmul_kernel", "q4_quantize_rtn",
+                            "q4_select_kernel", "q4_status_string", "q4_version"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
 def test_version_and_status_strings():
-    assert q4.version() == 10000
+    assert q4.version() == 10100
     for st in range(-8, 1):
         s = q4.status_string(st)
         assert s and s != "unknown status"
@@ -80,6 +80,28 @@ def test_quantize_validation(kw, status):
 ])
 def test_matmul_validation(kw, status):
     assert _mm(**kw) == status
+
+
+def _deq(N=4, K=128, g=32, mode=0, p=B16, s=C16, z=D16, out=0x50000, dtype=0):
+    return q4.library().q4_dequantize(N, K, g, mode, p, s, z, out, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), -2), (dict(K=0), -2), (dict(K=2 ** 31), -2),
+    (dict(g=16), -3), (dict(K=96, g=64), -3),
+    (dict(mode=2), -4), (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(p=0), -1), (dict(s=0), -1), (dict(z=0), -1), (dict(out=0), -1),
+    (dict(p=B16 + 4), -5), (dict(s=C16 + 1), -5), (dict(out=0x50008), -5), (dict(out=0x50002), -5),
+    (dict(out=B16), -7), (dict(out=B16 - 16), -7), (dict(out=C16), -7), (dict(out=D16 - 1008), -7),
+])
+def test_dequantize_validation(kw, status):
+    assert _deq(**kw) == status
+
+
+def test_dequantize_sym_ignores_zeros():
+    # zeros is NULL or overlapping in symmetric mode: only the shape error remains.
+    assert _deq(mode=1, z=0, N=0) == -2
+    assert _deq(mode=1, z=0x50000, K=96, g=64) == -3
 
 
 def test_matmul_m0_and_sym_zeros_null_are_accepted_without_launch():

@@ -13,7 +13,8 @@ import threading
 
 __all__ = [
     "Q4Error", "library", "library_path", "quantize_rtn", "quantize_rtn_into", "matmul",
-    "matmul_into", "select_kernel", "status_string", "version", "MODES", "KERNELS",
+    "matmul_into", "dequantize", "dequantize_into", "select_kernel", "status_string", "version",
+    "MODES", "KERNELS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +50,8 @@ def library() -> ctypes.CDLL:
             lib.q4_matmul.restype = ctypes.c_int
             lib.q4_matmul_kernel.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp, i32, vp]
             lib.q4_matmul_kernel.restype = ctypes.c_int
+            lib.q4_dequantize.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, i32, vp]
+            lib.q4_dequantize.restype = ctypes.c_int
             lib.q4_select_kernel.argtypes = [i64, i64, i64, i32]
             lib.q4_select_kernel.restype = ctypes.c_int
             lib.q4_status_string.argtypes = [ctypes.c_int]
@@ -149,3 +152,36 @@ def matmul(X, packed, scales, zeros, g: int = 128, mode: str = "asym", kernel: s
     Y = torch.empty((X.shape[0], packed.shape[0]), dtype=torch.bfloat16, device=packed.device)
     matmul_into(X, packed, scales, zeros, g, mode, Y, kernel)
     return Y
+
+
+def _out_dtype(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return 0
+    if dtype == torch.float16:
+        return 1
+    raise ValueError(f"out dtype must be bfloat16 or float16, got {dtype}")
+
+
+def dequantize_into(packed, scales, zeros, g: int, mode: str, out) -> None:
+    """q4_dequantize on a caller-provided out[N, K] (bfloat16 or float16; no allocation)."""
+    _check_cuda(packed, scales, zeros, out)
+    if packed.dim() != 2:
+        raise ValueError("packed must be 2-D")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    if tuple(out.shape) != (N, K):
+        raise ValueError(f"shape mismatch: packed {tuple(packed.shape)}, out {tuple(out.shape)}")
+    with __import__("torch").cuda.device(packed.device):
+        st = library().q4_dequantize(N, K, g, _mode(mode), _ptr(packed), _ptr(scales), _ptr(zeros),
+                                     _ptr(out), _out_dtype(out.dtype), _stream(packed.device))
+    if st != 0:
+        raise Q4Error(st, "q4_dequantize")
+
+
+def dequantize(packed, scales, zeros, g: int = 128, mode: str = "asym", dtype=None):
+    """dequant(packed, scales, zeros) as an [N, K] tensor (bfloat16 unless dtype says float16)."""
+    import torch
+    out = torch.empty((packed.shape[0], packed.shape[1] * 2),
+                      dtype=torch.bfloat16 if dtype is None else dtype, device=packed.device)
+    dequantize_into(packed, scales, zeros, g, mode, out)
+    return out

@@ -30,6 +30,7 @@ SOURCES = {
     "gemm.hip": [],
     "prefill.hip": [],
     "decode.hip": [],
+    "dequant.hip": [],
     "q4_abi.cpp": [],
 }
 

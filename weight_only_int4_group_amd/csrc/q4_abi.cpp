@@ -95,8 +95,9 @@ const char* q4_status_string(int status) {
     case Q4_ERR_NULL: return "a required pointer is NULL";
     case Q4_ERR_SHAPE: return "invalid shape: need N >= 1, K >= 1, M >= 0, all <= 2^31-1";
     case Q4_ERR_GROUP: return "invalid group size: need g >= 32, g % 32 == 0 and K % g == 0";
-    case Q4_ERR_MODE: return "invalid mode or kernel selector";
-    case Q4_ERR_ALIGN: return "misaligned pointer: W, X, packed need 16 bytes; scales, Y need 2";
+    case Q4_ERR_MODE: return "invalid mode, kernel selector or output type";
+    case Q4_ERR_ALIGN:
+      return "misaligned pointer: W, X, packed and dequantize's out need 16 bytes; scales, Y need 2";
     case Q4_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case Q4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case Q4_ERR_UNSUPPORTED: return "the chosen kernel does not support this shape";
@@ -147,6 +148,24 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
   if (q4::prefill_fits(M, N, K, g))
     return finish(q4::launch_prefill(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+}
+
+int q4_dequantize(int64_t N, int64_t K, int32_t g, int32_t mode, const void* packed,
+                  const void* scales, const void* zeros, void* out, int32_t out_dtype,
+                  void* stream) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (out_dtype != Q4_DTYPE_BF16 && out_dtype != Q4_DTYPE_F16) return Q4_ERR_MODE;
+  if (!packed || !scales || !out || (mode == Q4_ASYM && !zeros)) return Q4_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+  const int64_t G = K / g;
+  const Range o = range_of(out, N * K * 2);
+  if (overlap(o, range_of(packed, N * K / 2)) || overlap(o, range_of(scales, N * G * 2)) ||
+      (mode == Q4_ASYM && overlap(o, range_of(zeros, N * G))))
+    return Q4_ERR_ALIAS;
+  return finish(q4::launch_dequantize(packed, scales, zeros, N, K, g, mode == Q4_SYM, out,
+                                      out_dtype == Q4_DTYPE_F16, num_cus(),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,

@@ -9,6 +9,11 @@ namespace q4 {
 hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
                            void* scales, void* zeros, int num_cus, hipStream_t stream);
 
+// Standalone dequantisation of the packed codes to bf16 (or fp16 when f16_out) [N, K].
+hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
+                             int64_t K, int g, bool sym, void* out, bool f16_out, int num_cus,
+                             hipStream_t stream);
+
 // Decode GEMV: M == 1 with K <= kGemvMaxK, or M == 2 with K <= kGemvMaxK2 (the lane's slice
 // of X stays in registers).
 constexpr int64_t kGemvMaxK = 16384;
