@@ -82,16 +82,19 @@ def parse_args(argv=None):
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 512 MiB device copy (counter calibration)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="per-kernel duration statistics of a rocprofv3 --kernel-trace csv run")
     return p.parse_args(argv)
 
 
 # --------------------------------------------------------------------------- context
-def measure_context(torch, sets, X5, W5, reps=10):
+def measure_context(torch, q4, sets, X5, W5, w5, reps=10):
     """Practical ceilings on this GPU, measured after the timed steps and reported beside the
     kernels (not targets): a plain streaming read of the same decode weight bytes (torch
-    reduction over the packed codes of the weight copies, rotating as the GEMV does) and the
+    reduction over the packed codes of the weight copies, rotating as the GEMV does), the
     vendor bf16 GEMM (torch.matmul, hipBLASLt) on the prefill shape with unquantized bf16
-    weights."""
+    weights, and the two-step alternative to the fused prefill GEMM: q4_dequantize of the
+    INT4 weights to bf16, then the vendor GEMM."""
     def timed(fn, n):
         for i in range(3):
             fn(i)
@@ -108,11 +111,22 @@ def measure_context(torch, sets, X5, W5, reps=10):
     read_ms = timed(lambda i: views[i % len(views)].sum(), reps * len(views))
     flops = 2.0 * X5.shape[0] * W5.shape[0] * X5.shape[1]
     mm_ms = timed(lambda i: torch.matmul(X5, W5.t()), reps)
+    Wd = torch.empty_like(W5)
+    p5, s5, z5 = w5[128]
+    deq_ms = timed(lambda i: q4.dequantize_into(p5, s5, z5, 128, "asym", Wd), reps)
+    two_ms = timed(lambda i: (q4.dequantize_into(p5, s5, z5, 128, "asym", Wd),
+                              torch.matmul(X5, Wd.t())), reps)
+    deq_bytes = p5.numel() + s5.numel() * 2 + z5.numel() + Wd.numel() * 2
     return {
         "stream_read": {"GB/s": round(read_bytes / (read_ms * 1e-3) / 1e9, 1), "bytes": read_bytes,
                         "how": "torch.sum over the int32 view of one decode weight's packed codes, rotating over the copies"},
         "vendor_bf16_gemm": {"TFLOP/s": round(flops / (mm_ms * 1e-3) / 1e12, 1), "ms": round(mm_ms, 4),
                              "how": "torch.matmul (hipBLASLt) X[2048,8192] @ W[8192,8192]^T in bf16, unquantized W"},
+        "dequantize_then_vendor_gemm": {
+            "ms": round(two_ms, 4), "TFLOP/s": round(flops / (two_ms * 1e-3) / 1e12, 1),
+            "dequantize_ms": round(deq_ms, 4),
+            "dequantize_GB/s": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
+            "how": "q4_dequantize of the g=128 INT4 weights to bf16 [8192,8192], then torch.matmul"},
     }
 
 
@@ -174,6 +188,34 @@ def summarize_counters(fetch_dir, write_dir):
     else:
         res["traffic_bytes_per_launch"] = None
     return res
+
+
+def summarize_trace(trace_dir):
+    """Per-kernel dispatch count and duration statistics (us) from rocprofv3 kernel-trace
+    csv files: mean, median, p10, p90, min, max, sorted by total time."""
+    import statistics
+    durs = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                durs.setdefault(r["Kernel_Name"], []).append(d)
+
+    def pct(v, q):
+        v = sorted(v)
+        i = q * (len(v) - 1)
+        lo = int(i)
+        hi = min(lo + 1, len(v) - 1)
+        return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+    rows = []
+    for name, v in durs.items():
+        rows.append({"kernel": name, "calls": len(v), "total_us": round(sum(v), 1),
+                     "mean_us": round(sum(v) / len(v), 2), "median_us": round(statistics.median(v), 2),
+                     "p10_us": round(pct(v, 0.1), 2), "p90_us": round(pct(v, 0.9), 2),
+                     "min_us": round(min(v), 2), "max_us": round(max(v), 2)})
+    rows.sort(key=lambda r: -r["total_us"])
+    return rows
 
 
 # --------------------------------------------------------------------------- workload
@@ -249,6 +291,10 @@ def main(argv=None):
     if args.summarize_counters:
         res = summarize_counters(*args.summarize_counters)
         print(json.dumps(res, indent=1))
+        return 0
+    if args.summarize_trace:
+        for r in summarize_trace(args.summarize_trace):
+            print(json.dumps(r))
         return 0
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path is single-GPU; sharding is "
@@ -383,7 +429,7 @@ def main(argv=None):
         "parity_max_tolerance_usage": max_usage,
     }
     if not args.no_context:
-        out["context"] = measure_context(torch, sets, X5, W5)
+        out["context"] = measure_context(torch, q4, sets, X5, W5, w5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
     print(json.dumps(out), flush=True)
