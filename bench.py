@@ -90,11 +90,17 @@ def parse_args(argv=None):
 # --------------------------------------------------------------------------- context
 def measure_context(torch, q4, sets, X5, W5, w5, reps=10):
     """Practical ceilings on this GPU, measured after the timed steps and reported beside the
-    kernels (not targets): a plain streaming read of the same decode weight bytes (torch
-    reduction over the packed codes of the weight copies, rotating as the GEMV does), the
-    vendor bf16 GEMM (torch.matmul, hipBLASLt) on the prefill shape with unquantized bf16
-    weights, and the two-step alternative to the fused prefill GEMM: q4_dequantize of the
-    INT4 weights to bf16, then the vendor GEMM."""
+    kernels (not targets):
+      * a plain streaming read of the decode weight bytes (libq4_bench.so, eight 16-byte loads
+        in flight per lane, rotating over the weight copies as the GEMV does; the best of a few
+        grid sizes), and torch's device copy of the same bytes (read + write);
+      * the vendor bf16 GEMM (torch.matmul, hipBLASLt) on the prefill shape with unquantized
+        bf16 weights;
+      * the two-step alternative to the fused prefill GEMM: q4_dequantize of the INT4 weights
+        to bf16, then the vendor GEMM."""
+    import ctypes
+    from weight_only_int4_group_amd.build import BENCH_LIB
+
     def timed(fn, n):
         for i in range(3):
             fn(i)
@@ -106,28 +112,50 @@ def measure_context(torch, q4, sets, X5, W5, w5, reps=10):
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
-    views = [s[0].view(torch.int32) for s in sets]
-    read_bytes = views[0].numel() * 4
-    read_ms = timed(lambda i: views[i % len(views)].sum(), reps * len(views))
+
+    res = {}
+    codes = [s[0] for s in sets]
+    read_bytes = codes[0].numel()
+    if os.path.exists(BENCH_LIB):
+        lib = ctypes.CDLL(BENCH_LIB)
+        lib.q4b_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+        lib.q4b_stream_read.restype = ctypes.c_int
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(cus * 64 * 4, dtype=torch.int32, device=codes[0].device)
+        stream = torch.cuda.current_stream().cuda_stream
+        best = None
+        for per_cu in (4, 8, 16, 32):
+            blocks = cus * per_cu
+            run = lambda i: lib.q4b_stream_read(codes[i % len(codes)].data_ptr(), read_bytes,
+                                                sink.data_ptr(), blocks, stream)
+            ms = timed(run, reps * len(codes))
+            if best is None or ms < best[0]:
+                best = (ms, blocks)
+        res["stream_read"] = {"GB/s": round(read_bytes / (best[0] * 1e-3) / 1e9, 1), "bytes": read_bytes,
+                              "us": round(best[0] * 1e3, 2), "blocks": best[1],
+                              "how": "libq4_bench stream_read over one decode weight's packed codes, "
+                                     "rotating over the copies; best of 4, 8, 16, 32 blocks per CU"}
+    dst = torch.empty_like(codes[0])
+    copy_ms = timed(lambda i: dst.copy_(codes[i % len(codes)]), reps * len(codes))
+    res["device_copy"] = {"GB/s": round(2 * read_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                          "how": "torch copy_ of one decode weight's packed codes (read + write bytes)"}
     flops = 2.0 * X5.shape[0] * W5.shape[0] * X5.shape[1]
     mm_ms = timed(lambda i: torch.matmul(X5, W5.t()), reps)
+    res["vendor_bf16_gemm"] = {"TFLOP/s": round(flops / (mm_ms * 1e-3) / 1e12, 1), "ms": round(mm_ms, 4),
+                               "how": "torch.matmul (hipBLASLt) X[2048,8192] @ W[8192,8192]^T in bf16, unquantized W"}
     Wd = torch.empty_like(W5)
     p5, s5, z5 = w5[128]
     deq_ms = timed(lambda i: q4.dequantize_into(p5, s5, z5, 128, "asym", Wd), reps)
     two_ms = timed(lambda i: (q4.dequantize_into(p5, s5, z5, 128, "asym", Wd),
                               torch.matmul(X5, Wd.t())), reps)
     deq_bytes = p5.numel() + s5.numel() * 2 + z5.numel() + Wd.numel() * 2
-    return {
-        "stream_read": {"GB/s": round(read_bytes / (read_ms * 1e-3) / 1e9, 1), "bytes": read_bytes,
-                        "how": "torch.sum over the int32 view of one decode weight's packed codes, rotating over the copies"},
-        "vendor_bf16_gemm": {"TFLOP/s": round(flops / (mm_ms * 1e-3) / 1e12, 1), "ms": round(mm_ms, 4),
-                             "how": "torch.matmul (hipBLASLt) X[2048,8192] @ W[8192,8192]^T in bf16, unquantized W"},
-        "dequantize_then_vendor_gemm": {
-            "ms": round(two_ms, 4), "TFLOP/s": round(flops / (two_ms * 1e-3) / 1e12, 1),
-            "dequantize_ms": round(deq_ms, 4),
-            "dequantize_GB/s": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
-            "how": "q4_dequantize of the g=128 INT4 weights to bf16 [8192,8192], then torch.matmul"},
-    }
+    res["dequantize_then_vendor_gemm"] = {
+        "ms": round(two_ms, 4), "TFLOP/s": round(flops / (two_ms * 1e-3) / 1e12, 1),
+        "dequantize_ms": round(deq_ms, 4),
+        "dequantize_GB/s": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
+        "how": "q4_dequantize of the g=128 INT4 weights to bf16 [8192,8192], then torch.matmul"}
+    return res
 
 
 # --------------------------------------------------------------------------- counters
@@ -137,6 +165,31 @@ def _counter_rows(d):
         with open(path) as f:
             rows.extend(csv.DictReader(f))
     return rows
+
+
+def measured_clocks(d):
+    """Shader clock during the prefill GEMM: GRBM_GUI_ACTIVE (GPU-busy cycles, summed over the
+    XCDs) / number of XCDs / dispatch duration, from a counter run that collected
+    GRBM_GUI_ACTIVE.  (For a kernel of a few tens of microseconds the counter window's own
+    busy time dominates, so the decode kernels get no such figure.)"""
+    xcc = 1
+    for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Name", "").startswith("gfx") and int(r.get("Num_Xcc") or 0) > 0:
+                    xcc = int(r["Num_Xcc"])
+    out = {}
+    for label, key in (("prefill", "prefill_kernel"),):
+        cyc, ns = [], []
+        for r in _counter_rows(d):
+            if r.get("Counter_Name") == "GRBM_GUI_ACTIVE" and key in r.get("Kernel_Name", ""):
+                cyc.append(float(r["Counter_Value"]))
+                ns.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        if cyc:
+            ghz = sum(c / xcc / t for c, t in zip(cyc, ns)) / len(cyc)
+            out[f"{label}_clock_GHz"] = round(ghz, 3)
+            out[f"{label}_clock_dispatches"] = len(cyc)
+    return out
 
 
 def summarize_counters(fetch_dir, write_dir):
@@ -179,6 +232,7 @@ def summarize_counters(fetch_dir, write_dir):
         "copy_fetch_kib": cf,
         "copy_write_kib": cw,
     }
+    res.update(measured_clocks(fetch_dir))
     if gf and gw and cf and cw:
         ff = copy_bytes / (cf * 1024)
         fw = copy_bytes / (cw * 1024)
@@ -219,11 +273,23 @@ def summarize_trace(trace_dir):
 
 
 # --------------------------------------------------------------------------- workload
-def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, block=4096):
-    """The CPU oracle's W4A16 matmul (M=1), over row blocks of the 70B-shaped layer.
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The oracle quantizes each block first (not timed); matmul_ref is then timed over the
-    blocks, cycling through the layer until about budget_s seconds of CPU work are spent.
+
+def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, q_budget_s=6.0, block=4096):
+    """The CPU oracle, timed on this host over bounded samples of the 70B-shaped layer.
+
+    matmul_ref (M=1, fp64 dequantisation + BLAS, all BLAS threads): the oracle quantizes each
+    row block first (not timed), then matmul_ref is timed over the blocks, cycling through the
+    layer until about budget_s seconds are spent.  quantize_ref (elementwise numpy, one
+    thread) is timed on consecutive row blocks until about q_budget_s seconds are spent.
     """
     import numpy as np
     from oracle import q4_oracle as orc
@@ -243,10 +309,24 @@ def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, block=4096):
             done_rows += p.shape[0]
         passes += 1
     nbytes = matmul_bytes(X_bits.shape[0], done_rows, K, g, mode)
+    q_rows, q_spent, qb = 0, 0.0, 512
+    while q_spent < q_budget_s and q_rows < N:
+        t = time.perf_counter()
+        orc.quantize_rtn_ref(W_bits[q_rows:q_rows + qb], g, mode)
+        q_spent += time.perf_counter() - t
+        q_rows += min(qb, N - q_rows)
+    G = K // g
+    q_bytes = q_rows * (2 * K + K // 2 + G * (3 if mode == "asym" else 2))
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"oracle matmul_ref (fp64 dequantisation + BLAS), M=1, the whole {N}x{K} "
-                      f"layer in row blocks of {block}, {passes} passes, {spent:.1f} s"}
+                      f"layer in row blocks of {block}, {passes} passes, {spent:.1f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "gflops": round(2.0 * done_rows * K / spent / 1e9, 3),
+            "quantize_ref": {"GB/s": round(q_bytes / q_spent / 1e9, 4), "cores": 1,
+                             "sample": f"oracle quantize_rtn_ref (elementwise numpy fp32), first {q_rows} rows "
+                                       f"of the {N}x{K} weight in blocks of {qb}, {q_spent:.1f} s; bytes = "
+                                       f"bf16 W read + codes, scales, zeros written"}}
 
 
 def check_parity(q4, torch, W4_bits, X4_bits, sets, Y4, W5_bits, X5_host, X5_dev, w5, Y5):

@@ -15,6 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4.so")
+# Measurement helper for bench.py (a plain streaming read), kept out of the product library.
+BENCH_LIB = os.path.join(PKG, "libq4_bench.so")
+BENCH_SOURCES = [os.path.join("bench", "stream_read.hip")]
 
 ARCH = "gfx950"
 COMMON = [
@@ -54,7 +57,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link libq4.so; returns the library path."""
+    """Compile every source, link libq4.so and the measurement helper libq4_bench.so; returns
+    the path of libq4.so."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
 
@@ -69,6 +73,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    bench_objs = []
+    for src in BENCH_SOURCES:
+        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        _run([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        bench_objs.append(obj)
+    tmp = BENCH_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *bench_objs], verbose)
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 
