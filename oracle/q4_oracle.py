@@ -41,6 +41,18 @@ R7  x_hat = fp64(scale_fp16) * (q - z)  (exact in fp64).
 R8  the standalone dequantisation returns x_hat rounded once to bf16 or fp16, round half
     to even (R3); an fp16 result beyond the fp16 range becomes +-inf as IEEE rounding
     says.  x_hat has at most 15 significant bits and lies in bf16's normal range (or is 0).
+R9  AWQ-style scaling ("LLM Weight Quantization ...", "GPTQ vs AWQ" toy; "DL S067" §5 "AWQ
+    intuition"): a_j = mean over calibration rows of |X[m, j]|; s = a^alpha, divided by
+    sqrt(max s * min s); the weights W * s are quantized and 1/s is folded back onto the
+    activations; alpha is searched on a grid of [0, 1] by the layer's output error on the
+    calibration rows, the first smallest error winning.  In the library's formats:
+    a_j is floored at 2^-20 max_j a_j (a channel the calibration never activates gets the
+    weakest scale rather than 0; an all-zero X gives s = 1), s is rounded to fp32, the
+    quantized weights are bf16(fl32(W[n, j] * s_j)), the activations bf16(fl32(X[m, j] / s_j))
+    (IEEE fp32 product / quotient, then round half to even), the grid is i / (n_alpha - 1),
+    and the error of alpha is sum (Y_alpha - Y_ref)^2 with Y_alpha the exact product of the
+    scaled activations and the dequantised scaled weights and Y_ref the layer's unquantized
+    output on the calibration rows (an input, as the calibration activations are).
 """
 from __future__ import annotations
 
@@ -48,7 +60,9 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_groups", "quantize_rtn_ref", "unpack_codes_ref",
-    "dequantize_ref", "round_to_bf16_bits_ref", "dequantize_rounded_ref", "matmul_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
+    "dequantize_ref", "round_to_bf16_bits_ref", "dequantize_rounded_ref", "matmul_ref",
+    "f32_to_bf16_bits_ref", "awq_search", "channel_absmean_ref", "awq_scales_ref",
+    "scale_columns_ref", "quantize_rtn_scaled_ref", "awq_search_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
     "bits_per_weight", "weight_bytes", "format_math_row",
 ]
 
@@ -252,6 +266,112 @@ def check_matmul(Y_gpu_f64, Y_ref, A):
     usage = err / tol_ref(A)
     worst = float(usage.max()) if usage.size else 0.0
     return bool(np.all(usage <= 1.0)), worst
+
+
+# --------------------------------------------------------------------------- AWQ-style scaling
+def awq_search(W, X, qdq, alphas=np.linspace(0, 1, 11)):
+    """Activation-aware scaling search of the pages' toy (R9), in fp64, for any quantizer.
+
+    W [rows, d], X [m, d] calibration activations, qdq(Ws) -> quantized-dequantized Ws.
+    For each alpha: s = a^alpha with a_j = mean |X[:, j]|, normalised by sqrt(max s min s);
+    Q = qdq(W * s) / s (the 1/s folded back); error = ||X W^T - X Q^T||.  Returns
+    (Q of the best alpha, best alpha, errors per alpha); the first smallest error wins.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    a_mag = np.abs(X).mean(axis=0)
+    Y = X @ W.T
+    best, errs = None, []
+    for a in alphas:
+        s = a_mag ** a
+        s = s / np.sqrt(s.max() * s.min())
+        Q = qdq(W * s) / s
+        err = np.linalg.norm(Y - X @ Q.T)
+        errs.append(err)
+        if best is None or err < best[0]:
+            best = (err, float(a), Q)
+    return best[2], best[1], np.array(errs)
+
+
+def f32_to_bf16_bits_ref(x32) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round half to even on the bit pattern (R3): add half of the
+    dropped range, plus one when the kept part is odd, and keep the top 16 bits.  Exact for
+    every finite fp32 value, subnormals included; a result beyond bf16's range is +-inf."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    if not np.all(np.isfinite(np.asarray(x32, dtype=np.float32))):
+        raise ValueError("NaN or Inf input is outside the method's domain")
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def channel_absmean_ref(X_bits) -> np.ndarray:
+    """a_j = mean over rows m of |X[m, j]| (R9), fp64."""
+    X = bf16_bits_to_f32(X_bits).astype(np.float64)
+    return np.abs(X).mean(axis=0)
+
+
+AWQ_FLOOR = 2.0 ** -20
+
+
+def awq_scales_ref(a, alpha: float) -> np.ndarray:
+    """s = a^alpha / sqrt(max(a^alpha) min(a^alpha)) with a floored at 2^-20 max(a) (R9), in
+    fp64, rounded to fp32."""
+    a = np.asarray(a, dtype=np.float64)
+    amax = a.max()
+    if amax == 0.0:
+        return np.ones(a.shape, np.float32)
+    a = np.maximum(a, AWQ_FLOOR * amax)
+    s = a ** alpha
+    s = s / np.sqrt(s.max() * s.min())
+    return s.astype(np.float32)
+
+
+def scale_columns_ref(A_bits, s32, op: str) -> np.ndarray:
+    """bf16(fl32(A[r, j] * s_j)) for op="mul", bf16(fl32(A[r, j] / s_j)) for op="div" (R9):
+    one IEEE fp32 product or quotient (numpy float32), then round half to even to bf16."""
+    A = bf16_bits_to_f32(A_bits)
+    s = np.asarray(s32, dtype=np.float32)
+    if op == "mul":
+        v = A * s[None, :]
+    elif op == "div":
+        v = A / s[None, :]
+    else:
+        raise ValueError(f"unknown op {op!r}")
+    return f32_to_bf16_bits_ref(v)
+
+
+def quantize_rtn_scaled_ref(W_bits, s32, g: int = 128, mode: str = "asym"):
+    """RTN quantization of bf16(fl32(W * s)) (R9): the weights of AWQ-style scaling."""
+    return quantize_rtn_ref(scale_columns_ref(W_bits, s32, "mul"), g, mode)
+
+
+def awq_search_ref(W_bits, X_bits, Yref_bits, g: int = 128, mode: str = "asym", n_alpha: int = 11):
+    """AWQ-style scaling in the library's formats (R9).
+
+    W_bits [N, K] weights, X_bits [M, K] calibration activations, Yref_bits [M, N] the layer's
+    unquantized output on them (bf16 bit patterns).  For alpha_i = i / (n_alpha - 1): scales
+    s_i (awq_scales_ref), quantize bf16(W * s_i), scale the activations bf16(X / s_i), and
+    error_i = sum (Y_i - Y_ref)^2 with Y_i their exact product.  Returns a dict with the best
+    index (first smallest error), alphas, errors, the scales of every alpha (fp32) and the
+    best alpha's packed / scales / zeros.
+    """
+    if n_alpha < 1:
+        raise ValueError("n_alpha >= 1")
+    a = channel_absmean_ref(X_bits)
+    Yref = bf16_bits_to_f32(Yref_bits).astype(np.float64)
+    alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]
+    errs, svals, quants = [], [], []
+    for al in alphas:
+        s = awq_scales_ref(a, al)
+        q = quantize_rtn_scaled_ref(W_bits, s, g, mode)
+        Xs = scale_columns_ref(X_bits, s, "div")
+        Y, _ = matmul_ref(Xs, *q, g, mode)
+        errs.append(float(((Y - Yref) ** 2).sum()))
+        svals.append(s)
+        quants.append(q)
+    best = int(np.argmin(errs))             # first smallest
+    return {"best": best, "alphas": alphas, "errors": np.array(errs), "scales": np.array(svals),
+            "quant": quants[best], "absmean": a}
 
 
 # --------------------------------------------------------------------------- format math

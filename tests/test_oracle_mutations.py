@@ -32,6 +32,12 @@ MUTATIONS = {
     "bf16 ties away from zero": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m))"),
     "bf16 7 significant bits": ("np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)", "np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)"),
     "bf16 truncation": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
+    "AWQ magnitude is the max": ("a_mag = np.abs(X).mean(axis=0)", "a_mag = np.abs(X).max(axis=0)"),
+    "AWQ 1/s not folded back": ("        Q = qdq(W * s) / s\n", "        Q = qdq(W * s)\n"),
+    "AWQ scored on weight error": ("err = np.linalg.norm(Y - X @ Q.T)", "err = np.linalg.norm(W - Q)"),
+    "AWQ scales not normalised": ("    s = s / np.sqrt(s.max() * s.min())\n    return s.astype(np.float32)", "    return s.astype(np.float32)"),
+    "AWQ grid misses alpha 1": ("alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]", "alphas = [i / n_alpha for i in range(n_alpha)]"),
+    "bf16 bit rounding truncates": ("(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)", "u >> np.uint64(16)"),
 }
 
 
@@ -80,6 +86,9 @@ def _pins_pass(orc, golden_dir):
                 return False
         from tests.test_oracle_pins import rounding_pins_hold
         if not rounding_pins_hold(orc):
+            return False
+        from tests.test_oracle_awq import awq_pins_hold
+        if not awq_pins_hold(orc):
             return False
     except Exception:
         return False
