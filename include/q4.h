@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4_VERSION 10100  /* 1.1.0 */
+#define Q4_VERSION 10200  /* 1.2.0 */
 
 typedef enum {
     Q4_ASYM = 0,   /* uint4 codes [0, 15] with a uint8 zero-point per group */
@@ -74,6 +74,11 @@ typedef enum {
     Q4_DTYPE_F16 = 1       /* IEEE binary16 output */
 } q4_dtype_t;
 
+typedef enum {
+    Q4_SCALE_MUL = 0,      /* out = A * s per column */
+    Q4_SCALE_DIV = 1       /* out = A / s per column */
+} q4_scale_op_t;
+
 enum {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,      /* a required pointer is NULL                                    */
@@ -84,7 +89,8 @@ enum {
                               or Y not 2-byte                                                 */
     Q4_ERR_HIP = -6,       /* the HIP runtime rejected a launch                              */
     Q4_ERR_ALIAS = -7,     /* an output buffer overlaps an input or another output          */
-    Q4_ERR_UNSUPPORTED = -8 /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
+    Q4_ERR_UNSUPPORTED = -8, /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
+    Q4_ERR_WORKSPACE = -9  /* workspace smaller than q4_awq_workspace_bytes() requires        */
 };
 
 /*
@@ -139,6 +145,72 @@ int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t
  */
 int q4_dequantize(int64_t N, int64_t K, int32_t g, int32_t mode, const void* packed,
                   const void* scales, const void* zeros, void* out, int32_t out_dtype,
+                  void* stream);
+
+/*
+ * AWQ-style activation-aware scaling before RTN.
+ * Source: "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
+ * "GPTQ vs AWQ: two ways to choose what error to keep" (the toy's activation-aware search) and
+ * "DL S067 · Quantization", §5 "AWQ intuition": scale the weight columns of input channels with
+ * large activations up by s before quantizing, divide the activations by s, and search the
+ * exponent of s on calibration data by the layer's output error.  The kernels at serve time
+ * are the plain ones: the quantized weights are those of W * s, and the caller folds 1/s into
+ * the activations (or the previous layer).  Rules this library fixes:
+ *   - a_j = mean over calibration rows of |X[m, j]| (fp32, fixed summation order), floored at
+ *     2^-20 max_j a_j (an all-zero X gives s = 1);
+ *   - alpha_i = i / (n_alpha - 1) (alpha = 0 when n_alpha == 1);
+ *     s_j = a_j^alpha / sqrt(max_j a_j^alpha * min_j a_j^alpha), in fp32 (2^(alpha (log2 a_j -
+ *     mean of log2 max a and log2 min a)), so within a few fp32 ulps of the exact value); s = 1
+ *     exactly for alpha = 0;
+ *   - scaled weights bf16(fl32(W[n, j] * s_j)) and scaled activations bf16(fl32(X[m, j] / s_j)):
+ *     one IEEE fp32 product or quotient, then round to nearest even;
+ *   - error_i = sum over the calibration outputs of (Y_i - Y_ref)^2 in fp64, Y_i the library's
+ *     W4A16 product of the scaled activations and the quantized scaled weights, Y_ref the layer's
+ *     unquantized output; the first smallest error wins.
+ */
+
+/* RTN quantization of W * s: as q4_quantize_rtn applied to bf16(fl32(W[n, k] * s[k])).
+ *   s       device, fp32 [K], 16-byte aligned (input; must not overlap the outputs)
+ *   other arguments and errors as for q4_quantize_rtn.  Outputs are bit-exact. */
+int q4_quantize_rtn_scaled(const void* W, const void* s, int64_t N, int64_t K, int32_t g, int32_t mode,
+                           void* packed, void* scales, void* zeros, void* stream);
+
+/* out[r, c] = bf16(fl32(A[r, c] * s[c])) (Q4_SCALE_MUL) or bf16(fl32(A[r, c] / s[c]))
+ * (Q4_SCALE_DIV): the activation side of AWQ-style scaling (X / s) or the weight side (W * s).
+ *   A       device, bf16 [rows, cols], 16-byte aligned
+ *   rows    0 <= rows <= 2^31 - 1 (rows == 0 returns Q4_OK and launches nothing)
+ *   cols    8 <= cols <= 2^31 - 1, cols % 8 == 0 (else Q4_ERR_SHAPE)
+ *   s       device, fp32 [cols], 16-byte aligned
+ *   op      q4_scale_op_t (else Q4_ERR_MODE)
+ *   out     device, bf16 [rows, cols], 16-byte aligned; may be A itself (in place), must not
+ *           overlap A otherwise, nor s
+ * Outputs are bit-exact (IEEE product / quotient, round to nearest even). */
+int q4_scale_columns(const void* A, int64_t rows, int64_t cols, const void* s, int32_t op, void* out,
+                     void* stream);
+
+/* Bytes of device workspace q4_awq_search needs for these sizes, or a negative status
+ * (Q4_ERR_SHAPE when M < 1 or n_alpha outside [1, 64], the q4_quantize_rtn errors otherwise).
+ * Pure host function, no HIP call. */
+int64_t q4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t g, int32_t n_alpha);
+
+/* The activation-aware search and the final quantization, enqueued on `stream` without any
+ * host synchronization (the best index is chosen on the device).
+ *   X        device, bf16 [M, K] calibration activations, 16-byte aligned; 1 <= M <= 2^31 - 1
+ *   Yref     device, bf16 [M, N], the layer's unquantized output on X (e.g. X W^T), 2-byte aligned
+ *   W        device, bf16 [N, K] weights, 16-byte aligned
+ *   N, K, g, mode   as for q4_quantize_rtn
+ *   n_alpha  grid points in [1, 64] (11 gives the pages' grid 0, 0.1, ..., 1)
+ *   workspace, workspace_bytes  device scratch of at least q4_awq_workspace_bytes(M, N, K, g,
+ *            n_alpha) bytes, 256-byte aligned, owned by the caller; contents are overwritten
+ *   s_out    device, fp32 [K], 16-byte aligned (output): the chosen alpha's scales
+ *   packed, scales, zeros  outputs as for q4_quantize_rtn: the quantization of W * s_out
+ *   errors   device, fp64 [n_alpha], 8-byte aligned (output): error_i per grid point
+ *   best     device, int32 [1], 4-byte aligned (output): the chosen index i (alpha = i/(n_alpha-1))
+ * No output may overlap an input, the workspace or another output (Q4_ERR_ALIAS).  Errors as
+ * for q4_quantize_rtn and q4_matmul, plus Q4_ERR_WORKSPACE.  The outputs are deterministic. */
+int q4_awq_search(const void* X, int64_t M, const void* Yref, const void* W, int64_t N, int64_t K,
+                  int32_t g, int32_t mode, int32_t n_alpha, void* workspace, int64_t workspace_bytes,
+                  void* s_out, void* packed, void* scales, void* zeros, void* errors, void* best,
                   void* stream);
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires

@@ -13,8 +13,9 @@ import threading
 
 __all__ = [
     "Q4Error", "library", "library_path", "quantize_rtn", "quantize_rtn_into", "matmul",
-    "matmul_into", "dequantize", "dequantize_into", "select_kernel", "status_string", "version",
-    "MODES", "KERNELS",
+    "matmul_into", "dequantize", "dequantize_into", "quantize_rtn_scaled", "quantize_rtn_scaled_into",
+    "scale_columns", "scale_columns_into", "awq_workspace_bytes", "awq_search", "awq_search_into",
+    "select_kernel", "status_string", "version", "MODES", "KERNELS", "SCALE_OPS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -22,6 +23,7 @@ library_path = os.path.join(_HERE, "libq4.so")
 
 MODES = {"asym": 0, "sym": 1}
 KERNELS = {"auto": 0, "gemv": 1, "gemm": 2, "decode": 3}
+SCALE_OPS = {"mul": 0, "div": 1}
 _KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
 _lock = threading.Lock()
@@ -52,6 +54,15 @@ def library() -> ctypes.CDLL:
             lib.q4_matmul_kernel.restype = ctypes.c_int
             lib.q4_dequantize.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, i32, vp]
             lib.q4_dequantize.restype = ctypes.c_int
+            lib.q4_quantize_rtn_scaled.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp]
+            lib.q4_quantize_rtn_scaled.restype = ctypes.c_int
+            lib.q4_scale_columns.argtypes = [vp, i64, i64, vp, i32, vp, vp]
+            lib.q4_scale_columns.restype = ctypes.c_int
+            lib.q4_awq_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+            lib.q4_awq_workspace_bytes.restype = ctypes.c_int64
+            lib.q4_awq_search.argtypes = [vp, i64, vp, vp, i64, i64, i32, i32, i32, vp, i64, vp, vp, vp,
+                                          vp, vp, vp, vp]
+            lib.q4_awq_search.restype = ctypes.c_int
             lib.q4_select_kernel.argtypes = [i64, i64, i64, i32]
             lib.q4_select_kernel.restype = ctypes.c_int
             lib.q4_status_string.argtypes = [ctypes.c_int]
@@ -185,3 +196,108 @@ def dequantize(packed, scales, zeros, g: int = 128, mode: str = "asym", dtype=No
                       dtype=torch.bfloat16 if dtype is None else dtype, device=packed.device)
     dequantize_into(packed, scales, zeros, g, mode, out)
     return out
+
+
+def quantize_rtn_scaled_into(W, s, g: int, mode: str, packed, scales, zeros) -> None:
+    """q4_quantize_rtn_scaled (RTN of bf16(W * s)) on caller-provided outputs."""
+    import torch
+    _check_cuda(W, s, packed, scales, zeros)
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or s.dtype != torch.float32 or s.dim() != 1:
+        raise ValueError("W must be a 2-D bfloat16 tensor and s a 1-D float32 tensor")
+    N, K = W.shape
+    if s.shape[0] != K:
+        raise ValueError(f"s has {s.shape[0]} entries, W has {K} columns")
+    with torch.cuda.device(W.device):
+        st = library().q4_quantize_rtn_scaled(_ptr(W), _ptr(s), N, K, g, _mode(mode), _ptr(packed),
+                                              _ptr(scales), _ptr(zeros), _stream(W.device))
+    if st != 0:
+        raise Q4Error(st, "q4_quantize_rtn_scaled")
+
+
+def quantize_rtn_scaled(W, s, g: int = 128, mode: str = "asym"):
+    """RTN quantization of bf16(W * s) -> (packed, scales, zeros)."""
+    import torch
+    N, K = W.shape
+    G = K // g if g > 0 else 0
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    quantize_rtn_scaled_into(W, s, g, mode, packed, scales, zeros)
+    return packed, scales, zeros
+
+
+def scale_columns_into(A, s, op: str, out) -> None:
+    """q4_scale_columns: out = bf16(A * s) or bf16(A / s) per column (out may be A)."""
+    import torch
+    _check_cuda(A, s, out)
+    if A.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or A.dim() != 2 or s.dtype != torch.float32:
+        raise ValueError("A and out must be 2-D bfloat16 tensors and s float32")
+    if op not in SCALE_OPS:
+        raise ValueError(f"op must be one of {sorted(SCALE_OPS)}")
+    rows, cols = A.shape
+    if tuple(out.shape) != (rows, cols) or s.shape != (cols,):
+        raise ValueError("shape mismatch between A, s and out")
+    with torch.cuda.device(A.device):
+        st = library().q4_scale_columns(_ptr(A), rows, cols, _ptr(s), SCALE_OPS[op], _ptr(out),
+                                        _stream(A.device))
+    if st != 0:
+        raise Q4Error(st, "q4_scale_columns")
+
+
+def scale_columns(A, s, op: str = "div"):
+    import torch
+    out = torch.empty_like(A)
+    scale_columns_into(A, s, op, out)
+    return out
+
+
+def awq_workspace_bytes(M: int, N: int, K: int, g: int, n_alpha: int = 11) -> int:
+    v = int(library().q4_awq_workspace_bytes(M, N, K, g, n_alpha))
+    if v < 0:
+        raise Q4Error(v, "q4_awq_workspace_bytes")
+    return v
+
+
+def awq_search_into(X, Yref, W, g: int, mode: str, n_alpha: int, workspace, s_out, packed, scales,
+                    zeros, errors, best) -> None:
+    """q4_awq_search on caller-provided workspace and outputs (no allocation)."""
+    import torch
+    _check_cuda(X, Yref, W, workspace, s_out, packed, scales, zeros, errors, best)
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or Yref.dtype != torch.bfloat16:
+        raise ValueError("X, Yref and W must be bfloat16")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(Yref.shape) != (M, N):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, Yref {tuple(Yref.shape)}")
+    if errors.dtype != torch.float64 or best.dtype != torch.int32 or s_out.dtype != torch.float32:
+        raise ValueError("errors must be float64, best int32 and s_out float32")
+    with torch.cuda.device(W.device):
+        st = library().q4_awq_search(_ptr(X), M, _ptr(Yref), _ptr(W), N, K, g, _mode(mode), n_alpha,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _ptr(s_out), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(errors),
+                                     _ptr(best), _stream(W.device))
+    if st != 0:
+        raise Q4Error(st, "q4_awq_search")
+
+
+def awq_search(X, Yref, W, g: int = 128, mode: str = "asym", n_alpha: int = 11):
+    """AWQ-style search on calibration activations X and the layer's unquantized output Yref.
+
+    Returns (s, packed, scales, zeros, errors, best): s the chosen fp32 scales (the weights
+    quantized are W * s; divide the activations by s at serve time), errors per grid point
+    alpha_i = i / (n_alpha - 1), best the chosen index (device tensors).
+    """
+    import torch
+    M, K = X.shape
+    N = W.shape[0]
+    G = K // g if g > 0 else 0
+    dev = W.device
+    ws = torch.empty(awq_workspace_bytes(M, N, K, g, n_alpha), dtype=torch.uint8, device=dev)
+    s_out = torch.empty(K, dtype=torch.float32, device=dev)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, G), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    errors = torch.empty(n_alpha, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    awq_search_into(X, Yref, W, g, mode, n_alpha, ws, s_out, packed, scales, zeros, errors, best)
+    return s_out, packed, scales, zeros, errors, best

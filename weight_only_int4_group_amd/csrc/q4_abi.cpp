@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <initializer_list>
 
 #include "q4_internal.h"
 
@@ -83,6 +84,16 @@ int validate_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, i
 
 int finish(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
 
+// True if any two of the ranges overlap.
+bool any_overlap(std::initializer_list<Range> rs) {
+  for (auto a = rs.begin(); a != rs.end(); ++a)
+    for (auto b = a + 1; b != rs.end(); ++b)
+      if (overlap(*a, *b)) return true;
+  return false;
+}
+
+constexpr int kMaxAlphas = 64;
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +112,7 @@ const char* q4_status_string(int status) {
     case Q4_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case Q4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case Q4_ERR_UNSUPPORTED: return "the chosen kernel does not support this shape";
+    case Q4_ERR_WORKSPACE: return "workspace smaller than q4_awq_workspace_bytes() requires";
     default: return "unknown status";
   }
 }
@@ -148,6 +160,94 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
   if (q4::prefill_fits(M, N, K, g))
     return finish(q4::launch_prefill(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+}
+
+int q4_quantize_rtn_scaled(const void* W, const void* s, int64_t N, int64_t K, int32_t g, int32_t mode,
+                           void* packed, void* scales, void* zeros, void* stream) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (!W || !s || !packed || !scales || !zeros) return Q4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(s, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return Q4_ERR_ALIGN;
+  const int64_t G = K / g;
+  const Range w = range_of(W, N * K * 2), sc = range_of(s, K * 4), p = range_of(packed, N * K / 2),
+              sg = range_of(scales, N * G * 2), z = range_of(zeros, N * G);
+  if (any_overlap({p, sg, z}) || any_overlap({w, p}) || any_overlap({w, sg}) || any_overlap({w, z}) ||
+      any_overlap({sc, p}) || any_overlap({sc, sg}) || any_overlap({sc, z}))
+    return Q4_ERR_ALIAS;
+  return finish(q4::launch_quantize(W, N, K, g, mode == Q4_SYM, packed, scales, zeros, num_cus(),
+                                    static_cast<hipStream_t>(stream), static_cast<const float*>(s)));
+}
+
+int q4_scale_columns(const void* A, int64_t rows, int64_t cols, const void* s, int32_t op, void* out,
+                     void* stream) {
+  if (rows < 0 || rows > kMaxDim || cols < 8 || cols > kMaxDim) return Q4_ERR_SHAPE;
+  if (cols % 8 != 0) return Q4_ERR_SHAPE;
+  if (op != Q4_SCALE_MUL && op != Q4_SCALE_DIV) return Q4_ERR_MODE;
+  if (rows == 0) return Q4_OK;
+  if (!A || !s || !out) return Q4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(s, 16) || !aligned(out, 16)) return Q4_ERR_ALIGN;
+  const Range a = range_of(A, rows * cols * 2), o = range_of(out, rows * cols * 2), sc = range_of(s, cols * 4);
+  if ((A != out && overlap(a, o)) || overlap(sc, o)) return Q4_ERR_ALIAS;
+  return finish(q4::launch_scale_columns(A, rows, cols, s, op == Q4_SCALE_DIV, out, num_cus(),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int64_t q4_awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t g, int32_t n_alpha) {
+  int st = check_shape(N, K, g, Q4_ASYM);
+  if (st != Q4_OK) return st;
+  if (M < 1 || M > kMaxDim || n_alpha < 1 || n_alpha > kMaxAlphas) return Q4_ERR_SHAPE;
+  return (int64_t)q4::awq_layout(M, N, K, g, n_alpha).bytes;
+}
+
+int q4_awq_search(const void* X, int64_t M, const void* Yref, const void* W, int64_t N, int64_t K,
+                  int32_t g, int32_t mode, int32_t n_alpha, void* workspace, int64_t workspace_bytes,
+                  void* s_out, void* packed, void* scales, void* zeros, void* errors, void* best,
+                  void* stream) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (M < 1 || M > kMaxDim || n_alpha < 1 || n_alpha > kMaxAlphas) return Q4_ERR_SHAPE;
+  if (!X || !Yref || !W || !workspace || !s_out || !packed || !scales || !zeros || !errors || !best)
+    return Q4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Yref, 2) || !aligned(workspace, 256) ||
+      !aligned(s_out, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(errors, 8) ||
+      !aligned(best, 4))
+    return Q4_ERR_ALIGN;
+  const q4::AwqLayout L = q4::awq_layout(M, N, K, g, n_alpha);
+  if (workspace_bytes < (int64_t)L.bytes) return Q4_ERR_WORKSPACE;
+  const int64_t G = K / g;
+  const Range x = range_of(X, M * K * 2), yr = range_of(Yref, M * N * 2), w = range_of(W, N * K * 2),
+              ws = range_of(workspace, (int64_t)L.bytes), so = range_of(s_out, K * 4),
+              p = range_of(packed, N * K / 2), sg = range_of(scales, N * G * 2), z = range_of(zeros, N * G),
+              e = range_of(errors, (int64_t)n_alpha * 8), b = range_of(best, 4);
+  for (const Range& out : {ws, so, p, sg, z, e, b})
+    if (overlap(out, x) || overlap(out, yr) || overlap(out, w)) return Q4_ERR_ALIAS;
+  if (any_overlap({ws, so, p, sg, z, e, b})) return Q4_ERR_ALIAS;
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool sym = mode == Q4_SYM;
+  char* base = static_cast<char*>(workspace);
+  float* s_all = reinterpret_cast<float*>(base + L.scales_all);
+  hipError_t he = q4::launch_absmean(X, M, K, base + L.partial, base + L.absmean, hs);
+  if (he == hipSuccess) he = q4::launch_awq_scales(base + L.absmean, K, n_alpha, s_all, hs);
+  for (int i = 0; i < n_alpha && he == hipSuccess; ++i) {
+    const float* si = s_all + (size_t)i * K;
+    he = q4::launch_quantize(W, N, K, g, sym, base + L.packed, base + L.qscales, base + L.qzeros, num_cus(),
+                             hs, si);
+    if (he == hipSuccess) he = q4::launch_scale_columns(X, M, K, si, true, base + L.xs, num_cus(), hs);
+    if (he == hipSuccess) {
+      const int mst = q4_matmul(base + L.xs, M, N, K, g, mode, base + L.packed, base + L.qscales,
+                                base + L.qzeros, base + L.y, stream);
+      if (mst != Q4_OK) return mst;
+    }
+    if (he == hipSuccess)
+      he = q4::launch_sq_err(base + L.y, Yref, M * N, base + L.err_partial,
+                             static_cast<double*>(errors) + i, hs);
+  }
+  if (he == hipSuccess) he = q4::launch_awq_select(errors, n_alpha, s_all, K, best, s_out, hs);
+  if (he == hipSuccess)
+    he = q4::launch_quantize(W, N, K, g, sym, packed, scales, zeros, num_cus(), hs,
+                             static_cast<const float*>(s_out));
+  return finish(he);
 }
 
 int q4_dequantize(int64_t N, int64_t K, int32_t g, int32_t mode, const void* packed,

@@ -6,13 +6,35 @@
 
 namespace q4 {
 
+// colscale (optional, fp32 [K], 16-byte aligned): quantize bf16(fl32(W[n, k] * colscale[k])).
 hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
-                           void* scales, void* zeros, int num_cus, hipStream_t stream);
+                           void* scales, void* zeros, int num_cus, hipStream_t stream,
+                           const float* colscale = nullptr);
 
 // Standalone dequantisation of the packed codes to bf16 (or fp16 when f16_out) [N, K].
 hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
                              int64_t K, int g, bool sym, void* out, bool f16_out, int num_cus,
                              hipStream_t stream);
+
+// AWQ-style scaling (awq.hip).  Workspace layout of q4_awq_search: byte offsets of each
+// buffer (256-byte aligned) and the total.
+struct AwqLayout {
+  uint64_t partial, absmean, scales_all, packed, qscales, qzeros, xs, y, err_partial, bytes;
+};
+AwqLayout awq_layout(int64_t M, int64_t N, int64_t K, int g, int n_alpha);
+// a[k] = mean_m |X[m, k]| (fp32), via partial sums in `partial` (64 K floats).
+hipError_t launch_absmean(const void* X, int64_t M, int64_t K, void* partial, void* a, hipStream_t stream);
+// s_all[i][k] for alpha_i = i / (n_alpha - 1).
+hipError_t launch_awq_scales(const void* a, int64_t K, int n_alpha, void* s_all, hipStream_t stream);
+// out = bf16(fl32(A * s)) or bf16(fl32(A / s)) per column; cols % 8 == 0.
+hipError_t launch_scale_columns(const void* A, int64_t rows, int64_t cols, const void* s, bool divide,
+                                void* out, int num_cus, hipStream_t stream);
+// *err (fp64) = sum over n bf16 elements of (Yq - Yref)^2.
+hipError_t launch_sq_err(const void* Yq, const void* Yref, int64_t n, void* partial, void* err,
+                         hipStream_t stream);
+// *best = first index of the smallest err; s_out = s_all[best].
+hipError_t launch_awq_select(const void* err, int n_alpha, const void* s_all, int64_t K, void* best,
+                             void* s_out, hipStream_t stream);
 
 // Decode GEMV: M == 1 with K <= kGemvMaxK, or M == 2 with K <= kGemvMaxK2 (the lane's slice
 // of X stays in registers).

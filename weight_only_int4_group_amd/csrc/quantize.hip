@@ -93,6 +93,25 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
   }
 }
 
+// Optional per-column scale applied before quantization (AWQ-style scaling): the weight
+// quantized is bf16(fl32(w * s_j)), one IEEE fp32 product rounded to nearest even to bf16.
+// c8 = K / 8 chunks per row; `small` says every flat chunk index fits 32 bits (then the
+// column of a chunk is a 32-bit remainder).
+struct ColScale {
+  const float* s;
+  int64_t c8;
+  bool small;
+};
+
+__device__ __forceinline__ void apply_colscale(const ColScale& cs, int64_t chunk, float x[8]) {
+  const uint32_t cc = cs.small ? (uint32_t)chunk % (uint32_t)cs.c8 : (uint32_t)(chunk % cs.c8);
+  const float4* sp = reinterpret_cast<const float4*>(cs.s + 8 * (size_t)cc);
+  const float4 a = sp[0], b = sp[1];
+  const float sv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)(__bf16)(x[i] * sv[i]);
+}
+
 template <bool SYM>
 __device__ __forceinline__ uint32_t pack8(const float x[8], const GroupParams& p) {
   uint32_t w = 0;
@@ -116,10 +135,10 @@ __device__ __forceinline__ float lanes_max(float v) {
 
 // g in {32, 64, 128, 256, 512}: a group is L = g/8 consecutive lanes, each holding one chunk.
 // A wave covers 64 consecutive chunks (512 weights) per step; U steps are loaded together.
-template <int L, bool SYM, int U>
+template <int L, bool SYM, int U, bool SC>
 __global__ __launch_bounds__(256) void quantize_lanes_kernel(
     const u32x4* __restrict__ W, int64_t nchunks, uint32_t* __restrict__ packed,
-    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, ColScale cs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) / kWave;
@@ -135,6 +154,7 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(
       const int64_t c = (base + u) * kWave + lane;
       float x[8];
       unpack8(v[u], x);
+      if (SC) apply_colscale(cs, c < nchunks ? c : 0, x);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -163,10 +183,10 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(
 
 // Any g (multiple of 32): one wave per group, two passes over the group's chunks
 // (range, then codes); the second pass re-reads the group, normally from cache.
-template <bool SYM>
+template <bool SYM, bool SC>
 __global__ __launch_bounds__(256) void quantize_wave_kernel(
     const u32x4* __restrict__ W, int64_t ngroups, int cpg, uint32_t* __restrict__ packed,
-    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, ColScale cs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) / kWave;
@@ -176,6 +196,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     for (int j = lane; j < cpg; j += kWave) {
       float x[8];
       unpack8(W[c0 + j], x);
+      if (SC) apply_colscale(cs, c0 + j, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (SYM) {
@@ -192,6 +213,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     for (int j = lane; j < cpg; j += kWave) {
       float x[8];
       unpack8(W[c0 + j], x);
+      if (SC) apply_colscale(cs, c0 + j, x);
       packed[c0 + j] = pack8<SYM>(x, p);
     }
     if (lane == 0) {
@@ -203,7 +225,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
 
 template <int L, bool SYM>
 hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scales, void* zeros,
-                        int num_cus, hipStream_t stream) {
+                        const ColScale& cs, int num_cus, hipStream_t stream) {
   constexpr int U = 4;
   const int64_t steps = (nchunks + kWave * U - 1) / (kWave * U);   // wave-steps needed
   const int64_t waves_wanted = steps;
@@ -211,31 +233,35 @@ hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scal
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((quantize_lanes_kernel<L, SYM, U>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, (const u32x4*)W, nchunks, (uint32_t*)packed, (uint16_t*)scales,
-                     (uint8_t*)zeros);
-  return hipGetLastError();
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)W, nchunks,
+                       (uint32_t*)packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
+    return hipGetLastError();
+  };
+  return cs.s ? go(quantize_lanes_kernel<L, SYM, U, true>) : go(quantize_lanes_kernel<L, SYM, U, false>);
 }
 
 template <bool SYM>
 hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed, void* scales,
-                       void* zeros, int num_cus, hipStream_t stream) {
+                       void* zeros, const ColScale& cs, int num_cus, hipStream_t stream) {
   const int64_t nchunks = N * K / 8;
   switch (g) {
-    case 32: return launch_lanes<4, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
-    case 64: return launch_lanes<8, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
-    case 128: return launch_lanes<16, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
-    case 256: return launch_lanes<32, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
-    case 512: return launch_lanes<64, SYM>(W, nchunks, packed, scales, zeros, num_cus, stream);
+    case 32: return launch_lanes<4, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 64: return launch_lanes<8, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 128: return launch_lanes<16, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 256: return launch_lanes<32, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 512: return launch_lanes<64, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
     default: {
       const int64_t ngroups = N * (K / g);
       int64_t blocks = (ngroups + 3) / 4;
       const int64_t cap = (int64_t)num_cus * 8;
       if (blocks > cap) blocks = cap;
-      hipLaunchKernelGGL((quantize_wave_kernel<SYM>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const u32x4*)W, ngroups, g / 8, (uint32_t*)packed, (uint16_t*)scales,
-                         (uint8_t*)zeros);
-      return hipGetLastError();
+      auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)W, ngroups,
+                           g / 8, (uint32_t*)packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
+        return hipGetLastError();
+      };
+      return cs.s ? go(quantize_wave_kernel<SYM, true>) : go(quantize_wave_kernel<SYM, false>);
     }
   }
 }
@@ -243,9 +269,11 @@ hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed,
 }  // namespace
 
 hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
-                           void* scales, void* zeros, int num_cus, hipStream_t stream) {
-  return sym ? launch_mode<true>(W, N, K, g, packed, scales, zeros, num_cus, stream)
-             : launch_mode<false>(W, N, K, g, packed, scales, zeros, num_cus, stream);
+                           void* scales, void* zeros, int num_cus, hipStream_t stream,
+                           const float* colscale) {
+  const ColScale cs{colscale, K / 8, N * K / 8 <= (int64_t)0xffffffff};
+  return sym ? launch_mode<true>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream)
+             : launch_mode<false>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream);
 }
 
 }  // namespace q4
