@@ -79,6 +79,8 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-context", action="store_true",
                    help="skip the practical-ceiling measurements reported as context")
+    p.add_argument("--no-awq", action="store_true",
+                   help="skip the AWQ-style scaling search measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 512 MiB device copy (counter calibration)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -155,6 +157,80 @@ def measure_context(torch, q4, sets, X5, W5, w5, reps=10):
         "dequantize_ms": round(deq_ms, 4),
         "dequantize_GB/s": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
         "how": "q4_dequantize of the g=128 INT4 weights to bf16 [8192,8192], then torch.matmul"}
+    return res
+
+
+# --------------------------------------------------------------------------- AWQ-style scaling
+def measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, n_alpha=11, reps=3,
+                with_oracle=True, oracle_rows=512, oracle_calib=64):
+    """AWQ-style scaling search on the prefill layer W[8192, 8192]: `calib` calibration rows of
+    its activations, the unquantized layer output on them as the reference (torch.matmul, an
+    input of the search, not timed), n_alpha grid points, g=128 asym.  Times q4_awq_search
+    (HIP events on the launch stream) and, alone, the scaled RTN quantization it runs per alpha
+    (HBM roofline).  The oracle's awq_search_ref is timed beside it on a bounded sample
+    (`oracle_rows` rows of W, `oracle_calib` calibration rows)."""
+    import numpy as np
+    dev = W5.device
+    N, K = W5.shape
+    G = K // g
+    Xc = X5[:calib].contiguous()
+    Yref = torch.matmul(Xc, W5.t().contiguous())
+    ws = torch.empty(q4.awq_workspace_bytes(calib, N, K, g, n_alpha), dtype=torch.uint8, device=dev)
+    s_out = torch.empty(K, dtype=torch.float32, device=dev)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, G), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    errors = torch.empty(n_alpha, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    run = lambda: q4.awq_search_into(Xc, Yref, W5, g, "asym", n_alpha, ws, s_out, packed, scales, zeros,
+                                     errors, best)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    search_ms = e0.elapsed_time(e1) / reps
+    qs = lambda: q4.quantize_rtn_scaled_into(W5, s_out, g, "asym", packed, scales, zeros)
+    qs()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5 * reps):
+        qs()
+    e1.record()
+    torch.cuda.synchronize()
+    qs_ms = e0.elapsed_time(e1) / (5 * reps)
+    qs_bytes = N * K * 2 + N * K // 2 + N * G * 3
+    qs_gbs = qs_bytes / (qs_ms * 1e-3) / 1e9
+    bi = int(best.cpu().numpy()[0])
+    errs = errors.cpu().numpy()
+    res = {
+        "workload": f"AWQ-style scaling search, W[{N},{K}] asym g={g}, {calib} calibration rows, "
+                    f"{n_alpha} alphas",
+        "ms": round(search_ms, 4), "ms_per_alpha": round(search_ms / n_alpha, 4),
+        "weights_alphas_per_s": round(N * K * n_alpha / (search_ms * 1e-3), 1),
+        "best_alpha": round(bi / max(n_alpha - 1, 1), 3),
+        "error_ratio_best_vs_rtn": round(float(errs[bi] / errs[0]), 4) if errs[0] > 0 else None,
+        "quantize_scaled": {"ms": round(qs_ms, 4), "roofline": {
+            "bound": "hbm", "achieved": round(qs_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(qs_gbs / HBM_PEAK_GBS, 4)}},
+    }
+    if with_oracle:
+        from oracle import q4_oracle as orc
+        from synth import f64_to_bf16_bits
+        Wb = W5_bits[:oracle_rows]
+        Xb = X5_bits[:oracle_calib]
+        Yb = f64_to_bf16_bits(orc.bf16_bits_to_f32(Xb).astype(np.float64) @
+                              orc.bf16_bits_to_f32(Wb).astype(np.float64).T)
+        t = time.perf_counter()
+        orc.awq_search_ref(Wb, Xb, Yb, g, "asym", n_alpha)
+        spent = time.perf_counter() - t
+        res["cpu_oracle"] = {"weights_alphas_per_s": round(oracle_rows * K * n_alpha / spent, 1),
+                             "seconds": round(spent, 2), "kind": "oracle",
+                             "sample": f"oracle awq_search_ref on the first {oracle_rows} rows of W and "
+                                       f"{oracle_calib} calibration rows, {n_alpha} alphas"}
     return res
 
 
@@ -510,6 +586,8 @@ def main(argv=None):
     }
     if not args.no_context:
         out["context"] = measure_context(torch, q4, sets, X5, W5, w5)
+    if not args.no_awq:
+        out["awq"] = measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, with_oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
     print(json.dumps(out), flush=True)

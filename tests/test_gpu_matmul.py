@@ -208,3 +208,22 @@ def test_m0_is_noop_and_nondefault_stream():
     stream.synchronize()
     ok, usage = orc.check_matmul(host_bf16_to_f64(Y), Y_ref, A)
     assert ok, usage
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1024, 8192, 256, 128), (1000, 8000, 384, 64),
+                                     (512, 8192, 256, 128), (520, 8100, 256, 32)])
+def test_prefill_tile_choices(M, N, K, g):
+    """The GEMM's 128-row X tiles on a 256-CU device: 256-row W tiles when they fill every
+    compute unit (first two shapes), else twice as many 128-row W tiles (last two), each full
+    and with ragged M and N edges."""
+    import torch
+    from tests.gpu_util import log
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wide = -(-M // 128) * -(-N // 256)
+    log(f"tile choice M={M} N={N}: {wide} 128x256 tiles on {cus} CUs -> "
+        f"{'256' if wide >= cus else '128'}-row W tiles")
+    rng = np.random.default_rng(M + N + K + g + 1)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full(X_bits, W_bits, g, mode, "prefill-tiles", ("auto",))

@@ -55,8 +55,17 @@ __global__ __launch_bounds__(256) void absmean_final_kernel(const float* __restr
                                                             int slices, int64_t M, float* __restrict__ a) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
+  // the slices are independent loads: fetch them eight at a time, add them in slice order
   float sum = 0.0f;
-  for (int y = 0; y < slices; ++y) sum += partial[(size_t)y * K + k];
+  int y = 0;
+  for (; y + 8 <= slices; y += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(size_t)(y + u) * K + k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; y < slices; ++y) sum += partial[(size_t)y * K + k];
   a[k] = sum / (float)M;
 }
 
@@ -148,12 +157,14 @@ __global__ __launch_bounds__(256) void sq_err_partial_kernel(const uint16_t* __r
   if (threadIdx.x == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// One wave: lane l adds the block sums l, l + 64, ... in fp64, then a fixed butterfly.
 __global__ __launch_bounds__(64) void sq_err_final_kernel(const float* __restrict__ partial, int nb,
                                                           double* __restrict__ err) {
-  if (threadIdx.x != 0) return;
   double sum = 0.0;
-  for (int b = 0; b < nb; ++b) sum += (double)partial[b];
-  *err = sum;
+  for (int b = threadIdx.x; b < nb; b += kWave) sum += (double)partial[b];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  if (threadIdx.x == 0) *err = sum;
 }
 
 // ---- first smallest error -> best index, and that alpha's scales -> s_out.
@@ -162,12 +173,24 @@ __global__ __launch_bounds__(256) void awq_select_kernel(const double* __restric
                                                          int32_t* __restrict__ best,
                                                          float* __restrict__ s_out) {
   __shared__ int sel;
-  if (threadIdx.x == 0) {
-    int b = 0;
-    for (int i = 1; i < n_alpha; ++i)
-      if (err[i] < err[b]) b = i;
-    sel = b;
-    *best = b;
+  if (threadIdx.x < kWave) {
+    // lane i holds (err[i], i); a butterfly keeps the smaller error, the smaller index on ties
+    const int i = threadIdx.x;
+    double e = i < n_alpha ? err[i] : __builtin_huge_val();
+    int idx = i;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double oe = __shfl_xor(e, o);
+      const int oi = __shfl_xor(idx, o);
+      if (oe < e || (oe == e && oi < idx)) {
+        e = oe;
+        idx = oi;
+      }
+    }
+    if (i == 0) {
+      sel = idx;
+      *best = idx;
+    }
   }
   __syncthreads();
   const float* src = s_all + (size_t)sel * K;

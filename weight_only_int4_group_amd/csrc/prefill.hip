@@ -6,7 +6,8 @@
 // x_hat = scale * (q - z) ("DL S067 · Quantization", §1), formed exactly in fp32 by one
 // mixed-precision fma per weight and rounded once to bf16.
 //
-// Block = 4 waves, tile = 256 rows of X x 256 rows of W, k walked in steps of 128.
+// Block = 4 waves, tile = 256 (or 128) rows of X x 256 rows of W, k walked in steps of 128;
+// shapes with too few such tiles to fill every compute unit take 128 x 128 tiles instead.
 //   * X: the block's 256 x 128 bf16 slice of each step is copied global -> LDS by the
 //     direct-to-LDS loads of gfx950 (no registers), double-buffered: the copy for step s + 1
 //     is issued at the start of step s.  Rows are XOR-swizzled in 16-byte chunks so that the
@@ -133,11 +134,14 @@ __device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int,
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-// EDGE = false: every tile of the launch is full (256 W rows, 128 X rows in range), so the
+// EDGE = false: every tile of the launch is full (TN W rows, TM X rows in range), so the
 // per-lane parts of all addresses are the same for every row group and the rest is
 // wave-uniform.  EDGE = true: the last row and / or column of tiles of a ragged shape; X rows
 // past M are clamped to row M - 1 and W rows past N read as 0 (their outputs are dropped).
-template <int TM, bool SYM, bool EDGE>
+//
+// NBW: 16-row blocks of W per wave (4: 256-row W tiles; 2: 128-row tiles, for shapes whose
+// 256-row tiles would leave compute units idle).
+template <int TM, int NBW, bool SYM, bool EDGE>
 __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, int lg,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -145,7 +149,14 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     int edge_row, int vec_store) {
   static_assert(TM == kTileMSmall || TM == kTileMLarge, "tile of 128 or 256 X rows");
   constexpr int MB = TM / 16;                          // 16-row blocks of X
-  constexpr int NB = 4;                                // 16-row blocks of W per wave
+  static_assert(NBW == 4 || (NBW == 2 && TM == kTileMSmall), "256-row W tiles, or 128-row with 128 X rows");
+  constexpr int NB = NBW;                              // 16-row blocks of W per wave
+  constexpr int TN = 64 * NBW;                         // W rows per block
+  constexpr int RPW = 16 * NBW;                        // W rows per wave
+  // Scales and zero-points reach registers by per-lane loads issued with the codes (edge
+  // tiles and narrow tiles), or through LDS words copied one step ahead (full 256-row tiles,
+  // whose copy instructions cover 64 rows per wave).
+  constexpr bool REGSZ = EDGE || NBW != 4;
   constexpr int RW = TM / 4;                           // X rows each wave copies per step
   constexpr uint32_t kStageBytes = TM * kRowBytes;     // 32 or 64 KiB
   constexpr uint32_t kWaveDma = kStageBytes / 4;       // bytes each wave copies per step
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     bm = t / tiles_n;
     bn = t - bm * tiles_n;
   }
-  const int m0 = bm * TM, n0 = bn * kTileN;
+  const int m0 = bm * TM, n0 = bn * TN;
   const int KT = K / kStepK;
   const int G = K >> lg;
   const uint32_t xrow_bytes = (uint32_t)K * 2u;
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   // for every power-of-two g >= 32.  Full tiles: one lane offset (row li of a 16-row block)
   // plus a wave-uniform offset for the block and step; edge tiles: a lane offset per block,
   // so that a row past N is out of range on its own.
-  const uint32_t rows_left = (uint32_t)min(N - n0, kTileN);
+  const uint32_t rows_left = (uint32_t)min(N - n0, TN);
   const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + (size_t)n0 * (size_t)(K / 2), rows_left * (uint32_t)(K / 2));
   const __amdgpu_buffer_rsrc_t rs = buffer_over(scales + (size_t)n0 * G, rows_left * (uint32_t)G * 2u);
   const __amdgpu_buffer_rsrc_t rz = buffer_over(zeros + (size_t)n0 * G, rows_left * (uint32_t)G);
@@ -216,7 +227,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   uint32_t voff_w[NV], voff_s[NV], voff_z[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const uint32_t r = EDGE ? (uint32_t)(64 * wave + 16 * v + li) : (uint32_t)li;
+    const uint32_t r = EDGE ? (uint32_t)(RPW * wave + 16 * v + li) : (uint32_t)li;
     voff_w[v] = r * (uint32_t)(K / 2) + 16u * (uint32_t)lq;
     voff_z[v] = r * (uint32_t)G + gl;
     voff_s[v] = 2u * voff_z[v];
@@ -272,10 +283,10 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int v = EDGE ? nb : 0;
-      const int rb = EDGE ? 0 : 64 * wave + 16 * nb;    // wave-uniform row of the block
+      const int rb = EDGE ? 0 : RPW * wave + 16 * nb;   // wave-uniform row of the block
       wq[R][nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
           rw, voff_w[v], rb * (K / 2) + ktc * (kStepK / 2), 0));
-      if (EDGE) {
+      if (REGSZ) {
         ws[R][nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s[v], 2 * (rb * G + gs), 0);
         wz[R][nb] = SYM ? 8u : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, voff_z[v], rb * G + gs, 0);
       }
@@ -289,13 +300,13 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     // The previous barrier already waited for these registers; naming them here, before any
     // new load is issued, keeps the compiler's own wait for them from covering the new loads.
     asm volatile("" ::"v"(wq[R][0]), "v"(wq[R][1]), "v"(wq[R][2]), "v"(wq[R][3]));
-    if (EDGE) {
+    if (REGSZ) {
       asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
       if (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
     }
     // This step's scale / zero words (copied during the previous step) -> registers.
     uint32_t sb[NB], zb[NB];
-    if (!EDGE) {
+    if (!REGSZ) {
       const uint32_t gs = (uint32_t)((kt * kStepK) >> lg);
       const uint32_t par = rg_r + gs;
       const uint8_t* st = xl + 2u * kStageBytes + (uint32_t)R * kSzStage;
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       }
     }
     copy_x(R ^ 1, kt + 1);
-    if (!EDGE) copy_sz(R ^ 1, kt + 1);
+    if (!REGSZ) copy_sz(R ^ 1, kt + 1);
     load_w(Slot<R ^ 1>{}, kt + 1);
     // Keep the loads here: left alone, the scheduler sinks them to the end of the step to
     // shorten register lifetimes, which exposes their whole latency at the barrier.
@@ -317,8 +328,8 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     float s[NB], c1[NB], c64[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = (float)__builtin_bit_cast(_Float16, (uint16_t)(EDGE ? ws[R][nb] : sb[nb]));
-      const float zf = (float)(EDGE ? wz[R][nb] : zb[nb]);
+      s[nb] = (float)__builtin_bit_cast(_Float16, (uint16_t)(REGSZ ? ws[R][nb] : sb[nb]));
+      const float zf = (float)(REGSZ ? wz[R][nb] : zb[nb]);
       c1[nb] = -s[nb] * (1024.0f + zf);
       c64[nb] = -s[nb] * (64.0f + zf);
     }
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     // Wait for the next step's W registers, and so for everything issued before them (the X
     // and scale / zero copies), before the barrier.
     asm volatile("" ::"v"(wq[R ^ 1][0]), "v"(wq[R ^ 1][1]), "v"(wq[R ^ 1][2]), "v"(wq[R ^ 1][3]));
-    if (EDGE) {
+    if (REGSZ) {
       asm volatile("" ::"v"(ws[R ^ 1][0]), "v"(ws[R ^ 1][1]), "v"(ws[R ^ 1][2]), "v"(ws[R ^ 1][3]));
       if (!SYM) asm volatile("" ::"v"(wz[R ^ 1][0]), "v"(wz[R ^ 1][1]), "v"(wz[R ^ 1][2]), "v"(wz[R ^ 1][3]));
     }
@@ -350,10 +361,10 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 
   if constexpr (TM == kTileMSmall) {
     copy_x(0, 0);
-    if (!EDGE) copy_sz(0, 0);
+    if (!REGSZ) copy_sz(0, 0);
     load_w(Slot<0>{}, 0);
     asm volatile("" ::"v"(wq[0][0]), "v"(wq[0][1]), "v"(wq[0][2]), "v"(wq[0][3]));
-    if (EDGE) {
+    if (REGSZ) {
       asm volatile("" ::"v"(ws[0][0]), "v"(ws[0][1]), "v"(ws[0][2]), "v"(ws[0][3]));
       if (!SYM) asm volatile("" ::"v"(wz[0][0]), "v"(wz[0][1]), "v"(wz[0][2]), "v"(wz[0][3]));
     }
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         uint32_t sbits, zbits;
-        if (EDGE) {
+        if (REGSZ) {
           sbits = ws[R][nb];
           zbits = wz[R][nb];
         } else {
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     auto wait_codes = [&wq, &ws, &wz](auto S) {
       constexpr int R = decltype(S)::value;
       asm volatile("" ::"v"(wq[R][0]), "v"(wq[R][1]), "v"(wq[R][2]), "v"(wq[R][3]));
-      if (EDGE) {
+      if (REGSZ) {
         asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
         if (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
       }
@@ -438,7 +449,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
         if constexpr (g + XA < NG) bx[(g + XA) % (XA + 1)] = xfrag(g + XA);
         if constexpr (g == 0) load_w(Slot<R ^ 1>{}, kt + 1);
         if constexpr (g < kDmaOps) copy_x_piece(R ^ 1, kt + 1, g);
-        if constexpr (g == kDmaOps) { if (!EDGE) copy_sz(R ^ 1, kt + 1); }
+        if constexpr (g == kDmaOps) { if (!REGSZ) copy_sz(R ^ 1, kt + 1); }
         __builtin_amdgcn_sched_barrier(0);
         // Slot 1: the biased fp16 pairs of a new code dword.
         mfma_acc(acc[1][mb], a[ks & 1][1], b);
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     };
 
     copy_x(0, 0);
-    if (!EDGE) copy_sz(0, 0);
+    if (!REGSZ) copy_sz(0, 0);
     load_w(Slot<0>{}, 0);
     wait_codes(Slot<0>{});
     prep_scales(Slot<0>{}, 0);
@@ -493,7 +504,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + mb * 16 + li;
-      const int nbase = n0 + 64 * wave + nb * 16 + 4 * lq;
+      const int nbase = n0 + RPW * wave + nb * 16 + 4 * lq;
       if (m < M) {
         const f32x4 v = acc[nb][mb];
         uint16_t* yrow = Y + (size_t)m * N;
@@ -509,17 +520,18 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   }
 }
 
-template <int TM, bool SYM>
+template <int TM, int NBW, bool SYM>
 hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
                      const void* scales, const void* zeros, void* Y, hipStream_t stream) {
-  const int full_m = (int)(M / TM), full_n = (int)(N / kTileN);
+  constexpr int TN = 64 * NBW;
+  const int full_m = (int)(M / TM), full_n = (int)(N / TN);
   const int tiles_m = (int)((M + TM - 1) / TM);
-  const int tiles_n = (int)((N + kTileN - 1) / kTileN);
+  const int tiles_n = (int)((N + TN - 1) / TN);
   const int vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 7) == 0);
   const int64_t full_blocks = (int64_t)full_m * full_n;
   if ((int64_t)tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
   if (full_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<TM, SYM, false>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, false>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, full_m, full_n, 0, vec);
     const hipError_t e = hipGetLastError();
@@ -530,7 +542,7 @@ hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, con
   const int edge_row = tiles_m != full_m;
   const int64_t edge_blocks = (edge_row ? tiles_n : 0) + (tiles_n != full_n ? full_m : 0);
   if (edge_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<TM, SYM, true>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, true>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, tiles_m, tiles_n,
                        edge_row, vec);
@@ -545,8 +557,12 @@ hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, co
   // The 256-row tile runs one block per compute unit: take it when its tiles fill every unit.
   const int64_t large_tiles = ((M + kTileMLarge - 1) / kTileMLarge) * ((N + kTileN - 1) / kTileN);
   if (large_tiles >= num_cus)
-    return launch_tm<kTileMLarge, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
-  return launch_tm<kTileMSmall, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+    return launch_tm<kTileMLarge, 4, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  // 128 X rows: 256-row W tiles when they fill every unit, else twice as many 128-row tiles.
+  const int64_t small_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + kTileN - 1) / kTileN);
+  if (small_tiles >= num_cus)
+    return launch_tm<kTileMSmall, 4, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  return launch_tm<kTileMSmall, 2, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
 }
 
 }  // namespace

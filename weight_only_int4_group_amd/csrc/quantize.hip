@@ -95,16 +95,26 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float x[8]) {
 
 // Optional per-column scale applied before quantization (AWQ-style scaling): the weight
 // quantized is bf16(fl32(w * s_j)), one IEEE fp32 product rounded to nearest even to bf16.
-// c8 = K / 8 chunks per row; `small` says every flat chunk index fits 32 bits (then the
-// column of a chunk is a 32-bit remainder).
+// c8 = K / 8 chunks per row; `row64` says c8 is a multiple of 64, so the 64 consecutive
+// chunks of a wave step never straddle a row and their columns follow from one wave-uniform
+// remainder; `small` says every flat chunk index fits 32 bits.
 struct ColScale {
   const float* s;
   int64_t c8;
-  bool small;
+  bool row64, small;
 };
 
-__device__ __forceinline__ void apply_colscale(const ColScale& cs, int64_t chunk, float x[8]) {
-  const uint32_t cc = cs.small ? (uint32_t)chunk % (uint32_t)cs.c8 : (uint32_t)(chunk % cs.c8);
+// Column chunk of flat chunk `chunk` whose wave step starts at flat chunk `wave_base`.
+__device__ __forceinline__ uint32_t col_chunk(const ColScale& cs, int64_t wave_base, int64_t chunk) {
+  if (cs.row64) {
+    const int64_t b = __builtin_amdgcn_readfirstlane((int)(uint32_t)wave_base) |
+                      ((int64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(wave_base >> 32)) << 32);
+    return (uint32_t)(b % cs.c8) + (uint32_t)(chunk - wave_base);
+  }
+  return cs.small ? (uint32_t)chunk % (uint32_t)cs.c8 : (uint32_t)(chunk % cs.c8);
+}
+
+__device__ __forceinline__ void apply_colscale(const ColScale& cs, uint32_t cc, float x[8]) {
   const float4* sp = reinterpret_cast<const float4*>(cs.s + 8 * (size_t)cc);
   const float4 a = sp[0], b = sp[1];
   const float sv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(
       const int64_t c = (base + u) * kWave + lane;
       float x[8];
       unpack8(v[u], x);
-      if (SC) apply_colscale(cs, c < nchunks ? c : 0, x);
+      if (SC) apply_colscale(cs, c < nchunks ? col_chunk(cs, (base + u) * kWave, c) : 0u, x);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -193,10 +203,12 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
   for (int64_t grp = wave; grp < ngroups; grp += nwaves) {
     const int64_t c0 = grp * cpg;
     float lo = 0.0f, hi = 0.0f;
+    // the group's first column chunk (groups never straddle rows)
+    const uint32_t gc = SC ? (uint32_t)((grp % (cs.c8 / cpg)) * cpg) : 0u;
     for (int j = lane; j < cpg; j += kWave) {
       float x[8];
       unpack8(W[c0 + j], x);
-      if (SC) apply_colscale(cs, c0 + j, x);
+      if (SC) apply_colscale(cs, gc + (uint32_t)j, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (SYM) {
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     for (int j = lane; j < cpg; j += kWave) {
       float x[8];
       unpack8(W[c0 + j], x);
-      if (SC) apply_colscale(cs, c0 + j, x);
+      if (SC) apply_colscale(cs, gc + (uint32_t)j, x);
       packed[c0 + j] = pack8<SYM>(x, p);
     }
     if (lane == 0) {
@@ -271,7 +283,7 @@ hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed,
 hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym, void* packed,
                            void* scales, void* zeros, int num_cus, hipStream_t stream,
                            const float* colscale) {
-  const ColScale cs{colscale, K / 8, N * K / 8 <= (int64_t)0xffffffff};
+  const ColScale cs{colscale, K / 8, (K / 8) % kWave == 0, N * K / 8 <= (int64_t)0xffffffff};
   return sym ? launch_mode<true>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream)
              : launch_mode<false>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream);
 }
