@@ -255,7 +255,7 @@ def measured_clocks(d):
                 if r.get("Name", "").startswith("gfx") and int(r.get("Num_Xcc") or 0) > 0:
                     xcc = int(r["Num_Xcc"])
     out = {}
-    for label, key in (("prefill", "prefill_kernel"),):
+    for label, key in (("prefill", "prefill_kernel<256"),):
         cyc, ns = [], []
         for r in _counter_rows(d):
             if r.get("Counter_Name") == "GRBM_GUI_ACTIVE" and key in r.get("Kernel_Name", ""):

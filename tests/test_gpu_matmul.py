@@ -210,18 +210,21 @@ def test_m0_is_noop_and_nondefault_stream():
     assert ok, usage
 
 
-@pytest.mark.parametrize("M,N,K,g", [(1024, 8192, 256, 128), (1000, 8000, 384, 64),
-                                     (512, 8192, 256, 128), (520, 8100, 256, 32)])
+@pytest.mark.parametrize("M,N,K,g", [(512, 8192, 256, 128), (520, 8100, 256, 32),
+                                     (1024, 8192, 256, 128), (1000, 8000, 384, 64),
+                                     (1088, 16384, 256, 128)])
 def test_prefill_tile_choices(M, N, K, g):
-    """The GEMM's 128-row X tiles on a 256-CU device: 256-row W tiles when they fill every
-    compute unit (first two shapes), else twice as many 128-row W tiles (last two), each full
-    and with ragged M and N edges."""
+    """The GEMM's tile choice on a 256-CU device: 256 x 256 tiles when they fill every compute
+    unit (last shape), otherwise 128 x 128 tiles (the 128 x 256 tile would need twice as many
+    tiles as units, which the 256 x 256 tile already covers at this CU count), full and with
+    ragged M and N edges."""
     import torch
     from tests.gpu_util import log
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    large = -(-M // 256) * -(-N // 256)
     wide = -(-M // 128) * -(-N // 256)
-    log(f"tile choice M={M} N={N}: {wide} 128x256 tiles on {cus} CUs -> "
-        f"{'256' if wide >= cus else '128'}-row W tiles")
+    kind = "256x256" if large >= cus else ("128x256" if wide >= 2 * cus else "128x128")
+    log(f"tile choice M={M} N={N} on {cus} CUs: {kind} tiles")
     rng = np.random.default_rng(M + N + K + g + 1)
     W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
     X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
