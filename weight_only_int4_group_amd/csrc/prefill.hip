@@ -19,8 +19,8 @@
 // The k order inside a step is permuted identically for both operands (lane group q takes the
 // 32 contiguous k of its codes), which leaves each output sum unchanged.
 // MFMA: D[n][m] = sum_k W[n][k] X[m][k]; a lane's four accumulators are four consecutive n of
-// one m, written as one 8-byte store into row-major Y.  Blocks are numbered so the tiles that
-// share X rows land on one XCD (one L2).
+// one m, written as one 8-byte store into row-major Y.  Blocks are numbered so that each XCD
+// (one L2) works on a rectangle of tiles that share X and W slices.
 #include <type_traits>
 #include <utility>
 
@@ -183,9 +183,21 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     else { bm = b - first; bn = tiles_n - 1; }
   } else {
     const int tiles = tiles_m * tiles_n;
-    const int t = (tiles & 7) == 0 ? (b & 7) * (tiles >> 3) + (b >> 3) : b;
-    bm = t / tiles_n;
-    bn = t - bm * tiles_n;
+    // Blocks are dealt to the XCDs round-robin (b & 7).  With an even number of tile rows and
+    // tile columns a multiple of 4, XCD x takes the rectangle of half the tile rows by a
+    // quarter of the tile columns, so its concurrent tiles share X and W slices in its L2
+    // (per step it fetches half the X slices and a quarter of the W slices of the launch);
+    // otherwise the tiles sharing X rows go to one XCD.
+    if ((tiles_m & 1) == 0 && (tiles_n & 3) == 0) {
+      const int x = b & 7, i = b >> 3;
+      const int rm = tiles_m >> 1, rn = tiles_n >> 2;
+      bm = rm * (x & 1) + i / rn;
+      bn = rn * (x >> 1) + i % rn;
+    } else {
+      const int t = (tiles & 7) == 0 ? (b & 7) * (tiles >> 3) + (b >> 3) : b;
+      bm = t / tiles_n;
+      bn = t - bm * tiles_n;
+    }
   }
   const int m0 = bm * TM, n0 = bn * TN;
   const int KT = K / kStepK;
