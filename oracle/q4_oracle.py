@@ -53,6 +53,12 @@ R9  AWQ-style scaling ("LLM Weight Quantization ...", "GPTQ vs AWQ" toy; "DL S06
     and the error of alpha is sum (Y_alpha - Y_ref)^2 with Y_alpha the exact product of the
     scaled activations and the dequantised scaled weights and Y_ref the layer's unquantized
     output on the calibration rows (an input, as the calibration activations are).
+R10 W8A16 (the INT8 weight-only format of "LLM Weight Quantization ...", "Granularity and
+    outliers" and "DL S067" §1's INT8 ranges): the same group-wise RTN with 8-bit codes,
+    asymmetric [0, 255] with a uint8 zero-point or symmetric [-127, 127] with zero-point 0,
+    fp16 scale, one code per byte (symmetric codes as int8 two's complement); g = K is the
+    per-channel case.  [-127, 127] and [-128, 127] give the same symmetric codes, since
+    |x| / s <= 127 / (1 - 2^-11) < 127.5.
 """
 from __future__ import annotations
 
@@ -62,7 +68,8 @@ __all__ = [
     "bf16_bits_to_f32", "quantize_groups", "quantize_rtn_ref", "unpack_codes_ref",
     "dequantize_ref", "round_to_bf16_bits_ref", "dequantize_rounded_ref", "matmul_ref",
     "f32_to_bf16_bits_ref", "awq_search", "channel_absmean_ref", "awq_scales_ref",
-    "scale_columns_ref", "quantize_rtn_scaled_ref", "awq_search_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
+    "scale_columns_ref", "quantize_rtn_scaled_ref", "awq_search_ref",
+    "quantize8_rtn_ref", "codes8_ref", "dequantize8_ref", "matmul8_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
     "bits_per_weight", "weight_bytes", "format_math_row",
 ]
 
@@ -266,6 +273,48 @@ def check_matmul(Y_gpu_f64, Y_ref, A):
     usage = err / tol_ref(A)
     worst = float(usage.max()) if usage.size else 0.0
     return bool(np.all(usage <= 1.0)), worst
+
+
+# --------------------------------------------------------------------------- W8A16
+Q8_RANGE = {"asym": (0, 255), "sym": (-127, 127)}
+
+
+def quantize8_rtn_ref(W_bits, g: int = 128, mode: str = "sym"):
+    """bf16 W [N, K] -> (codes uint8 [N, K], scales fp16 [N, K/g], zeros uint8 [N, K/g]) (R10):
+    the generic group quantizer with 8-bit ranges, fp32 arithmetic, fp16 scales; symmetric
+    codes stored as int8 two's complement, zeros 0."""
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    _check_shape(N, K, g)
+    x = bf16_bits_to_f32(W_bits).reshape(N, K // g, g)
+    q_min, q_max = Q8_RANGE[mode]
+    q, s16, z = quantize_groups(x, q_min, q_max, mode)
+    codes = (q.reshape(N, K) & 0xFF).astype(np.uint8)
+    return codes, s16.astype(np.float16), z.astype(np.uint8)
+
+
+def codes8_ref(codes, mode: str) -> np.ndarray:
+    """uint8 codes -> int64 code values (symmetric: int8 two's complement)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c) if mode == "sym" else c
+
+
+def dequantize8_ref(codes, scales, zeros, g: int, mode: str) -> np.ndarray:
+    """x_hat = fp64(scale) * (q - z), exact in fp64."""
+    q = codes8_ref(codes, mode)
+    N, K = q.shape
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    z = np.zeros(s.shape, np.int64) if mode == "sym" else np.asarray(zeros).astype(np.int64)
+    if s.shape != (N, K // g) or z.shape != (N, K // g):
+        raise ValueError("scales/zeros shape does not match codes and g")
+    return (s[..., None] * (q.reshape(N, K // g, g) - z[..., None])).reshape(N, K)
+
+
+def matmul8_ref(X_bits, codes, scales, zeros, g: int, mode: str):
+    """Y_ref = X x_hat^T in fp64 and A = |X| |x_hat|^T (the tolerance scale), as matmul_ref."""
+    X = bf16_bits_to_f32(X_bits).astype(np.float64)
+    What = dequantize8_ref(codes, scales, zeros, g, mode)
+    return X @ What.T, np.abs(X) @ np.abs(What).T
 
 
 # --------------------------------------------------------------------------- AWQ-style scaling

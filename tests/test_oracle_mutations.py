@@ -28,7 +28,7 @@ MUTATIONS = {
     "dequant adds z": ("(qg - z[..., None])", "(qg + z[..., None])"),
     "symmetric q_max 8": ('quantize_groups(x, -8, 7, "sym")', 'quantize_groups(x, -8, 8, "sym")'),
     "group index off": ("s[..., None] * (qg - z[..., None])", "np.roll(s, 1, axis=-1)[..., None] * (qg - z[..., None])"),
-    "abs dropped in A": ("np.abs(X) @ np.abs(What).T", "X @ What.T"),
+    "abs dropped in A": ("    A = np.abs(X) @ np.abs(What).T", "    A = X @ What.T"),
     "bf16 ties away from zero": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m))"),
     "bf16 7 significant bits": ("np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)", "np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)"),
     "bf16 truncation": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
@@ -37,6 +37,8 @@ MUTATIONS = {
     "AWQ scored on weight error": ("err = np.linalg.norm(Y - X @ Q.T)", "err = np.linalg.norm(W - Q)"),
     "AWQ scales not normalised": ("    s = s / np.sqrt(s.max() * s.min())\n    return s.astype(np.float32)", "    return s.astype(np.float32)"),
     "AWQ grid misses alpha 1": ("alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]", "alphas = [i / n_alpha for i in range(n_alpha)]"),
+    "INT8 asym range 254": ('Q8_RANGE = {"asym": (0, 255), "sym": (-127, 127)}', 'Q8_RANGE = {"asym": (0, 254), "sym": (-127, 127)}'),
+    "INT8 sym codes offset binary": ("return np.where(c >= 128, c - 256, c) if mode == \"sym\" else c", "return c - 128 if mode == \"sym\" else c"),
     "bf16 bit rounding truncates": ("(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)", "u >> np.uint64(16)"),
 }
 
@@ -89,6 +91,9 @@ def _pins_pass(orc, golden_dir):
             return False
         from tests.test_oracle_awq import awq_pins_hold
         if not awq_pins_hold(orc):
+            return False
+        from tests.test_oracle_w8 import w8_pins_hold
+        if not w8_pins_hold(orc):
             return False
     except Exception:
         return False
