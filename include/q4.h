@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4_VERSION 10200  /* 1.2.0 */
+#define Q4_VERSION 10300  /* 1.3.0 */
 
 typedef enum {
     Q4_ASYM = 0,   /* uint4 codes [0, 15] with a uint8 zero-point per group */
@@ -226,6 +226,44 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
  * Q4_KERNEL_GEMM), or a negative status for an invalid shape.  Pure host function, no HIP
  * call. */
 int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g);
+
+/*
+ * W8A16: the same group-wise round-to-nearest with 8-bit codes, and its matmul.
+ * Source: "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
+ * "Granularity and outliers" (W8A16: INT8 weights, 16-bit activations, the conservative choice)
+ * with the formulas and INT8 ranges of "DL S067 · Quantization — INT8, INT4, GPTQ, AWQ", §1
+ * "The core math".  The rules of q4_quantize_rtn hold with these changes:
+ *   - asymmetric: codes in [0, 255], s32 = fl32(fl32(beta - alpha) / 255), z in [0, 255];
+ *     symmetric:  codes in [-127, 127], s32 = fl32(max|x| / 127), z = 0;
+ *   - g = K gives one scale per output row (per-channel).
+ * Layouts
+ *   codes   uint8 [N, K]      one code per byte; symmetric codes are int8 two's complement
+ *   scales  fp16  [N, K/g];  zeros uint8 [N, K/g] (0 in symmetric mode)
+ */
+
+/* Quantize W[N, K] (bf16) group-wise to 8-bit codes.  Arguments, alignment (W and codes 16
+ * bytes, scales 2), aliasing and errors as for q4_quantize_rtn, with codes [N, K].  Outputs are
+ * bit-exact with the rules above. */
+int q4_quantize_rtn8(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, void* codes,
+                     void* scales, void* zeros, void* stream);
+
+/* Y[M, N] = X[M, K] * dequant(codes, scales, zeros)^T, bf16 out, fp32 accumulation, with the
+ * accuracy bound of q4_matmul.  Arguments as for q4_matmul_kernel, with codes [N, K] (16-byte
+ * aligned) in place of packed.  kernel:
+ *   Q4_KERNEL_AUTO  Q4_KERNEL_GEMV when it fits, else Q4_KERNEL_GEMM (see q4_select_kernel_w8);
+ *   Q4_KERNEL_GEMV  decode GEMV for 1 <= M <= 4 with X staged in LDS, which needs
+ *                   2.25 M K <= 160 KiB (e.g. M <= 4 at K = 16384, M <= 2 at K = 28672): exact
+ *                   (q - z) in fp16 against x scaled by a power of two per 16 weights;
+ *   Q4_KERNEL_GEMM  bf16 MFMA GEMM on dequantised bf16 tiles, any M;
+ *   Q4_KERNEL_DECODE  not provided for 8-bit codes.
+ * Q4_ERR_UNSUPPORTED when the chosen kernel cannot run the shape. */
+int q4_matmul_w8(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+                 const void* codes, const void* scales, const void* zeros, void* Y, int32_t kernel,
+                 void* stream);
+
+/* The kernel q4_matmul_w8 picks under Q4_KERNEL_AUTO (Q4_KERNEL_GEMV or Q4_KERNEL_GEMM; GEMM
+ * for M == 0), or a negative status for an invalid shape.  Pure host function, no HIP call. */
+int q4_select_kernel_w8(int64_t M, int64_t N, int64_t K, int32_t g);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* q4_status_string(int status);

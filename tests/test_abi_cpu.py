@@ -29,14 +29,14 @@ def test_library_exports_all_declared_symbols():
     assert names == sorted(["q4_dequantize", "q4_matmul", "q4_matmul_kernel", "q4_quantize_rtn",
                             "q4_select_kernel", "q4_status_string", "q4_version",
                             "q4_quantize_rtn_scaled", "q4_scale_columns", "q4_awq_workspace_bytes",
-                            "q4_awq_search"])
+                            "q4_awq_search", "q4_quantize_rtn8", "q4_matmul_w8", "q4_select_kernel_w8"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
 def test_version_and_status_strings():
-    assert q4.version() == 10200
+    assert q4.version() == 10300
     for st in range(-9, 1):
         s = q4.status_string(st)
         assert s and s != "unknown status"
@@ -215,3 +215,77 @@ def _awq(X=A16, M=4, Y=B16, W=C16, N=8, K=64, g=32, mode=0, na=11, ws=WS, wsb=No
 ])
 def test_awq_search_validation(kw, status):
     assert _awq(**kw) == status
+
+
+# ---------------------------------------------------------------- W8A16 (8-bit codes, [N, K])
+def _quant8(W=A16, N=4, K=128, g=32, mode=1, p=B16, s=C16, z=D16):
+    return q4.library().q4_quantize_rtn8(W, N, K, g, mode, p, s, z, None)
+
+
+def _mm8(X=A16, M=1, N=4, K=128, g=32, mode=1, p=B16, s=C16, z=D16, Y=0x50000, kernel=0):
+    return q4.library().q4_matmul_w8(X, M, N, K, g, mode, p, s, z, Y, kernel, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), -2), (dict(K=0), -2), (dict(K=2 ** 31), -2),
+    (dict(g=16), -3), (dict(K=96, g=64), -3), (dict(mode=2), -4),
+    (dict(W=0), -1), (dict(p=0), -1), (dict(s=0), -1), (dict(z=0), -1),
+    (dict(W=A16 + 8), -5), (dict(p=B16 + 8), -5), (dict(s=C16 + 1), -5),
+    (dict(p=A16), -7), (dict(z=C16 + 2), -7),
+    # the codes are N K = 512 bytes here (the 4-bit packing would be 256): a scale buffer at
+    # byte 496 of them overlaps only with 8-bit codes
+    (dict(s=B16 + 496), -7),
+])
+def test_quantize8_validation(kw, status):
+    assert _quant8(**kw) == status
+
+
+def test_quantize4_packing_is_half_the_bytes():
+    # the same placement is accepted by the 4-bit quantizer's checks (fails only on the shape)
+    assert _quant(s=B16 + 496, N=4, K=128, g=96) == -3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), -2), (dict(M=2 ** 31), -2), (dict(N=0), -2),
+    (dict(g=8), -3), (dict(K=100), -3),
+    (dict(mode=3), -4), (dict(kernel=4), -4), (dict(kernel=-1), -4),
+    (dict(X=0), -1), (dict(p=0), -1), (dict(s=0), -1), (dict(Y=0), -1), (dict(mode=0, z=0), -1),
+    (dict(X=A16 + 2), -5), (dict(p=B16 + 8), -5), (dict(Y=0x50001), -5),
+    (dict(Y=A16), -7), (dict(Y=B16 + 400), -7), (dict(Y=C16), -7), (dict(mode=0, Y=D16), -7),
+    (dict(kernel=3), -8), (dict(M=5, kernel=1), -8),
+    (dict(M=3, K=28672, g=128, kernel=1, Y=1 << 32), -8),
+    (dict(M=1, K=81920, g=128, kernel=1, Y=1 << 32), -8),
+])
+def test_matmul_w8_validation(kw, status):
+    assert _mm8(**kw) == status
+
+
+def test_matmul_w8_m0_and_sym_zeros_null():
+    assert _mm8(X=0, M=0, Y=0, p=0, s=0, z=0) == 0
+    assert _mm8(mode=1, z=0, N=0) == -2
+
+
+def test_select_kernel_w8():
+    assert q4.select_kernel_w8(1, 28672, 8192, 128) == "gemv"
+    assert q4.select_kernel_w8(4, 4096, 16384, 128) == "gemv"     # 2.25 * 4 * 16384 = 144 KiB
+    assert q4.select_kernel_w8(2, 8192, 28672, 128) == "gemv"     # 126 KiB
+    assert q4.select_kernel_w8(3, 8192, 28672, 128) == "gemm"     # 189 KiB > 160 KiB
+    assert q4.select_kernel_w8(1, 4096, 81920, 128) == "gemm"
+    assert q4.select_kernel_w8(5, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel_w8(0, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel_w8(2048, 8192, 8192, 128) == "gemm"
+    with pytest.raises(q4.Q4Error):
+        q4.select_kernel_w8(1, 8192, 8192, 48)
+
+
+def test_w8_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    W = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q4.quantize_rtn8(W, 32, "sym")                    # CPU tensor
+    X = torch.zeros((1, 64), dtype=torch.bfloat16)
+    c = torch.zeros((4, 64), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        q4.matmul_w8(X, c, c, c, 32, "sym")
+    with pytest.raises(ValueError):
+        q4.matmul_w8_into(X, c, c, c, 32, "bogus", X)

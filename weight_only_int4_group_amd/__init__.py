@@ -15,6 +15,7 @@ __all__ = [
     "Q4Error", "library", "library_path", "quantize_rtn", "quantize_rtn_into", "matmul",
     "matmul_into", "dequantize", "dequantize_into", "quantize_rtn_scaled", "quantize_rtn_scaled_into",
     "scale_columns", "scale_columns_into", "awq_workspace_bytes", "awq_search", "awq_search_into",
+    "quantize_rtn8", "quantize_rtn8_into", "matmul_w8", "matmul_w8_into", "select_kernel_w8",
     "select_kernel", "status_string", "version", "MODES", "KERNELS", "SCALE_OPS",
 ]
 
@@ -65,6 +66,12 @@ def library() -> ctypes.CDLL:
             lib.q4_awq_search.restype = ctypes.c_int
             lib.q4_select_kernel.argtypes = [i64, i64, i64, i32]
             lib.q4_select_kernel.restype = ctypes.c_int
+            lib.q4_quantize_rtn8.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+            lib.q4_quantize_rtn8.restype = ctypes.c_int
+            lib.q4_matmul_w8.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, vp, i32, vp]
+            lib.q4_matmul_w8.restype = ctypes.c_int
+            lib.q4_select_kernel_w8.argtypes = [i64, i64, i64, i32]
+            lib.q4_select_kernel_w8.restype = ctypes.c_int
             lib.q4_status_string.argtypes = [ctypes.c_int]
             lib.q4_status_string.restype = ctypes.c_char_p
             lib.q4_version.argtypes = []
@@ -85,6 +92,13 @@ def select_kernel(M: int, N: int, K: int, g: int) -> str:
     st = library().q4_select_kernel(M, N, K, g)
     if st < 0:
         raise Q4Error(st, "q4_select_kernel")
+    return _KERNEL_NAMES[st]
+
+
+def select_kernel_w8(M: int, N: int, K: int, g: int) -> str:
+    st = library().q4_select_kernel_w8(M, N, K, g)
+    if st < 0:
+        raise Q4Error(st, "q4_select_kernel_w8")
     return _KERNEL_NAMES[st]
 
 
@@ -301,3 +315,58 @@ def awq_search(X, Yref, W, g: int = 128, mode: str = "asym", n_alpha: int = 11):
     best = torch.empty(1, dtype=torch.int32, device=dev)
     awq_search_into(X, Yref, W, g, mode, n_alpha, ws, s_out, packed, scales, zeros, errors, best)
     return s_out, packed, scales, zeros, errors, best
+
+
+def quantize_rtn8_into(W, g: int, mode: str, codes, scales, zeros) -> None:
+    """q4_quantize_rtn8 (8-bit codes, W8A16) on caller-provided outputs (no allocation)."""
+    import torch
+    _check_cuda(W, codes, scales, zeros)
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise ValueError("W must be a 2-D bfloat16 tensor")
+    N, K = W.shape
+    with torch.cuda.device(W.device):
+        st = library().q4_quantize_rtn8(_ptr(W), N, K, g, _mode(mode), _ptr(codes), _ptr(scales),
+                                        _ptr(zeros), _stream(W.device))
+    if st != 0:
+        raise Q4Error(st, "q4_quantize_rtn8")
+
+
+def quantize_rtn8(W, g: int = 128, mode: str = "sym"):
+    """W[N, K] bf16 -> (codes uint8[N, K], scales fp16[N, K/g], zeros uint8[N, K/g])."""
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    G = K // g if g > 0 else 0
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    quantize_rtn8_into(W, g, mode, codes, scales, zeros)
+    return codes, scales, zeros
+
+
+def matmul_w8_into(X, codes, scales, zeros, g: int, mode: str, Y, kernel: str = "auto") -> None:
+    """q4_matmul_w8 on a caller-provided Y (no allocation)."""
+    import torch
+    _check_cuda(X, codes, scales, zeros, Y)
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or Y.dtype != torch.bfloat16:
+        raise ValueError("X and Y must be 2-D bfloat16 tensors")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    M, K = X.shape
+    N = codes.shape[0]
+    if codes.shape[1] != K or tuple(Y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, codes {tuple(codes.shape)}, Y {tuple(Y.shape)}")
+    with torch.cuda.device(codes.device):
+        st = library().q4_matmul_w8(_ptr(X), M, N, K, g, _mode(mode), _ptr(codes), _ptr(scales),
+                                    _ptr(zeros), _ptr(Y), KERNELS[kernel], _stream(codes.device))
+    if st != 0:
+        raise Q4Error(st, "q4_matmul_w8")
+
+
+def matmul_w8(X, codes, scales, zeros, g: int = 128, mode: str = "sym", kernel: str = "auto"):
+    """Y[M, N] = X[M, K] @ dequant(codes, scales, zeros)^T with 8-bit codes, bf16."""
+    import torch
+    Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.bfloat16, device=codes.device)
+    matmul_w8_into(X, codes, scales, zeros, g, mode, Y, kernel)
+    return Y

@@ -34,6 +34,7 @@ SOURCES = {
     "prefill.hip": [],
     "decode.hip": [],
     "dequant.hip": [],
+    "gemv8.hip": [],
     # the activation scaling's IEEE division and product must not be contracted or re-associated
     "awq.hip": ["-ffp-contract=off", "-fno-fast-math"],
     "q4_abi.cpp": [],

@@ -48,7 +48,27 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float s16th, flo
   return u32x4{pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5), pack_bf16x2(w6, w7)};
 }
 
-template <int BM, int BN, int WM, int WN, bool SYM>
+// W8A16: eight 8-bit codes (two dwords, code i in byte i) -> 8 bf16 operand values, each
+// fma(q, s, -s z) exact in fp32 (fp16 scale x integer <= 255) and rounded once to bf16.
+// Symmetric codes (int8 two's complement) are offset by 128 (XOR 0x80), with z = 128.
+template <bool SYM>
+__device__ __forceinline__ u32x4 dequant8_bytes(uint32_t d0, uint32_t d1, float s, float sz) {
+  if (SYM) {
+    d0 ^= 0x80808080u;
+    d1 ^= 0x80808080u;
+  }
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[i] = __builtin_fmaf((float)((d0 >> (8 * i)) & 0xFFu), s, -sz);
+    w[i + 4] = __builtin_fmaf((float)((d1 >> (8 * i)) & 0xFFu), s, -sz);
+  }
+  return u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+               pack_bf16x2(w[6], w[7])};
+}
+
+// B: code width, 4 (W4A16, two codes per byte) or 8 (W8A16, one code per byte).
+template <int BM, int BN, int WM, int WN, bool SYM, int B = 4>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, int g,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -74,7 +94,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   const int bm = t / tiles_n, bn = t - bm * tiles_n;
   const int m0 = bm * BM, n0 = bn * BN;
   const int G = K / g;
-  const size_t rowbytes = (size_t)K / 2;
+  const size_t rowbytes = B == 8 ? (size_t)K : (size_t)K / 2;
   const int KT = (K + kBK - 1) / kBK;
 
   f32x4 acc[NB][MB];
@@ -83,7 +103,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 pw[TPT];
+  constexpr int CW = B / 4;                      // 16-byte code loads per 32 weights
+  u32x4 pw[TPT][CW];
   uint16_t ps[TPT];
   uint8_t pz[TPT];
   auto load_w = [&](int kt) {
@@ -91,17 +112,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int task = tid + 256 * i;
-      pw[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int c = 0; c < CW; ++c) pw[i][c] = u32x4{0u, 0u, 0u, 0u};
       ps[i] = 0;
       pz[i] = 0;
       if (task < TASKS) {
         const int r = task >> 1, h = task & 1;
         const int n = n0 + r;
         if (n < N && 32 * h < kvalid) {
-          pw[i] = *reinterpret_cast<const u32x4*>(packed + (size_t)n * rowbytes + (size_t)kt * 32 + 16 * h);
+          const uint8_t* src = packed + (size_t)n * rowbytes + (size_t)kt * (kBK * B / 8) + 16 * CW * h;
+#pragma unroll
+          for (int c = 0; c < CW; ++c) pw[i][c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
           const size_t gi = (size_t)n * G + (kt * kBK + 32 * h) / g;
           ps[i] = scales[gi];
-          pz[i] = SYM ? (uint8_t)8 : zeros[gi];
+          pz[i] = SYM ? (uint8_t)(B == 8 ? 128 : 8) : zeros[gi];
         }
       }
     }
@@ -114,12 +138,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(
         const int r = task >> 1, h = task & 1;
         const float s = (float)__builtin_bit_cast(_Float16, ps[i]);
         const float zf = (float)pz[i];
-        const float c1 = -s * (1024.0f + zf);
-        const float c16 = -s * (64.0f + zf);
-        const float s16th = s * 0.0625f;
         u32x4* dst = reinterpret_cast<u32x4*>(&wt[buf][r * kLdsK + 32 * h]);
+        if constexpr (B == 8) {
+          const float sz = s * zf;
 #pragma unroll
-        for (int o = 0; o < 4; ++o) dst[o] = dequant8<SYM>(pw[i][o], s, s16th, c1, c16);
+          for (int o = 0; o < 4; ++o)
+            dst[o] = dequant8_bytes<SYM>(pw[i][o / 2][2 * (o % 2)], pw[i][o / 2][2 * (o % 2) + 1], s, sz);
+        } else {
+          const float c1 = -s * (1024.0f + zf);
+          const float c16 = -s * (64.0f + zf);
+          const float s16th = s * 0.0625f;
+#pragma unroll
+          for (int o = 0; o < 4; ++o) dst[o] = dequant8<SYM>(pw[i][0][o], s, s16th, c1, c16);
+        }
       }
     }
   };
@@ -199,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int B = 4>
 hipError_t launch_cfg(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
                       const void* packed, const void* scales, const void* zeros, void* Y,
                       hipStream_t stream) {
@@ -209,11 +240,11 @@ hipError_t launch_cfg(const void* X, int64_t M, int64_t N, int64_t K, int g, boo
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 7) == 0);
   if (sym) {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, B>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, g, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, tiles_m, tiles_n, vec);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false, B>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, g, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, tiles_m, tiles_n, vec);
   }
@@ -231,6 +262,17 @@ hipError_t launch_gemm(const void* X, int64_t M, int64_t N, int64_t K, int g, bo
   if (M <= 64) return launch_cfg<64, 64, 1, 4>(X, M, N, K, g, sym, packed, scales, zeros, Y, stream);
   if (M <= 128) return launch_cfg<128, 128, 2, 2>(X, M, N, K, g, sym, packed, scales, zeros, Y, stream);
   return launch_cfg<256, 128, 4, 1>(X, M, N, K, g, sym, packed, scales, zeros, Y, stream);
+}
+
+hipError_t launch_gemm8(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
+                        const void* codes, const void* scales, const void* zeros, void* Y,
+                        int num_cus, hipStream_t stream) {
+  (void)num_cus;
+  if (M <= 16) return launch_cfg<16, 64, 1, 4, 8>(X, M, N, K, g, sym, codes, scales, zeros, Y, stream);
+  if (M <= 32) return launch_cfg<32, 64, 1, 4, 8>(X, M, N, K, g, sym, codes, scales, zeros, Y, stream);
+  if (M <= 64) return launch_cfg<64, 64, 1, 4, 8>(X, M, N, K, g, sym, codes, scales, zeros, Y, stream);
+  if (M <= 128) return launch_cfg<128, 128, 2, 2, 8>(X, M, N, K, g, sym, codes, scales, zeros, Y, stream);
+  return launch_cfg<256, 128, 4, 1, 8>(X, M, N, K, g, sym, codes, scales, zeros, Y, stream);
 }
 
 }  // namespace q4

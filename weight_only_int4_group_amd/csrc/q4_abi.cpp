@@ -64,8 +64,10 @@ int auto_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
   return Q4_KERNEL_GEMM;
 }
 
+// bits: code width, 4 (packed [N, K/2]) or 8 (codes [N, K]).
 int validate_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
-                    const void* packed, const void* scales, const void* zeros, const void* Y) {
+                    const void* packed, const void* scales, const void* zeros, const void* Y,
+                    int bits = 4) {
   int st = check_shape(N, K, g, mode);
   if (st != Q4_OK) return st;
   if (M < 0 || M > kMaxDim) return Q4_ERR_SHAPE;
@@ -75,9 +77,25 @@ int validate_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, i
     return Q4_ERR_ALIGN;
   const int64_t G = K / g;
   const Range y = range_of(Y, M * N * 2);
-  if (overlap(y, range_of(X, M * K * 2)) || overlap(y, range_of(packed, N * K / 2)) ||
+  if (overlap(y, range_of(X, M * K * 2)) || overlap(y, range_of(packed, N * K * bits / 8)) ||
       overlap(y, range_of(scales, N * G * 2)) ||
       (mode == Q4_ASYM && overlap(y, range_of(zeros, N * G))))
+    return Q4_ERR_ALIAS;
+  return Q4_OK;
+}
+
+// Quantizer arguments: W [N, K] bf16 in, codes of `bits` bits, scales and zeros out.
+int validate_quantize(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, const void* packed,
+                      const void* scales, const void* zeros, int bits) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (!W || !packed || !scales || !zeros) return Q4_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return Q4_ERR_ALIGN;
+  const int64_t G = K / g;
+  const Range w = range_of(W, N * K * 2), p = range_of(packed, N * K * bits / 8),
+              s = range_of(scales, N * G * 2), z = range_of(zeros, N * G);
+  if (overlap(w, p) || overlap(w, s) || overlap(w, z) || overlap(p, s) || overlap(p, z) ||
+      overlap(s, z))
     return Q4_ERR_ALIAS;
   return Q4_OK;
 }
@@ -119,16 +137,8 @@ const char* q4_status_string(int status) {
 
 int q4_quantize_rtn(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, void* packed,
                     void* scales, void* zeros, void* stream) {
-  int st = check_shape(N, K, g, mode);
+  const int st = validate_quantize(W, N, K, g, mode, packed, scales, zeros, 4);
   if (st != Q4_OK) return st;
-  if (!W || !packed || !scales || !zeros) return Q4_ERR_NULL;
-  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return Q4_ERR_ALIGN;
-  const int64_t G = K / g;
-  const Range w = range_of(W, N * K * 2), p = range_of(packed, N * K / 2),
-              s = range_of(scales, N * G * 2), z = range_of(zeros, N * G);
-  if (overlap(w, p) || overlap(w, s) || overlap(w, z) || overlap(p, s) || overlap(p, z) ||
-      overlap(s, z))
-    return Q4_ERR_ALIAS;
   return finish(q4::launch_quantize(W, N, K, g, mode == Q4_SYM, packed, scales, zeros, num_cus(),
                                     static_cast<hipStream_t>(stream)));
 }
@@ -271,6 +281,38 @@ int q4_dequantize(int64_t N, int64_t K, int32_t g, int32_t mode, const void* pac
 int q4_matmul(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
               const void* packed, const void* scales, const void* zeros, void* Y, void* stream) {
   return q4_matmul_kernel(X, M, N, K, g, mode, packed, scales, zeros, Y, Q4_KERNEL_AUTO, stream);
+}
+
+int q4_quantize_rtn8(const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, void* codes,
+                     void* scales, void* zeros, void* stream) {
+  const int st = validate_quantize(W, N, K, g, mode, codes, scales, zeros, 8);
+  if (st != Q4_OK) return st;
+  return finish(q4::launch_quantize8(W, N, K, g, mode == Q4_SYM, codes, scales, zeros, num_cus(),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int q4_select_kernel_w8(int64_t M, int64_t N, int64_t K, int32_t g) {
+  int st = check_shape(N, K, g, Q4_ASYM);
+  if (st != Q4_OK) return st;
+  if (M < 0 || M > kMaxDim) return Q4_ERR_SHAPE;
+  return (M >= 1 && q4::gemv8_fits(M, K)) ? Q4_KERNEL_GEMV : Q4_KERNEL_GEMM;
+}
+
+int q4_matmul_w8(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
+                 const void* codes, const void* scales, const void* zeros, void* Y, int32_t kernel,
+                 void* stream) {
+  if (kernel < Q4_KERNEL_AUTO || kernel > Q4_KERNEL_DECODE) return Q4_ERR_MODE;
+  int st = validate_matmul(X, M, N, K, g, mode, codes, scales, zeros, Y, 8);
+  if (st != Q4_OK) return st;
+  if (M == 0) return Q4_OK;
+  if (kernel == Q4_KERNEL_AUTO) kernel = q4_select_kernel_w8(M, N, K, g);
+  if (kernel == Q4_KERNEL_DECODE || (kernel == Q4_KERNEL_GEMV && !q4::gemv8_fits(M, K)))
+    return Q4_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool sym = mode == Q4_SYM;
+  if (kernel == Q4_KERNEL_GEMV)
+    return finish(q4::launch_gemv8(X, (int)M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
+  return finish(q4::launch_gemm8(X, M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
 }
 
 }  // extern "C"

@@ -36,6 +36,19 @@ hipError_t launch_sq_err(const void* Yq, const void* Yref, int64_t n, void* part
 hipError_t launch_awq_select(const void* err, int n_alpha, const void* s_all, int64_t K, void* best,
                              void* s_out, hipStream_t stream);
 
+// W8A16: 8-bit group-wise RTN (codes uint8 [N, K], one byte per code) and its matmul.
+hipError_t launch_quantize8(const void* W, int64_t N, int64_t K, int g, bool sym, void* codes,
+                            void* scales, void* zeros, int num_cus, hipStream_t stream);
+// GEMV for M <= kGemv8MaxM with X staged in LDS as scaled fp16 (gemv8_fits: 2.25 M K bytes fit).
+constexpr int64_t kGemv8MaxM = 4;
+bool gemv8_fits(int64_t M, int64_t K);
+hipError_t launch_gemv8(const void* X, int M, int64_t N, int64_t K, int g, bool sym, const void* codes,
+                        const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream);
+// MFMA GEMM for any M with 8-bit codes (the general GEMM's tiling).
+hipError_t launch_gemm8(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
+                        const void* codes, const void* scales, const void* zeros, void* Y,
+                        int num_cus, hipStream_t stream);
+
 // Decode GEMV: M == 1 with K <= kGemvMaxK, or M == 2 with K <= kGemvMaxK2 (the lane's slice
 // of X stays in registers).
 constexpr int64_t kGemvMaxK = 16384;

@@ -36,8 +36,30 @@ struct GroupParams {
 };
 
 // alpha <= 0 <= beta already; returns the stored scale, its reciprocal and the zero-point.
-template <bool SYM>
+// B = 4: codes [0, 15] / [-8, 7], scale d / 15 or d / 7 through the exact-division sequence
+// below; B = 8 (W8A16): codes [0, 255] / [-127, 127], scale d / 255 or d / 127 by an IEEE
+// division (once per group).  The caps keep d finite and are far above 65504 * k.
+template <bool SYM, int B = 4>
 __device__ __forceinline__ GroupParams group_params(float alpha, float beta_or_absmax) {
+  if constexpr (B == 8) {
+    const float d = SYM ? fminf(beta_or_absmax, 1.0e7f) : fminf(beta_or_absmax - alpha, 3.0e7f);
+    const float s32 = fminf(d / (SYM ? 127.0f : 255.0f), 65504.0f);
+    _Float16 h = (_Float16)s32;
+    if (h == (_Float16)0.0f) h = (_Float16)1.0f;
+    GroupParams p;
+    p.sf = (float)h;
+    p.s16 = __builtin_bit_cast(uint16_t, h);
+    p.rcp = __builtin_amdgcn_rcpf(p.sf);
+    if (SYM) {
+      p.zf = 0.0f;
+    } else {
+      const float t = alpha * p.rcp;
+      const float res = __builtin_fmaf(-t, p.sf, alpha);
+      const float tq = __builtin_fmaf(res, p.rcp, t);
+      p.zf = fminf(fmaxf(-rintf(tq), 0.0f), 255.0f);
+    }
+    return p;
+  }
   float d, c, k;
   if (SYM) {
     d = fminf(beta_or_absmax, 1.0e6f);       // >= 65504 * 7 saturates either way
@@ -69,17 +91,20 @@ __device__ __forceinline__ GroupParams group_params(float alpha, float beta_or_a
   return p;
 }
 
-template <bool SYM>
+template <bool SYM, int B = 4>
 __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
   const float t = x * p.rcp;
   const float res = __builtin_fmaf(-t, p.sf, x);
   const float tq = __builtin_fmaf(res, p.rcp, t);            // ~ x / s
   const float c = rintf(tq);
+  constexpr float kLo = B == 8 ? -127.0f : -8.0f, kHi = B == 8 ? 127.0f : 7.0f;
+  constexpr float kTop = B == 8 ? 255.0f : 15.0f;
+  constexpr uint32_t kMask = B == 8 ? 0xFFu : 0xFu;
   if (SYM) {
-    const float v = fminf(fmaxf(c, -8.0f), 7.0f);
-    return (uint32_t)(int)v & 0xFu;                           // 4-bit two's complement
+    const float v = fminf(fmaxf(c, kLo), kHi);
+    return (uint32_t)(int)v & kMask;                          // B-bit two's complement
   } else {
-    const float v = fminf(fmaxf(c + p.zf, 0.0f), 15.0f);
+    const float v = fminf(fmaxf(c + p.zf, 0.0f), kTop);
     return (uint32_t)v;
   }
 }
@@ -130,6 +155,28 @@ __device__ __forceinline__ uint32_t pack8(const float x[8], const GroupParams& p
   return w;
 }
 
+// Eight 8-bit codes, element i in byte i.
+template <bool SYM>
+__device__ __forceinline__ u32x2 pack8_bytes(const float x[8], const GroupParams& p) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= code_of<SYM, 8>(x[i], p) << (8 * i);
+    hi |= code_of<SYM, 8>(x[i + 4], p) << (8 * i);
+  }
+  return u32x2{lo, hi};
+}
+
+// Store the codes of chunk c (8 weights): a dword of nibbles (B = 4) or two dwords of bytes.
+template <bool SYM, int B>
+__device__ __forceinline__ void store_codes(void* codes, int64_t c, const float x[8], const GroupParams& p) {
+  if constexpr (B == 8) {
+    reinterpret_cast<u32x2*>(codes)[c] = pack8_bytes<SYM>(x, p);
+  } else {
+    reinterpret_cast<uint32_t*>(codes)[c] = pack8<SYM>(x, p);
+  }
+}
+
 template <int L>
 __device__ __forceinline__ float lanes_min(float v) {
 #pragma unroll
@@ -145,9 +192,9 @@ __device__ __forceinline__ float lanes_max(float v) {
 
 // g in {32, 64, 128, 256, 512}: a group is L = g/8 consecutive lanes, each holding one chunk.
 // A wave covers 64 consecutive chunks (512 weights) per step; U steps are loaded together.
-template <int L, bool SYM, int U, bool SC>
+template <int L, bool SYM, int U, bool SC, int B>
 __global__ __launch_bounds__(256) void quantize_lanes_kernel(
-    const u32x4* __restrict__ W, int64_t nchunks, uint32_t* __restrict__ packed,
+    const u32x4* __restrict__ W, int64_t nchunks, void* __restrict__ packed,
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, ColScale cs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -177,10 +224,9 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(
       }
       if (!SYM) lo = lanes_min<L>(lo);
       hi = lanes_max<L>(hi);
-      const GroupParams p = group_params<SYM>(lo, hi);
-      const uint32_t w = pack8<SYM>(x, p);
+      const GroupParams p = group_params<SYM, B>(lo, hi);
       if (c < nchunks) {
-        packed[c] = w;
+        store_codes<SYM, B>(packed, c, x, p);
         if ((lane & (L - 1)) == 0) {
           const int64_t grp = c / L;
           scales[grp] = p.s16;
@@ -193,9 +239,9 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(
 
 // Any g (multiple of 32): one wave per group, two passes over the group's chunks
 // (range, then codes); the second pass re-reads the group, normally from cache.
-template <bool SYM, bool SC>
+template <bool SYM, bool SC, int B>
 __global__ __launch_bounds__(256) void quantize_wave_kernel(
-    const u32x4* __restrict__ W, int64_t ngroups, int cpg, uint32_t* __restrict__ packed,
+    const u32x4* __restrict__ W, int64_t ngroups, int cpg, void* __restrict__ packed,
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, ColScale cs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -221,12 +267,12 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
     }
     if (!SYM) lo = lanes_min<kWave>(lo);
     hi = lanes_max<kWave>(hi);
-    const GroupParams p = group_params<SYM>(lo, hi);
+    const GroupParams p = group_params<SYM, B>(lo, hi);
     for (int j = lane; j < cpg; j += kWave) {
       float x[8];
       unpack8(W[c0 + j], x);
       if (SC) apply_colscale(cs, gc + (uint32_t)j, x);
-      packed[c0 + j] = pack8<SYM>(x, p);
+      store_codes<SYM, B>(packed, c0 + j, x, p);
     }
     if (lane == 0) {
       scales[grp] = p.s16;
@@ -235,7 +281,7 @@ __global__ __launch_bounds__(256) void quantize_wave_kernel(
   }
 }
 
-template <int L, bool SYM>
+template <int L, bool SYM, int B>
 hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scales, void* zeros,
                         const ColScale& cs, int num_cus, hipStream_t stream) {
   constexpr int U = 4;
@@ -247,22 +293,22 @@ hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scal
   if (blocks < 1) blocks = 1;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)W, nchunks,
-                       (uint32_t*)packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
+                       packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
     return hipGetLastError();
   };
-  return cs.s ? go(quantize_lanes_kernel<L, SYM, U, true>) : go(quantize_lanes_kernel<L, SYM, U, false>);
+  return cs.s ? go(quantize_lanes_kernel<L, SYM, U, true, B>) : go(quantize_lanes_kernel<L, SYM, U, false, B>);
 }
 
-template <bool SYM>
+template <bool SYM, int B>
 hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed, void* scales,
                        void* zeros, const ColScale& cs, int num_cus, hipStream_t stream) {
   const int64_t nchunks = N * K / 8;
   switch (g) {
-    case 32: return launch_lanes<4, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
-    case 64: return launch_lanes<8, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
-    case 128: return launch_lanes<16, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
-    case 256: return launch_lanes<32, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
-    case 512: return launch_lanes<64, SYM>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 32: return launch_lanes<4, SYM, B>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 64: return launch_lanes<8, SYM, B>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 128: return launch_lanes<16, SYM, B>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 256: return launch_lanes<32, SYM, B>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
+    case 512: return launch_lanes<64, SYM, B>(W, nchunks, packed, scales, zeros, cs, num_cus, stream);
     default: {
       const int64_t ngroups = N * (K / g);
       int64_t blocks = (ngroups + 3) / 4;
@@ -270,10 +316,10 @@ hipError_t launch_mode(const void* W, int64_t N, int64_t K, int g, void* packed,
       if (blocks > cap) blocks = cap;
       auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)W, ngroups,
-                           g / 8, (uint32_t*)packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
+                           g / 8, packed, (uint16_t*)scales, (uint8_t*)zeros, cs);
         return hipGetLastError();
       };
-      return cs.s ? go(quantize_wave_kernel<SYM, true>) : go(quantize_wave_kernel<SYM, false>);
+      return cs.s ? go(quantize_wave_kernel<SYM, true, B>) : go(quantize_wave_kernel<SYM, false, B>);
     }
   }
 }
@@ -284,8 +330,15 @@ hipError_t launch_quantize(const void* W, int64_t N, int64_t K, int g, bool sym,
                            void* scales, void* zeros, int num_cus, hipStream_t stream,
                            const float* colscale) {
   const ColScale cs{colscale, K / 8, (K / 8) % kWave == 0, N * K / 8 <= (int64_t)0xffffffff};
-  return sym ? launch_mode<true>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream)
-             : launch_mode<false>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream);
+  return sym ? launch_mode<true, 4>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream)
+             : launch_mode<false, 4>(W, N, K, g, packed, scales, zeros, cs, num_cus, stream);
+}
+
+hipError_t launch_quantize8(const void* W, int64_t N, int64_t K, int g, bool sym, void* codes,
+                            void* scales, void* zeros, int num_cus, hipStream_t stream) {
+  const ColScale cs{nullptr, K / 8, false, true};
+  return sym ? launch_mode<true, 8>(W, N, K, g, codes, scales, zeros, cs, num_cus, stream)
+             : launch_mode<false, 8>(W, N, K, g, codes, scales, zeros, cs, num_cus, stream);
 }
 
 }  // namespace q4
