@@ -59,6 +59,21 @@ R10 W8A16 (the INT8 weight-only format of "LLM Weight Quantization ...", "Granul
     fp16 scale, one code per byte (symmetric codes as int8 two's complement); g = K is the
     per-channel case.  [-127, 127] and [-128, 127] give the same symmetric codes, since
     |x| / s <= 127 / (1 - 2^-11) < 127.5.
+R11 GPTQ ("LLM Weight Quantization ...", "GPTQ vs AWQ" table and toy; overview page §2.1;
+    "DL S067" §4 "GPTQ intuition"): H = X^T X over the calibration rows (the factor 2 of
+    "DL S067" cancels in every update), dampened by damp * mean(diag H) on the diagonal with
+    damp = 0.01 as in the toy; columns are quantized in order and each column's error,
+    divided by the diagonal entry of the current inverse Hessian, is pushed onto the
+    remaining columns of its row through that inverse's row, after which the column is
+    removed from the inverse.  The toy fixes each row's scale up front from the original
+    weights; in the library's group format that reading gives every group the scale and
+    zero-point RTN computes from the original weights (so GPTQ changes codes only), and the
+    code of a compensated weight w' is clamp(rint(fl32(fl32(w') / scale)) + z): the same fp32
+    decision as RTN.  The row updates use the upper Cholesky factor U of H^-1 (U^T U = H^-1),
+    whose row i is the current inverse's row i divided by the square root of its diagonal
+    entry (the overview page's "Cholesky decomposition of the inverse Hessian"); the toy's
+    explicit downdates give the same updates.  An all-zero calibration set (mean diag H = 0)
+    carries no information: H = I, and GPTQ reduces to RTN.
 """
 from __future__ import annotations
 
@@ -70,6 +85,7 @@ __all__ = [
     "f32_to_bf16_bits_ref", "awq_search", "channel_absmean_ref", "awq_scales_ref",
     "scale_columns_ref", "quantize_rtn_scaled_ref", "awq_search_ref",
     "quantize8_rtn_ref", "codes8_ref", "dequantize8_ref", "matmul8_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
+    "gptq_toy", "gptq_hessian_ref", "gptq_ref", "pack_codes_ref",
     "bits_per_weight", "weight_bytes", "format_math_row",
 ]
 
@@ -168,9 +184,15 @@ def quantize_rtn_ref(W_bits, g: int = 128, mode: str = "asym"):
         q, s16, z = quantize_groups(x, -8, 7, "sym")
     else:
         raise ValueError(f"unknown mode {mode!r}")
-    nib = (q.reshape(N, K) & 0xF).astype(np.uint8)            # R6: two's complement nibble
-    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    packed = pack_codes_ref(q.reshape(N, K))
     return packed, s16.reshape(N, K // g).astype(np.float16), z.reshape(N, K // g).astype(np.uint8)
+
+
+def pack_codes_ref(q) -> np.ndarray:
+    """codes int[N, K] -> packed uint8[N, K/2]: even k in the low nibble, symmetric codes as
+    4-bit two's complement (R6)."""
+    nib = (np.asarray(q) & 0xF).astype(np.uint8)
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
 
 
 def unpack_codes_ref(packed, mode: str) -> np.ndarray:
@@ -421,6 +443,78 @@ def awq_search_ref(W_bits, X_bits, Yref_bits, g: int = 128, mode: str = "asym", 
     best = int(np.argmin(errs))             # first smallest
     return {"best": best, "alphas": alphas, "errors": np.array(errs), "scales": np.array(svals),
             "quant": quants[best], "absmean": a}
+
+
+# --------------------------------------------------------------------------- GPTQ
+def gptq_toy(W, X, quant, damp=0.01):
+    """The pages' toy GPTQ (R11), in fp64, for any per-element quantizer.
+
+    W [rows, d], X [m, d] calibration activations; quant(r, i, v) -> the quantized-dequantized
+    value of v in column i of row r (its scale fixed up front by the caller).  H = X^T X plus
+    damp * mean(diag H) on the diagonal; for each row, from the full inverse: quantize column i,
+    err = (w_i - Q_i) / Hinv[i, i], w[i+1:] -= err * Hinv[i, i+1:], then drop column i from the
+    inverse: Hinv -= Hinv[:, i] Hinv[i, :] / Hinv[i, i].  Returns Q [rows, d].
+    """
+    W = np.asarray(W, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    d = W.shape[1]
+    H = X.T @ X
+    H = H + damp * np.mean(np.diag(H)) * np.eye(d)
+    Q = np.zeros_like(W)
+    for r in range(W.shape[0]):
+        w = W[r].copy()
+        Hinv = np.linalg.inv(H)
+        for i in range(d):
+            Q[r, i] = quant(r, i, w[i])
+            err = (w[i] - Q[r, i]) / Hinv[i, i]
+            w[i + 1:] -= err * Hinv[i, i + 1:]
+            Hinv = Hinv - np.outer(Hinv[:, i], Hinv[i, :]) / Hinv[i, i]
+    return Q
+
+
+def gptq_hessian_ref(X_bits, damp: float = 0.01) -> np.ndarray:
+    """H = X^T X (fp64, X the bf16 calibration rows) + damp * mean(diag H) * I; I when X is all
+    zero (R11)."""
+    X = bf16_bits_to_f32(X_bits).astype(np.float64)
+    H = X.T @ X
+    m = np.mean(np.diag(H))
+    if m == 0.0:
+        return np.eye(H.shape[0])
+    return H + damp * m * np.eye(H.shape[0])
+
+
+def gptq_ref(W_bits, X_bits, g: int = 128, mode: str = "asym", damp: float = 0.01):
+    """GPTQ of a bf16 weight W[N, K] on bf16 calibration rows X[M, K], in the library's INT4
+    group format (R11): (packed uint8[N, K/2], scales fp16[N, K/g], zeros uint8[N, K/g]).
+
+    The scales and zero-points are RTN's on the original weights (fixed up front).  The sweep
+    runs in fp64 over all rows at once, column by column, with U the upper Cholesky factor of
+    H^-1: code of the compensated column (fp32 decision, as RTN), err = (w_i - x_hat_i) / U_ii,
+    w[:, i+1:] -= err U[i, i+1:].
+    """
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    _check_shape(N, K, g)
+    if np.asarray(X_bits).shape[1:] != (K,):
+        raise ValueError("X must have K columns")
+    q_min, q_max = {"asym": (0, 15), "sym": (-8, 7)}[mode]
+    W32 = bf16_bits_to_f32(W_bits)
+    _, s16, z = quantize_groups(W32.reshape(N, K // g, g), q_min, q_max, mode)
+    s32 = s16.astype(np.float32)                              # [N, G]
+    s64 = s32.astype(np.float64)
+    H = gptq_hessian_ref(X_bits, damp)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T               # upper, U^T U = H^-1
+    w = W32.astype(np.float64)
+    q = np.empty((N, K), dtype=np.int64)
+    for i in range(K):
+        G = i // g
+        quot = w[:, i].astype(np.float32) / s32[:, G]         # fl32(fl32(w') / scale)
+        r = np.clip(np.rint(quot), np.float32(-2.0 ** 40), np.float32(2.0 ** 40)).astype(np.int64)
+        q[:, i] = np.clip(r + z[:, G], q_min, q_max)
+        what = s64[:, G] * (q[:, i] - z[:, G])
+        err = (w[:, i] - what) / U[i, i]
+        w[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    return pack_codes_ref(q), s16.astype(np.float16), z.astype(np.uint8)
 
 
 # --------------------------------------------------------------------------- format math

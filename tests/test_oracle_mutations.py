@@ -39,6 +39,11 @@ MUTATIONS = {
     "AWQ grid misses alpha 1": ("alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]", "alphas = [i / n_alpha for i in range(n_alpha)]"),
     "INT8 asym range 254": ('Q8_RANGE = {"asym": (0, 255), "sym": (-127, 127)}', 'Q8_RANGE = {"asym": (0, 254), "sym": (-127, 127)}'),
     "INT8 sym codes offset binary": ("return np.where(c >= 128, c - 256, c) if mode == \"sym\" else c", "return c - 128 if mode == \"sym\" else c"),
+    "GPTQ toy without damping": ("    H = H + damp * np.mean(np.diag(H)) * np.eye(d)\n    Q = np.zeros_like(W)", "    Q = np.zeros_like(W)"),
+    "GPTQ toy error not divided by the diagonal": ("err = (w[i] - Q[r, i]) / Hinv[i, i]", "err = (w[i] - Q[r, i])"),
+    "GPTQ toy inverse not downdated": ("            Hinv = Hinv - np.outer(Hinv[:, i], Hinv[i, :]) / Hinv[i, i]\n", ""),
+    "GPTQ Cholesky of H instead of its inverse": ("np.linalg.cholesky(np.linalg.inv(H)).T", "np.linalg.cholesky(H).T"),
+    "GPTQ codes from the original weights": ("quot = w[:, i].astype(np.float32) / s32[:, G]", "quot = W32[:, i] / s32[:, G]"),
     "bf16 bit rounding truncates": ("(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)", "u >> np.uint64(16)"),
 }
 
@@ -94,6 +99,9 @@ def _pins_pass(orc, golden_dir):
             return False
         from tests.test_oracle_w8 import w8_pins_hold
         if not w8_pins_hold(orc):
+            return False
+        from tests.test_oracle_gptq import gptq_pins_hold
+        if not gptq_pins_hold(orc):
             return False
     except Exception:
         return False
