@@ -9,7 +9,10 @@ One step is one pass of the whole path over synthetic inputs resident in HBM:
   3. prefill   -- W4A16 GEMM, M = 2048, W[8192, 8192] (asym, g=128 and g=32)
 The headline value is the decode GEMV's HBM throughput: algorithmic bytes (packed codes +
 fp16 scales + uint8 zeros + X + Y) per launch / measured launch time, HIP events on the
-launch stream.  Parity against the CPU oracle is asserted on sampled outputs before timing.
+launch stream.  The CPU-baseline leg times the oracle on a bounded sample and asserts parity of
+sampled GPU outputs against it before timing (both skipped with --no-cpu-baseline).
+Also reported: the W8A16 path (8-bit codes), the AWQ-style scaling search, and practical
+ceilings (a plain streaming read, a device copy, the vendor bf16 GEMM) as context.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR   (writes the traffic summary)
@@ -34,6 +37,14 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_70b_mlp_m1_traffic.md")
 GEMV_SRC = os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", "gemv.hip")
+
+
+def note(msg):
+    """Progress of the run on stderr (the JSON result alone goes to stdout)."""
+    print(f"bench: {msg} ({time.perf_counter() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
+_T0 = time.perf_counter()
 
 
 def weight_bytes(N, K, g, mode):
@@ -75,12 +86,15 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--layers", type=int, default=6, help="distinct decode weight copies per step")
-    p.add_argument("--no-check", action="store_true", help="skip the parity assertion")
+    p.add_argument("--no-check", action="store_true",
+                   help="skip the parity assertion of the CPU-baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-context", action="store_true",
                    help="skip the practical-ceiling measurements reported as context")
     p.add_argument("--no-awq", action="store_true",
                    help="skip the AWQ-style scaling search measurement")
+    p.add_argument("--no-w8", action="store_true",
+                   help="skip the W8A16 (8-bit codes) measurements")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 512 MiB device copy (counter calibration)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -232,6 +246,131 @@ def measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, n_alpha=1
                              "sample": f"oracle awq_search_ref on the first {oracle_rows} rows of W and "
                                        f"{oracle_calib} calibration rows, {n_alpha} alphas"}
     return res
+
+
+def measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5, copies=3, reps=30, with_oracle=True,
+               oracle_rows=2048):
+    """W8A16 (8-bit codes) on the 70B-shaped weight W[28672, 8192]: the decode GEMV at M=1,
+    per-channel (g = K, the pages' W8A16) and g=128, symmetric, rotating over `copies` quantized
+    copies (705 MB) so the Infinity Cache cannot serve them, and M=4; the 8-bit RTN quantizer;
+    the 8-bit GEMM at the prefill shape M=2048.  HIP events on the launch stream.  Before timing,
+    the GPU's codes of the first and last 64 rows are compared bit for bit with the oracle's and
+    the decode outputs of those rows checked against the oracle's product (tolerance usage); these
+    checks and the oracle's own timing belong to the CPU-baseline leg (skipped with
+    --no-cpu-baseline)."""
+    import numpy as np
+    dev = W4.device
+    N, K = W4.shape
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {"workload": f"W8A16 on W[{N},{K}] (70B-shaped MLP), sym; GEMM on W[{W5.shape[0]},{W5.shape[1]}] M={X5.shape[0]}"}
+    usage = 0.0
+    for g in (K, 128):
+        G = K // g
+        sets = [q4.quantize_rtn8(W4, g, "sym") for _ in range(copies)]
+        torch.cuda.synchronize()
+        if with_oracle:
+            from oracle import q4_oracle as orc
+            rows = np.r_[0:64, N - 64:N]
+            ref = orc.quantize8_rtn_ref(W4_bits[rows], g, "sym")
+            got = (sets[0][0].cpu().numpy()[rows], sets[0][1].cpu().view(torch.int16).numpy().view(np.uint16)[rows],
+                   sets[0][2].cpu().numpy()[rows])
+            for a, b in zip(got, (ref[0], ref[1].view(np.uint16), ref[2])):
+                if not np.array_equal(a, b):
+                    raise AssertionError(f"W8A16 quantize parity failed (g={g})")
+        for M in ((1, 4) if g == 128 else (1,)):
+            X = X4[:1].expand(M, K).contiguous() if M > X4.shape[0] else X4[:M].contiguous()
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = lambda i: q4.matmul_w8_into(X, *sets[i % copies], g, "sym", Y)
+            ms = timed(fn, reps)
+            by = N * K + 2 * N * G + 2 * M * K + 2 * M * N
+            gbs = by / (ms * 1e-3) / 1e9
+            if with_oracle:
+                q4.matmul_w8_into(X, *sets[0], g, "sym", Y)
+                torch.cuda.synchronize()
+                Yh = Y.float().cpu().numpy().astype(np.float64)
+                Xb = X.cpu().view(torch.int16).numpy().view(np.uint16)
+                Yr, A = orc.matmul8_ref(Xb, ref[0], ref[1], ref[2], g, "sym")
+                ok, u = orc.check_matmul(Yh[:, rows], Yr, A)
+                if not ok:
+                    raise AssertionError(f"W8A16 GEMV parity failed (g={g}, M={M}, usage {u})")
+                usage = max(usage, u)
+            key = f"gemv_g{'K' if g == K else g}_M{M}"
+            res[key] = {"ms": round(ms, 5), "bytes_per_launch": by, "kernel": "gemv8_kernel",
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        if g == 128:
+            outs = sets
+            qfn = lambda i: q4.quantize_rtn8_into(W4, g, "sym", *outs[i % copies])
+            qms = timed(qfn, 10)
+            qby = 2 * N * K + N * K + 2 * N * G
+            res["quantize_g128"] = {"ms": round(qms, 5), "bytes": qby, "roofline": {
+                "bound": "hbm", "achieved": round(qby / (qms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(qby / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        del sets
+    w5 = q4.quantize_rtn8(W5, 128, "sym")
+    Y5 = torch.empty((X5.shape[0], W5.shape[0]), dtype=torch.bfloat16, device=dev)
+    gms = timed(lambda i: q4.matmul_w8_into(X5, *w5, 128, "sym", Y5), 5)
+    tf = 2.0 * X5.shape[0] * W5.shape[0] * W5.shape[1] / (gms * 1e-3) / 1e12
+    res["gemm_g128_M2048"] = {"ms": round(gms, 4), "roofline": {
+        "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+    if with_oracle:
+        res["parity_max_tolerance_usage"] = round(usage, 4)
+        from oracle import q4_oracle as orc
+        Wb = W4_bits[:oracle_rows]
+        t = time.perf_counter()
+        c, sc, z = orc.quantize8_rtn_ref(Wb, K, "sym")
+        t1 = time.perf_counter()
+        orc.matmul8_ref(X4_bits[:1], c, sc, z, K, "sym")
+        t2 = time.perf_counter()
+        res["cpu_oracle"] = {"kind": "oracle", "sample": f"the first {oracle_rows} rows, per-channel sym",
+                             "quantize_weights_per_s": round(oracle_rows * K / (t1 - t), 1),
+                             "gemv_GBps_weight_bytes": round(oracle_rows * (K + 2) / (t2 - t1) / 1e9, 4)}
+    return res
+
+
+def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
+    """The Llama-7B MLP up-projection decode, W[11008, 4096] asym g=128, M=1, seeded synthetic
+    inputs of that workload: W4A16 GEMV over enough distinct quantized copies that the
+    Infinity Cache cannot serve them, HIP events around `reps` back-to-back launches."""
+    from synth import CONFIGS, make_layer
+    import numpy as np
+    c = CONFIGS[1]
+    W_bits, X_bits = make_layer(c, M=1)
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    W, X = up(W_bits), up(X_bits)
+    by = matmul_bytes(1, c.N, c.K, c.g, c.mode)
+    copies = int(min_bytes // weight_bytes(c.N, c.K, c.g, c.mode)) + 1
+    sets = [q4.quantize_rtn(W, c.g, c.mode) for _ in range(copies)]
+    Y = torch.empty((1, c.N), dtype=torch.bfloat16, device=dev)
+    for i in range(copies):
+        q4.matmul_into(X, *sets[i], c.g, c.mode, Y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        q4.matmul_into(X, *sets[r % copies], c.g, c.mode, Y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"workload": f"{c.name}, {copies} weight copies", "kernel": q4.select_kernel(1, c.N, c.K, c.g),
+            "ms": round(ms, 5), "bytes_per_launch": by,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
 # --------------------------------------------------------------------------- counters
@@ -492,9 +631,12 @@ def main(argv=None):
         copy_dst = torch.empty_like(copy_src)
     torch.cuda.synchronize()
 
+    # The parity assertion is part of the CPU-baseline leg: the oracle runs only there.
+    note("inputs ready")
     max_usage = None
-    if not args.no_check:
+    if not args.no_check and not args.no_cpu_baseline:
         max_usage = check_parity(q4, torch, W4_bits, X4_bits, sets, Y4, W5_bits, X5_bits, X5, w5, Y5)
+        note("parity checked against the oracle")
 
     n_ev = 5
     def step(t, ev):
@@ -524,6 +666,7 @@ def main(argv=None):
         step(args.warmup + t, evs[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    note(f"{args.steps} timed steps done")
 
     def mean_ms(i, j):
         return sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs)
@@ -586,10 +729,19 @@ def main(argv=None):
     }
     if not args.no_context:
         out["context"] = measure_context(torch, q4, sets, X5, W5, w5)
+        note("context measured")
+    out["gemv_llama7b_up"] = measure_gemv_7b(torch, q4)
+    note("Llama-7B-shaped decode measured")
+    if not args.no_w8:
+        out["w8a16"] = measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5,
+                                  with_oracle=not args.no_cpu_baseline)
+        note("W8A16 measured")
     if not args.no_awq:
         out["awq"] = measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, with_oracle=not args.no_cpu_baseline)
+        note("AWQ search measured")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
+        note("CPU baseline timed")
     print(json.dumps(out), flush=True)
     return 0
 

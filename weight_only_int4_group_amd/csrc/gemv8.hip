@@ -10,8 +10,8 @@
 //     packed fp16 subtraction of 1024 + z leaves the integer q - z (|q - z| <= 255).
 //     Symmetric codes (int8) are offset by 128 (XOR of the sign bit) and taken with z = 128.
 //   * x is staged in LDS as fp16 after scaling each (row, 16-weight chunk) by the power of two
-//     2^e that puts its largest |x| in [2^14, 2^15): exact for every x down to 2^-17 of that
-//     largest value, and off by at most 2^-39 of it below.
+//     2^e that puts its largest |x| in [2^14, 2^15): exact for every x down to 2^-31 of that
+//     largest value, and off by at most 2^-39 of it below (fp16 subnormal rounding).
 //   * v_dot2_f32_f16 takes exact products with fp32 sums; each chunk's dot is multiplied by
 //     scale * 2^-e and accumulated in fp32; the row total is rounded once to bf16.
 //
