@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4_VERSION 10300  /* 1.3.0 */
+#define Q4_VERSION 10400  /* 1.4.0 */
 
 typedef enum {
     Q4_ASYM = 0,   /* uint4 codes [0, 15] with a uint8 zero-point per group */
@@ -90,7 +90,8 @@ enum {
     Q4_ERR_HIP = -6,       /* the HIP runtime rejected a launch                              */
     Q4_ERR_ALIAS = -7,     /* an output buffer overlaps an input or another output          */
     Q4_ERR_UNSUPPORTED = -8, /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
-    Q4_ERR_WORKSPACE = -9  /* workspace smaller than q4_awq_workspace_bytes() requires        */
+    Q4_ERR_WORKSPACE = -9, /* workspace smaller than the matching *_workspace_bytes() requires */
+    Q4_ERR_VALUE = -10     /* a numeric parameter out of range (GPTQ damping)                 */
 };
 
 /*
@@ -264,6 +265,47 @@ int q4_matmul_w8(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int3
 /* The kernel q4_matmul_w8 picks under Q4_KERNEL_AUTO (Q4_KERNEL_GEMV or Q4_KERNEL_GEMM; GEMM
  * for M == 0), or a negative status for an invalid shape.  Pure host function, no HIP call. */
 int q4_select_kernel_w8(int64_t M, int64_t N, int64_t K, int32_t g);
+
+/*
+ * GPTQ: quantization that compensates each column's rounding error in the columns not yet
+ * quantized, through the inverse Hessian of the layer's calibration inputs.
+ * Source: "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
+ * "GPTQ vs AWQ: two ways to choose what error to keep" (table and toy); the overview page,
+ * §2.1 (column-by-column quantization with a Cholesky factorisation of the inverse Hessian);
+ * "DL S067 · Quantization", §4 "GPTQ intuition" (the update rule).  Rules this library fixes:
+ *   - H = X^T X in fp32 over the M calibration rows, plus damp * mean(diag H) on the diagonal
+ *     (damp = 0.01 in the pages' toy); an all-zero X gives H = I, i.e. plain RTN;
+ *   - each group's scale and zero-point are RTN's on the original weights (fixed up front, as
+ *     the toy fixes its row scale), so the output differs from q4_quantize_rtn in codes only;
+ *   - columns are processed in order; the code of a compensated weight w' is
+ *     clamp(rint(fl32(w' / scale)) + z), the same fp32 decision as RTN;
+ *   - the compensation runs in fp32 (H, its Cholesky factor and the accumulated updates), so
+ *     codes can differ from an exact evaluation where w' / scale lies close to a rounding
+ *     boundary; the outputs are deterministic.
+ * The matmul kernels consume the result like any q4_quantize_rtn output.
+ */
+
+/* Bytes of device workspace q4_gptq needs: 4 K^2 + 4 N K + 128 N bytes, rounded up per part to
+ * 256; or a negative status (Q4_ERR_SHAPE when M < 1 or K > 32768, the q4_quantize_rtn errors
+ * otherwise).  Pure host function, no HIP call. */
+int64_t q4_gptq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t g);
+
+/* GPTQ of W on calibration activations X, enqueued on `stream` without host synchronization.
+ *   X        device, bf16 [M, K] calibration activations, 16-byte aligned; 1 <= M <= 2^31 - 1
+ *   W        device, bf16 [N, K] weights, 16-byte aligned; K <= 32768
+ *   g, mode  as for q4_quantize_rtn
+ *   damp     finite, >= 0 (else Q4_ERR_VALUE)
+ *   workspace, workspace_bytes  device scratch of at least q4_gptq_workspace_bytes(M, N, K, g)
+ *            bytes, 256-byte aligned, owned by the caller; contents are overwritten
+ *   packed, scales, zeros  outputs as for q4_quantize_rtn
+ *   info     device, int32 [1], 4-byte aligned (output): 0, or j + 1 when the Cholesky
+ *            factorisation met a non-positive pivot at (reversed) column j, which it replaced
+ *            by a tiny positive value so that the outputs are still written
+ * No output may overlap an input, the workspace or another output (Q4_ERR_ALIAS); errors
+ * otherwise as for q4_quantize_rtn plus Q4_ERR_WORKSPACE. */
+int q4_gptq(const void* X, int64_t M, const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, float damp,
+            void* workspace, int64_t workspace_bytes, void* packed, void* scales, void* zeros, void* info,
+            void* stream);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* q4_status_string(int status);

@@ -29,15 +29,16 @@ def test_library_exports_all_declared_symbols():
     assert names == sorted(["q4_dequantize", "q4_matmul", "q4_matmul_kernel", "q4_quantize_rtn",
                             "q4_select_kernel", "q4_status_string", "q4_version",
                             "q4_quantize_rtn_scaled", "q4_scale_columns", "q4_awq_workspace_bytes",
-                            "q4_awq_search", "q4_quantize_rtn8", "q4_matmul_w8", "q4_select_kernel_w8"])
+                            "q4_awq_search", "q4_quantize_rtn8", "q4_matmul_w8", "q4_select_kernel_w8",
+                            "q4_gptq_workspace_bytes", "q4_gptq"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
 def test_version_and_status_strings():
-    assert q4.version() == 10300
-    for st in range(-9, 1):
+    assert q4.version() == 10400
+    for st in range(-10, 1):
         s = q4.status_string(st)
         assert s and s != "unknown status"
     assert q4.status_string(-99) == "unknown status"
@@ -289,3 +290,33 @@ def test_w8_binding_rejects_bad_tensors_before_the_library():
         q4.matmul_w8(X, c, c, c, 32, "sym")
     with pytest.raises(ValueError):
         q4.matmul_w8_into(X, c, c, c, 32, "bogus", X)
+
+
+# ---------------------------------------------------------------- GPTQ
+def _gptq(X=A16, M=8, W=B16, N=4, K=128, g=32, mode=0, damp=0.01, ws=0x100000, wsb=1 << 30, p=C16, s=D16,
+          z=0x50000, info=0x60000):
+    return q4.library().q4_gptq(X, M, W, N, K, g, mode, damp, ws, wsb, p, s, z, info, None)
+
+
+def test_gptq_workspace_bytes():
+    lib = q4.library()
+    N, K = 4096, 8192
+    up = lambda b: (b + 255) // 256 * 256
+    assert lib.q4_gptq_workspace_bytes(512, N, K, 128) == up(4 * K * K) + up(4 * N * K) + up(128 * N)
+    assert lib.q4_gptq_workspace_bytes(0, N, K, 128) == -2
+    assert lib.q4_gptq_workspace_bytes(1, N, 65536, 128) == -2
+    assert lib.q4_gptq_workspace_bytes(1, N, K, 48) == -3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), -2), (dict(N=0), -2), (dict(K=65536), -2), (dict(g=16), -3), (dict(mode=2), -4),
+    (dict(damp=-0.1), -10), (dict(damp=float("nan")), -10), (dict(damp=float("inf")), -10),
+    (dict(X=0), -1), (dict(W=0), -1), (dict(ws=0), -1), (dict(p=0), -1), (dict(s=0), -1), (dict(z=0), -1),
+    (dict(info=0), -1),
+    (dict(X=A16 + 8), -5), (dict(W=B16 + 2), -5), (dict(p=C16 + 4), -5), (dict(s=D16 + 1), -5),
+    (dict(ws=0x100010), -5), (dict(info=0x60002), -5),
+    (dict(wsb=1000), -9),
+    (dict(p=A16), -7), (dict(s=B16 + 64), -7), (dict(info=0x100000 + 512), -7), (dict(z=C16 + 16), -7),
+])
+def test_gptq_validation(kw, status):
+    assert _gptq(**kw) == status

@@ -1,0 +1,129 @@
+"""GPU GPTQ (q4_gptq) against the CPU oracle's gptq_ref (reading R11 of the oracle).
+
+The scales and zero-points are RTN's and must be bit-exact.  The codes come from a sequential
+compensation that the GPU runs in fp32 and the oracle in fp64, so a code whose compensated
+weight lies near a rounding boundary may differ (and steer later columns of its row slightly
+differently); the comparison is therefore: at least 97 % identical codes, and a calibration
+output error ||X W^T - X W_hat^T|| within 2 % of the oracle's and below RTN's.  Cases without
+any compensation (a diagonal Hessian, an all-zero calibration set) must equal RTN bit for bit,
+and two runs must give identical outputs.
+"""
+import numpy as np
+import pytest
+
+from oracle import q4_oracle as orc
+from synth import CONFIGS, bf16_bits_to_f32, f64_to_bf16_bits, make_layer
+
+pytestmark = pytest.mark.gpu
+
+MIN_SAME = 0.97
+ERR_RATIO = 1.02
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    from tests.gpu_util import require_gpu
+    require_gpu()
+
+
+def _layer(N, K, M, seed, n_salient=4, factor=8.0):
+    """Correlated calibration activations with a few large channels, Gaussian weights."""
+    rng = np.random.default_rng(seed)
+    mix = rng.normal(0, 1, (K, K)) / np.sqrt(K)
+    fac = np.ones(K)
+    fac[rng.choice(K, n_salient, replace=False)] = factor
+    X = (rng.normal(0, 1, (M, K)) @ mix + 0.3 * rng.normal(0, 1, (M, K))) * fac
+    W = rng.normal(0, 0.05, (N, K))
+    return f64_to_bf16_bits(W), f64_to_bf16_bits(X)
+
+
+def _run(W_bits, X_bits, g, mode, damp=0.01):
+    import torch
+    import weight_only_int4_group_amd as q4
+    from tests.gpu_util import dev_bf16, host_u16
+    p, s, z, info = q4.gptq(dev_bf16(X_bits), dev_bf16(W_bits), g, mode, damp)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), host_u16(s), z.cpu().numpy(), int(info.cpu().numpy()[0])
+
+
+def _out_err(X_bits, W_bits, quant, g, mode, rows=None):
+    X = bf16_bits_to_f32(X_bits).astype(np.float64)
+    W = bf16_bits_to_f32(W_bits).astype(np.float64)
+    What = orc.dequantize_ref(*quant, g, mode)
+    if rows is not None:
+        W = W[rows]
+    return np.linalg.norm(X @ W.T - X @ What.T)
+
+
+def _compare(W_bits, X_bits, g, mode, label, rows=None):
+    from tests.gpu_util import log
+    p, s, z, info = _run(W_bits, X_bits, g, mode)
+    assert info == 0, f"{label}: Cholesky pivot failure at {info - 1}"
+    Wr = W_bits if rows is None else W_bits[rows]
+    rp, rs, rz = orc.gptq_ref(Wr, X_bits, g, mode)
+    if rows is not None:
+        p, s, z = p[rows], s[rows], z[rows]
+    assert np.array_equal(s, rs.view(np.uint16)), f"{label}: scales differ"
+    assert np.array_equal(z, rz), f"{label}: zeros differ"
+    same = (orc.unpack_codes_ref(p, mode) == orc.unpack_codes_ref(rp, mode)).mean()
+    e_gpu = _out_err(X_bits, Wr, (p, s.view(np.float16), z), g, mode)
+    e_ref = _out_err(X_bits, Wr, (rp, rs, rz), g, mode)
+    e_rtn = _out_err(X_bits, Wr, orc.quantize_rtn_ref(Wr, g, mode), g, mode)
+    log(f"gptq {label} N={Wr.shape[0]} K={Wr.shape[1]} M={X_bits.shape[0]} g={g} {mode}: codes same {same:.4f}, "
+        f"calibration error gpu/oracle {e_gpu / e_ref:.4f}, oracle/rtn {e_ref / e_rtn:.4f}")
+    assert same >= MIN_SAME, f"{label}: only {same:.4f} of the codes agree"
+    assert e_gpu <= ERR_RATIO * e_ref, f"{label}: error {e_gpu} vs oracle {e_ref}"
+    assert e_gpu < e_rtn
+
+
+@pytest.mark.parametrize("N,K,M,g,mode", [(64, 256, 512, 32, "asym"), (48, 512, 300, 128, "sym"),
+                                          (33, 384, 200, 64, "asym"), (100, 1024, 512, 128, "asym"),
+                                          (16, 96, 64, 32, "sym"), (300, 160, 1000, 32, "asym"),
+                                          (20, 480, 96, 96, "asym")])
+def test_gptq_matches_oracle(N, K, M, g, mode):
+    W_bits, X_bits = _layer(N, K, M, N + K + M + g)
+    _compare(W_bits, X_bits, g, mode, "layer")
+
+
+@pytest.mark.parametrize("mode", ["asym", "sym"])
+def test_gptq_diagonal_hessian_is_rtn(mode):
+    rng = np.random.default_rng(5)
+    K = 256
+    X = np.diag(np.exp2(rng.integers(-3, 4, K)).astype(np.float64))
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.05, (40, K)))
+    p, s, z, info = _run(W_bits, f64_to_bf16_bits(X), 64, mode)
+    rp, rs, rz = orc.quantize_rtn_ref(W_bits, 64, mode)
+    assert info == 0
+    assert np.array_equal(p, rp) and np.array_equal(s, rs.view(np.uint16)) and np.array_equal(z, rz)
+
+
+@pytest.mark.parametrize("mode", ["asym", "sym"])
+def test_gptq_zero_calibration_is_rtn(mode):
+    W_bits, _ = _layer(24, 128, 16, 6)
+    p, s, z, info = _run(W_bits, np.zeros((16, 128), np.uint16), 32, mode)
+    rp, rs, rz = orc.quantize_rtn_ref(W_bits, 32, mode)
+    assert info == 0
+    assert np.array_equal(p, rp) and np.array_equal(s, rs.view(np.uint16)) and np.array_equal(z, rz)
+
+
+def test_gptq_deterministic_and_damping():
+    W_bits, X_bits = _layer(64, 512, 256, 9)
+    a = _run(W_bits, X_bits, 128, "asym")
+    b = _run(W_bits, X_bits, 128, "asym")
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    # a larger dampening moves the result towards RTN (fewer codes changed)
+    c = _run(W_bits, X_bits, 128, "asym", damp=10.0)
+    rtn = orc.unpack_codes_ref(orc.quantize_rtn_ref(W_bits, 128, "asym")[0], "asym")
+    changed = lambda r: (orc.unpack_codes_ref(r[0], "asym") != rtn).mean()
+    assert changed(c) < changed(a)
+
+
+def test_gptq_prefill_layer_sampled_rows():
+    """The prefill layer W[8192, 8192] with 512 calibration rows of its activations: every row
+    quantized on the GPU, 12 rows compared with the oracle (which factors the full Hessian)."""
+    cfg = CONFIGS[4]
+    W_bits, X_bits = make_layer(cfg)
+    X_bits = X_bits[:512]
+    rows = np.r_[0:4, 4094:4098, cfg.N - 4:cfg.N]
+    _compare(W_bits, X_bits, 128, "asym", "prefill", rows=rows)

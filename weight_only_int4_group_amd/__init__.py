@@ -16,6 +16,7 @@ __all__ = [
     "matmul_into", "dequantize", "dequantize_into", "quantize_rtn_scaled", "quantize_rtn_scaled_into",
     "scale_columns", "scale_columns_into", "awq_workspace_bytes", "awq_search", "awq_search_into",
     "quantize_rtn8", "quantize_rtn8_into", "matmul_w8", "matmul_w8_into", "select_kernel_w8",
+    "gptq_workspace_bytes", "gptq", "gptq_into",
     "select_kernel", "status_string", "version", "MODES", "KERNELS", "SCALE_OPS",
 ]
 
@@ -72,6 +73,10 @@ def library() -> ctypes.CDLL:
             lib.q4_matmul_w8.restype = ctypes.c_int
             lib.q4_select_kernel_w8.argtypes = [i64, i64, i64, i32]
             lib.q4_select_kernel_w8.restype = ctypes.c_int
+            lib.q4_gptq_workspace_bytes.argtypes = [i64, i64, i64, i32]
+            lib.q4_gptq_workspace_bytes.restype = ctypes.c_int64
+            lib.q4_gptq.argtypes = [vp, i64, vp, i64, i64, i32, i32, ctypes.c_float, vp, i64, vp, vp, vp, vp, vp]
+            lib.q4_gptq.restype = ctypes.c_int
             lib.q4_status_string.argtypes = [ctypes.c_int]
             lib.q4_status_string.restype = ctypes.c_char_p
             lib.q4_version.argtypes = []
@@ -370,3 +375,43 @@ def matmul_w8(X, codes, scales, zeros, g: int = 128, mode: str = "sym", kernel: 
     Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.bfloat16, device=codes.device)
     matmul_w8_into(X, codes, scales, zeros, g, mode, Y, kernel)
     return Y
+
+
+def gptq_workspace_bytes(M: int, N: int, K: int, g: int) -> int:
+    st = int(library().q4_gptq_workspace_bytes(M, N, K, g))
+    if st < 0:
+        raise Q4Error(st, "q4_gptq_workspace_bytes")
+    return st
+
+
+def gptq_into(X, W, g: int, mode: str, damp: float, workspace, packed, scales, zeros, info) -> None:
+    """q4_gptq on caller-provided workspace and outputs (no allocation)."""
+    import torch
+    _check_cuda(X, W, workspace, packed, scales, zeros, info)
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D bfloat16 tensors")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}")
+    with torch.cuda.device(W.device):
+        st = library().q4_gptq(_ptr(X), M, _ptr(W), N, K, g, _mode(mode), float(damp), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(packed), _ptr(scales),
+                               _ptr(zeros), _ptr(info), _stream(W.device))
+    if st != 0:
+        raise Q4Error(st, "q4_gptq")
+
+
+def gptq(X, W, g: int = 128, mode: str = "asym", damp: float = 0.01):
+    """GPTQ of W[N, K] on calibration rows X[M, K] (bf16) -> (packed, scales, zeros, info)."""
+    import torch
+    M, K = X.shape
+    N = W.shape[0]
+    G = K // g if g > 0 else 0
+    ws = torch.empty(gptq_workspace_bytes(M, N, K, g), dtype=torch.uint8, device=W.device)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    info = torch.empty(1, dtype=torch.int32, device=W.device)
+    gptq_into(X, W, g, mode, damp, ws, packed, scales, zeros, info)
+    return packed, scales, zeros, info

@@ -35,6 +35,8 @@ SOURCES = {
     "decode.hip": [],
     "dequant.hip": [],
     "gemv8.hip": [],
+    # the codes' IEEE quotient must not be contracted or re-associated
+    "gptq.hip": ["-fno-fast-math"],
     # the activation scaling's IEEE division and product must not be contracted or re-associated
     "awq.hip": ["-ffp-contract=off", "-fno-fast-math"],
     "q4_abi.cpp": [],

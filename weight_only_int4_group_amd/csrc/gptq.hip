@@ -1,0 +1,353 @@
+// GPTQ quantization on the GPU (gfx950), in the library's INT4 group format.
+//
+// Method ("LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
+// "GPTQ vs AWQ: two ways to choose what error to keep"; overview page §2.1; "DL S067 ·
+// Quantization" §4 "GPTQ intuition"): H = X^T X over calibration rows, dampened on the
+// diagonal by damp * mean(diag H); the columns of each weight row are quantized in order and
+// each column's rounding error is pushed onto the columns not yet quantized through the
+// inverse Hessian.  As in the pages' toy, every group's scale and zero-point are fixed up
+// front (RTN's, from the original weights), so GPTQ chooses codes only.
+//
+// Formulation.  With H = Ut Ut^T, Ut upper triangular (the Cholesky factorisation of H taken
+// from the last column backwards), the sequential update is equivalent to error feedback from
+// the ORIGINAL weights:
+//     w'_i = w_i + sum_{j<i} (w_j - x_hat_j) Ut[j, i] / Ut[i, i],   q_i = code(w'_i),
+// because the pages' update coefficient [H_i^-1]_{i, j} / [H_i^-1]_{i, i} (H_i^-1 the inverse
+// downdated to columns >= i) equals the corresponding entry of Ut^-1 divided by its diagonal,
+// and W - X_hat = E Ut^-1 for the scaled errors E.  No inverse is formed: one Cholesky
+// factorisation and one sweep.  Ut is obtained as the ordinary lower Cholesky factor L of the
+// index-reversed Hessian R = J H J (R[a][b] = H[K-1-a][K-1-b]): Ut[i][j] = L[K-1-i][K-1-j].
+//
+// Kernels (all fp32, fixed summation order, no atomics):
+//   * gemm_f32_kernel: C = alpha A B + beta C on 64 x 64 tiles with arbitrary (signed) strides;
+//     it forms R from X with the columns read in reverse, the Cholesky's trailing updates
+//     (lower tiles only) and the sweep's block updates;
+//   * damp_kernel: one block; mean of the diagonal in a fixed order, then the dampening;
+//   * potf2_kernel / trsm_kernel: the 32 x 32 diagonal block and the panel below it;
+//   * colscale_kernel: L[a][b] / L[b][b] below the diagonal (the update coefficients);
+//   * sweep_block_kernel: one thread per weight row runs the 32 columns of a block in order
+//     (error feedback inside the block from LDS, earlier blocks through the accumulated
+//     updates), writes the 16 packed bytes and the block's residuals w_j - x_hat_j.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kTile = 64;          // GEMM output tile
+constexpr int kStep = 16;          // GEMM inner step
+constexpr int kB = 32;             // Cholesky block and sweep block (K % 32 == 0)
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_f32<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);       // bf16 -> fp32, exact
+}
+
+// C[m * ldc + n] = alpha * sum_k A(m, k) B(k, n) + beta * C, A(m, k) = A[m sam + k sak],
+// B(k, n) = B[k sbk + n sbn].  tri: only tiles with tile row >= tile column (lower part).
+// beta == 0 writes C without reading it.
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A, int64_t sam, int64_t sak,
+                                                       const TB* __restrict__ B, int64_t sbk, int64_t sbn,
+                                                       float* __restrict__ C, int64_t ldc, int M, int N, int Kd,
+                                                       float alpha, float beta, int tri) {
+  const int bm = blockIdx.y, bn = blockIdx.x;
+  if (tri && bn > bm) return;
+  __shared__ float As[kStep][kTile + 4];
+  __shared__ float Bs[kStep][kTile + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = bm * kTile, n0 = bn * kTile;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < Kd; k0 += kStep) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e;                 // 1024 = 64 x 16 elements of each operand
+      const int am = idx >> 4, ak = idx & 15;        // A: row-major over (m, k)
+      const int m = m0 + am, k = k0 + ak;
+      As[ak][am] = (m < M && k < Kd) ? ld_f32(A, (int64_t)m * sam + (int64_t)k * sak) : 0.0f;
+      const int bk = idx >> 6, bnn = idx & 63;       // B: row-major over (k, n)
+      const int kk = k0 + bk, n = n0 + bnn;
+      Bs[bk][bnn] = (kk < Kd && n < N) ? ld_f32(B, (int64_t)kk * sbk + (int64_t)n * sbn) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kStep; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty * 4 + i];
+        b[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float* c = C + (int64_t)m * ldc + n;
+      *c = beta == 0.0f ? alpha * acc[i][j] : __builtin_fmaf(alpha, acc[i][j], beta * *c);
+    }
+  }
+}
+
+__global__ void zero_info_kernel(int* __restrict__ info) {
+  if (threadIdx.x == 0) info[0] = 0;
+}
+
+// Dampening: mean of diag(R) summed in a fixed order (per-thread strided partials, then a
+// fixed tree), R[a][a] += damp * mean; an all-zero R (no calibration information) becomes I.
+__global__ __launch_bounds__(1024) void damp_kernel(float* __restrict__ R, int K, float damp) {
+  __shared__ float part[1024];
+  float s = 0.0f;
+  for (int a = threadIdx.x; a < K; a += 1024) s += R[(int64_t)a * K + a];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float mean = part[0] / (float)K;
+  for (int a = threadIdx.x; a < K; a += 1024) {
+    float* d = R + (int64_t)a * K + a;
+    *d = mean == 0.0f ? 1.0f : *d + damp * mean;
+  }
+}
+
+// Unblocked Cholesky of the 32 x 32 diagonal block at (k0, k0), lower part, one wave.  A
+// non-positive pivot records info = column + 1 (first failure only) and is replaced by
+// 1e-30 so the factorisation completes.
+__global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ R, int K, int k0, int* __restrict__ info) {
+  __shared__ float a[kB][kB + 1];
+  const int t = threadIdx.x;
+  for (int e = t; e < kB * kB; e += 64) {
+    const int i = e / kB, j = e % kB;
+    a[i][j] = j <= i ? R[(int64_t)(k0 + i) * K + k0 + j] : 0.0f;
+  }
+  __syncthreads();
+  for (int j = 0; j < kB; ++j) {
+    float d = a[j][j];
+    if (!(d > 0.0f)) {
+      if (t == 0 && info[0] == 0) info[0] = k0 + j + 1;
+      d = 1e-30f;
+    }
+    d = sqrtf(d);
+    __syncthreads();
+    if (t == 0) a[j][j] = d;
+    if (t > j && t < kB) a[t][j] /= d;
+    __syncthreads();
+    // trailing update inside the block: a[i][k] -= a[i][j] a[k][j], j < k <= i
+    for (int e = t; e < kB * kB; e += 64) {
+      const int i = e / kB, k = e % kB;
+      if (k > j && k <= i) a[i][k] -= a[i][j] * a[k][j];
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < kB * kB; e += 64) {
+    const int i = e / kB, j = e % kB;
+    if (j <= i) R[(int64_t)(k0 + i) * K + k0 + j] = a[i][j];
+  }
+}
+
+// Panel: rows r >= k0 + 32, L[r, k0:k0+32] = R[r, k0:k0+32] L_kk^-T (forward substitution with
+// the factored diagonal block), one thread per row.
+__global__ __launch_bounds__(256) void trsm_kernel(float* __restrict__ R, int K, int k0) {
+  __shared__ float l[kB][kB + 1];
+  for (int e = threadIdx.x; e < kB * kB; e += 256) {
+    const int i = e / kB, j = e % kB;
+    l[i][j] = j <= i ? R[(int64_t)(k0 + i) * K + k0 + j] : 0.0f;
+  }
+  __syncthreads();
+  const int64_t r = (int64_t)k0 + kB + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= K) return;
+  float* row = R + r * K + k0;
+  float x[kB];
+#pragma unroll
+  for (int j = 0; j < kB; ++j) {
+    float v = row[j];
+#pragma unroll
+    for (int t = 0; t < j; ++t) v = __builtin_fmaf(-x[t], l[j][t], v);
+    x[j] = v / l[j][j];
+  }
+#pragma unroll
+  for (int j = 0; j < kB; ++j) row[j] = x[j];
+}
+
+// L[a][b] / L[b][b] for a > b: the error-feedback coefficients (in reversed indices).
+__global__ __launch_bounds__(256) void colscale_kernel(float* __restrict__ R, int K) {
+  const int64_t a = blockIdx.y;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < a; b += (int64_t)gridDim.x * 256)
+    R[a * K + b] /= R[b * K + b];
+}
+
+// One block of 32 columns [i1, i1 + 32) for every weight row (one thread per row).  The block
+// lies inside one group.  Cb[j][i] = Ut[i1 + j][i1 + i] / Ut[i1 + i][i1 + i] for j < i.
+// acc holds the feedback of the earlier blocks (none when i1 == 0).  Writes the 16 packed
+// bytes of the block and the residuals w_j - x_hat_j (fp32) to D[n][0..31].
+template <bool SYM>
+__global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __restrict__ W, int64_t N, int K, int g,
+                                                          const float* __restrict__ Lc, const float* __restrict__ acc,
+                                                          int i1, const uint16_t* __restrict__ scales,
+                                                          const uint8_t* __restrict__ zeros,
+                                                          uint8_t* __restrict__ packed, float* __restrict__ D) {
+  __shared__ float Cb[kB][kB + 1];
+  for (int e = threadIdx.x; e < kB * kB; e += 256) {
+    const int j = e / kB, i = e % kB;
+    Cb[j][i] = j < i ? Lc[(int64_t)(K - 1 - i1 - j) * K + (K - 1 - i1 - i)] : 0.0f;
+  }
+  __syncthreads();
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int G = K / g;
+  const int grp = i1 / g;
+  const float s = (float)__builtin_bit_cast(_Float16, scales[n * G + grp]);
+  const float zf = SYM ? 0.0f : (float)zeros[n * G + grp];
+  constexpr float qlo = SYM ? -8.0f : 0.0f, qhi = SYM ? 7.0f : 15.0f;
+
+  const u32x4* wp = reinterpret_cast<const u32x4*>(W + n * (int64_t)K + i1);
+  float w[kB], f[kB], d[kB];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u32x4 p = wp[v];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      w[8 * v + 2 * t] = bf16_lo(p[t]);
+      w[8 * v + 2 * t + 1] = bf16_hi(p[t]);
+    }
+  }
+  if (i1 > 0) {
+    const float4* ap = reinterpret_cast<const float4*>(acc + n * (int64_t)K + i1);
+#pragma unroll
+    for (int v = 0; v < kB / 4; ++v) {
+      const float4 a4 = ap[v];
+      f[4 * v] = a4.x;
+      f[4 * v + 1] = a4.y;
+      f[4 * v + 2] = a4.z;
+      f[4 * v + 3] = a4.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kB; ++i) f[i] = 0.0f;
+  }
+  uint32_t nib[kB / 8] = {};
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    float v = w[i] + f[i];
+#pragma unroll
+    for (int j = 0; j < i; ++j) v = __builtin_fmaf(d[j], Cb[j][i], v);
+    const float c = fminf(fmaxf(rintf(v / s) + zf, qlo), qhi);       // IEEE quotient, as RTN
+    d[i] = w[i] - s * (c - zf);
+    nib[i / 8] |= ((uint32_t)(int)c & 0xFu) << (4 * (i % 8));
+  }
+  *reinterpret_cast<u32x4*>(packed + n * (int64_t)(K / 2) + i1 / 2) = u32x4{nib[0], nib[1], nib[2], nib[3]};
+  float4* dp = reinterpret_cast<float4*>(D + n * kB);
+#pragma unroll
+  for (int v = 0; v < kB / 4; ++v) dp[v] = float4{d[4 * v], d[4 * v + 1], d[4 * v + 2], d[4 * v + 3]};
+}
+
+template <typename TA, typename TB>
+hipError_t gemm(const TA* A, int64_t sam, int64_t sak, const TB* B, int64_t sbk, int64_t sbn, float* C,
+                int64_t ldc, int M, int N, int Kd, float alpha, float beta, bool tri, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((M + kTile - 1) / kTile));
+  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, C, ldc, M, N, Kd,
+                     alpha, beta, tri ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+GptqLayout gptq_layout(int64_t N, int64_t K) {
+  GptqLayout L;
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  L.R = 0;
+  L.acc = up(L.R + 4 * K * K);
+  L.D = up(L.acc + 4 * N * K);
+  L.bytes = up(L.D + 4 * N * kB);
+  return L;
+}
+
+hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64_t K, int g, bool sym, float damp,
+                       void* workspace, void* packed, void* scales, void* zeros, int* info, int num_cus,
+                       hipStream_t stream) {
+  const GptqLayout L = gptq_layout(N, K);
+  char* base = static_cast<char*>(workspace);
+  float* R = reinterpret_cast<float*>(base + L.R);
+  float* acc = reinterpret_cast<float*>(base + L.acc);
+  float* D = reinterpret_cast<float*>(base + L.D);
+  const int Ki = (int)K;
+  const uint16_t* Xh = static_cast<const uint16_t*>(X);
+
+  // 1. group parameters fixed up front: RTN of the original weights (its codes are replaced)
+  hipError_t e = launch_quantize(W, N, K, g, sym, packed, scales, zeros, num_cus, stream);
+  if (e != hipSuccess) return e;
+  // 2. R = J X^T X J (columns of X read backwards), lower tiles; then the dampening
+  hipLaunchKernelGGL(zero_info_kernel, dim3(1), dim3(64), 0, stream, info);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // R[a][b] = sum_t X[t][K-1-a] X[t][K-1-b]: A(a, t) and B(t, b) read the bf16 rows backwards
+  const uint16_t* Xr = Xh + (K - 1);
+  e = gemm<uint16_t, uint16_t>(Xr, -1, K, Xr, K, -1, R, K, Ki, Ki, (int)M, 1.0f, 0.0f, true, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, R, Ki, damp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 3. blocked lower Cholesky of R, in place
+  for (int k0 = 0; k0 < Ki; k0 += kB) {
+    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, stream, R, Ki, k0, info);
+    const int rest = Ki - k0 - kB;
+    if (rest > 0) {
+      hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0, stream, R, Ki, k0);
+      float* P = R + (int64_t)(k0 + kB) * K + k0;           // the panel, rest x 32
+      e = gemm<float, float>(P, K, 1, P, 1, K, R + (int64_t)(k0 + kB) * K + (k0 + kB), K, rest, rest, kB, -1.0f, 1.0f,
+                      true, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(colscale_kernel, dim3((unsigned)((K + 255) / 256 < 64 ? (K + 255) / 256 : 64), (unsigned)K),
+                     dim3(256), 0, stream, R, Ki);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 4. the sweep, 32 columns at a time
+  const unsigned rows_grid = (unsigned)((N + 255) / 256);
+  for (int i1 = 0; i1 < Ki; i1 += kB) {
+    if (sym)
+      hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1, static_cast<const uint16_t*>(scales),
+                         static_cast<const uint8_t*>(zeros), static_cast<uint8_t*>(packed), D);
+    else
+      hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1, static_cast<const uint16_t*>(scales),
+                         static_cast<const uint8_t*>(zeros), static_cast<uint8_t*>(packed), D);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int i2 = i1 + kB;
+    if (i2 < Ki) {
+      // acc[:, i2:] (+)= D[:, 0:32] C[i1:i2, i2:], C[j][i] = Lc[K-1-j][K-1-i]
+      const float* Bc = R + (int64_t)(Ki - 1 - i1) * K + (Ki - 1 - i2);
+      e = gemm<float, float>(D, kB, 1, Bc, -K, -1, acc + i2, K, (int)N, Ki - i2, kB, 1.0f, i1 == 0 ? 0.0f : 1.0f, false,
+                      stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace q4

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <initializer_list>
 
@@ -130,7 +131,8 @@ const char* q4_status_string(int status) {
     case Q4_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case Q4_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case Q4_ERR_UNSUPPORTED: return "the chosen kernel does not support this shape";
-    case Q4_ERR_WORKSPACE: return "workspace smaller than q4_awq_workspace_bytes() requires";
+    case Q4_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() requires";
+    case Q4_ERR_VALUE: return "a numeric parameter is out of range (e.g. GPTQ damping not finite and >= 0)";
     default: return "unknown status";
   }
 }
@@ -313,6 +315,37 @@ int q4_matmul_w8(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int3
   if (kernel == Q4_KERNEL_GEMV)
     return finish(q4::launch_gemv8(X, (int)M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm8(X, M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
+}
+
+int64_t q4_gptq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t g) {
+  int st = check_shape(N, K, g, Q4_ASYM);
+  if (st != Q4_OK) return st;
+  if (M < 1 || M > kMaxDim || K > q4::kGptqMaxK) return Q4_ERR_SHAPE;
+  return q4::gptq_layout(N, K).bytes;
+}
+
+int q4_gptq(const void* X, int64_t M, const void* W, int64_t N, int64_t K, int32_t g, int32_t mode, float damp,
+            void* workspace, int64_t workspace_bytes, void* packed, void* scales, void* zeros, void* info,
+            void* stream) {
+  int st = check_shape(N, K, g, mode);
+  if (st != Q4_OK) return st;
+  if (M < 1 || M > kMaxDim || K > q4::kGptqMaxK) return Q4_ERR_SHAPE;
+  if (!std::isfinite(damp) || damp < 0.0f) return Q4_ERR_VALUE;
+  if (!X || !W || !workspace || !packed || !scales || !zeros || !info) return Q4_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) ||
+      !aligned(workspace, 256) || !aligned(info, 4))
+    return Q4_ERR_ALIGN;
+  const q4::GptqLayout L = q4::gptq_layout(N, K);
+  if (workspace_bytes < L.bytes) return Q4_ERR_WORKSPACE;
+  const int64_t G = K / g;
+  const Range x = range_of(X, M * K * 2), w = range_of(W, N * K * 2), ws = range_of(workspace, L.bytes),
+              p = range_of(packed, N * K / 2), s = range_of(scales, N * G * 2), z = range_of(zeros, N * G),
+              in = range_of(info, 4);
+  for (const Range& o : {ws, p, s, z, in})
+    if (overlap(o, x) || overlap(o, w)) return Q4_ERR_ALIAS;
+  if (any_overlap({ws, p, s, z, in})) return Q4_ERR_ALIAS;
+  return finish(q4::launch_gptq(X, M, W, N, K, g, mode == Q4_SYM, damp, workspace, packed, scales, zeros,
+                                static_cast<int*>(info), num_cus(), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

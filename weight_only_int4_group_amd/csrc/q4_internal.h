@@ -39,6 +39,17 @@ hipError_t launch_awq_select(const void* err, int n_alpha, const void* s_all, in
 // W8A16: 8-bit group-wise RTN (codes uint8 [N, K], one byte per code) and its matmul.
 hipError_t launch_quantize8(const void* W, int64_t N, int64_t K, int g, bool sym, void* codes,
                             void* scales, void* zeros, int num_cus, hipStream_t stream);
+// GPTQ (group parameters fixed up front, Cholesky of the reversed Hessian, blocked
+// error-feedback sweep).  Workspace layout: R [K, K] fp32, accumulated feedback [N, K] fp32,
+// block residuals [N, 32] fp32, each 256-byte aligned.
+constexpr int64_t kGptqMaxK = 32768;
+struct GptqLayout {
+  int64_t R, acc, D, bytes;
+};
+GptqLayout gptq_layout(int64_t N, int64_t K);
+hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64_t K, int g, bool sym, float damp,
+                       void* workspace, void* packed, void* scales, void* zeros, int* info, int num_cus,
+                       hipStream_t stream);
 // GEMV for M <= kGemv8MaxM with X staged in LDS as scaled fp16 (gemv8_fits: 2.25 M K bytes fit).
 constexpr int64_t kGemv8MaxM = 4;
 bool gemv8_fits(int64_t M, int64_t K);
