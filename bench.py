@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; GEMM TFLOP/s at M=2048"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_70b_mlp_m1_traffic.md")
 GEMV_SRC = os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", "gemv.hip")
 
@@ -93,6 +94,8 @@ def parse_args(argv=None):
                    help="skip the practical-ceiling measurements reported as context")
     p.add_argument("--no-awq", action="store_true",
                    help="skip the AWQ-style scaling search measurement")
+    p.add_argument("--no-gptq", action="store_true",
+                   help="skip the GPTQ measurement")
     p.add_argument("--no-w8", action="store_true",
                    help="skip the W8A16 (8-bit codes) measurements")
     p.add_argument("--copy-calibration", action="store_true",
@@ -371,6 +374,52 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
             "ms": round(ms, 5), "bytes_per_launch": by,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def measure_gptq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, reps=3, with_oracle=True,
+                 oracle_rows=32):
+    """GPTQ of the prefill layer W[8192, 8192] (asym, g=128) on `calib` calibration rows of its
+    activations: q4_gptq timed with HIP events on the launch stream.  Algorithmic flops:
+    M K^2 for H = X^T X (its lower half), K^3 / 3 for the Cholesky factorisation and N K^2 for
+    the error-feedback sweep (sum over columns of 2 N i).  The oracle's gptq_ref is timed beside
+    it on a bounded sample (`oracle_rows` rows of W; its Hessian factorisation is full size)."""
+    import numpy as np
+    dev = W5.device
+    N, K = W5.shape
+    G = K // g
+    Xc = X5[:calib].contiguous()
+    ws = torch.empty(q4.gptq_workspace_bytes(calib, N, K, g), dtype=torch.uint8, device=dev)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, G), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    run = lambda: q4.gptq_into(Xc, W5, g, "asym", 0.01, ws, packed, scales, zeros, info)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = calib * K * K + K ** 3 / 3 + N * K * K
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": f"GPTQ of W[{N},{K}] asym g={g} on {calib} calibration rows (damp 0.01)",
+           "ms": round(ms, 3), "info": int(info.cpu().numpy()[0]), "flops": flops,
+           "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4)}}
+    if with_oracle:
+        from oracle import q4_oracle as orc
+        t = time.perf_counter()
+        orc.gptq_ref(W5_bits[:oracle_rows], X5_bits[:calib], g, "asym")
+        spent = time.perf_counter() - t
+        res["cpu_oracle"] = {"kind": "oracle", "seconds": round(spent, 2),
+                             "sample": f"oracle gptq_ref on the first {oracle_rows} rows of W with the full "
+                                       f"{K} x {K} Hessian ({calib} calibration rows)",
+                             "rows_per_s": round(oracle_rows / spent, 2),
+                             "gpu_rows_per_s": round(N / (ms * 1e-3), 1)}
+    return res
 
 
 # --------------------------------------------------------------------------- counters
@@ -736,6 +785,9 @@ def main(argv=None):
         out["w8a16"] = measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5,
                                   with_oracle=not args.no_cpu_baseline)
         note("W8A16 measured")
+    if not args.no_gptq:
+        out["gptq"] = measure_gptq(torch, q4, W5, X5, W5_bits, X5_bits, with_oracle=not args.no_cpu_baseline)
+        note("GPTQ measured")
     if not args.no_awq:
         out["awq"] = measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, with_oracle=not args.no_cpu_baseline)
         note("AWQ search measured")
