@@ -40,7 +40,8 @@ namespace {
 
 constexpr int kTile = 64;          // GEMM output tile
 constexpr int kStep = 16;          // GEMM inner step
-constexpr int kB = 32;             // Cholesky block and sweep block (K % 32 == 0)
+constexpr int kB = 32;             // Cholesky panel and sweep step (K % 32 == 0)
+constexpr int kOuter = 128;        // columns per outer block: the width of the big updates
 
 template <typename T>
 __device__ __forceinline__ float ld_f32(const T* p, int64_t i);
@@ -52,8 +53,9 @@ __device__ __forceinline__ float ld_f32<uint16_t>(const uint16_t* p, int64_t i) 
 }
 
 // C[m * ldc + n] = alpha * sum_k A(m, k) B(k, n) + beta * C, A(m, k) = A[m sam + k sak],
-// B(k, n) = B[k sbk + n sbn].  tri: only tiles with tile row >= tile column (lower part).
-// beta == 0 writes C without reading it.
+// B(k, n) = B[k sbk + n sbn], on the fp32 matrix cores (each product exact, fp32 sums).
+// tri: only tiles with tile row >= tile column (lower part).  beta == 0 writes C without
+// reading it.
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A, int64_t sam, int64_t sak,
                                                        const TB* __restrict__ B, int64_t sbk, int64_t sbn,
@@ -64,9 +66,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
   __shared__ float As[kStep][kTile + 4];
   __shared__ float Bs[kStep][kTile + 4];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;      // the wave's 32 x 32 quarter
   const int m0 = bm * kTile, n0 = bn * kTile;
-  float acc[4][4] = {};
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < Kd; k0 += kStep) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -79,33 +86,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
       Bs[bk][bnn] = (kk < Kd && n < N) ? ld_f32(B, (int64_t)kk * sbk + (int64_t)n * sbn) : 0.0f;
     }
     __syncthreads();
+    // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of a
+    // 16 x 4 by 4 x 16 step; the 16 x 16 result sits in lane l as rows 4 (l / 16) + r, column l % 16
 #pragma unroll
-    for (int kk = 0; kk < kStep; ++kk) {
-      float a[4], b[4];
+    for (int k4 = 0; k4 < kStep; k4 += 4) {
+      const int kr = k4 + (lane >> 4);
+      float a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = As[kk][ty * 4 + i];
-        b[i] = Bs[kk][tx * 4 + i];
+      for (int i = 0; i < 2; ++i) {
+        a[i] = As[kr][wm + 16 * i + (lane & 15)];
+        b[i] = Bs[kr][wn + 16 * i + (lane & 15)];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    if (m >= M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n >= N) continue;
-      float* c = C + (int64_t)m * ldc + n;
-      *c = beta == 0.0f ? alpha * acc[i][j] : __builtin_fmaf(alpha, acc[i][j], beta * *c);
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+        if (m >= M || n >= N) continue;
+        float* c = C + (int64_t)m * ldc + n;
+        *c = beta == 0.0f ? alpha * acc[i][j][r] : __builtin_fmaf(alpha, acc[i][j][r], beta * *c);
+      }
     }
-  }
 }
 
 __global__ void zero_info_kernel(int* __restrict__ info) {
@@ -131,38 +142,38 @@ __global__ __launch_bounds__(1024) void damp_kernel(float* __restrict__ R, int K
   }
 }
 
-// Unblocked Cholesky of the 32 x 32 diagonal block at (k0, k0), lower part, one wave.  A
-// non-positive pivot records info = column + 1 (first failure only) and is replaced by
-// 1e-30 so the factorisation completes.
+// Unblocked Cholesky of the 32 x 32 diagonal block at (k0, k0), lower part, one wave: lane i
+// holds row i in registers; the column loop is unrolled, so every pivot and every l_kj is a
+// lane read with a constant index.  A non-positive pivot records info = column + 1 (first
+// failure only) and is replaced by 1e-30 so the factorisation completes.
 __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ R, int K, int k0, int* __restrict__ info) {
-  __shared__ float a[kB][kB + 1];
-  const int t = threadIdx.x;
-  for (int e = t; e < kB * kB; e += 64) {
-    const int i = e / kB, j = e % kB;
-    a[i][j] = j <= i ? R[(int64_t)(k0 + i) * K + k0 + j] : 0.0f;
-  }
-  __syncthreads();
+  const int i = threadIdx.x & 31;
+  const bool own = threadIdx.x < kB;
+  float* row = R + (int64_t)(k0 + i) * K + k0;
+  float a[kB];
+#pragma unroll
+  for (int j = 0; j < kB; ++j) a[j] = (own && j <= i) ? row[j] : 0.0f;
+  int bad = 0;
+#pragma unroll
   for (int j = 0; j < kB; ++j) {
-    float d = a[j][j];
+    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
     if (!(d > 0.0f)) {
-      if (t == 0 && info[0] == 0) info[0] = k0 + j + 1;
+      if (bad == 0) bad = j + 1;
       d = 1e-30f;
     }
     d = sqrtf(d);
-    __syncthreads();
-    if (t == 0) a[j][j] = d;
-    if (t > j && t < kB) a[t][j] /= d;
-    __syncthreads();
-    // trailing update inside the block: a[i][k] -= a[i][j] a[k][j], j < k <= i
-    for (int e = t; e < kB * kB; e += 64) {
-      const int i = e / kB, k = e % kB;
-      if (k > j && k <= i) a[i][k] -= a[i][j] * a[k][j];
+    a[j] = i == j ? d : (i > j ? a[j] / d : a[j]);
+#pragma unroll
+    for (int k = j + 1; k < kB; ++k) {
+      const float lkj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), k));
+      if (i >= k) a[k] = __builtin_fmaf(-a[j], lkj, a[k]);
     }
-    __syncthreads();
   }
-  for (int e = t; e < kB * kB; e += 64) {
-    const int i = e / kB, j = e % kB;
-    if (j <= i) R[(int64_t)(k0 + i) * K + k0 + j] = a[i][j];
+  if (bad != 0 && threadIdx.x == 0 && info[0] == 0) info[0] = k0 + bad;
+  if (own) {
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (j <= i) row[j] = a[j];
   }
 }
 
@@ -197,16 +208,17 @@ __global__ __launch_bounds__(256) void colscale_kernel(float* __restrict__ R, in
     R[a * K + b] /= R[b * K + b];
 }
 
-// One block of 32 columns [i1, i1 + 32) for every weight row (one thread per row).  The block
+// One step of 32 columns [i1, i1 + 32) for every weight row (one thread per row).  The step
 // lies inside one group.  Cb[j][i] = Ut[i1 + j][i1 + i] / Ut[i1 + i][i1 + i] for j < i.
-// acc holds the feedback of the earlier blocks (none when i1 == 0).  Writes the 16 packed
-// bytes of the block and the residuals w_j - x_hat_j (fp32) to D[n][0..31].
+// acc holds the feedback of the earlier columns (none when i1 == 0).  Writes the 16 packed
+// bytes of the step and the residuals w_j - x_hat_j (fp32) to D[n * dld + doff + 0..31].
 template <bool SYM>
 __global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __restrict__ W, int64_t N, int K, int g,
                                                           const float* __restrict__ Lc, const float* __restrict__ acc,
                                                           int i1, const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
-                                                          uint8_t* __restrict__ packed, float* __restrict__ D) {
+                                                          uint8_t* __restrict__ packed, float* __restrict__ D,
+                                                          int dld, int doff) {
   __shared__ float Cb[kB][kB + 1];
   for (int e = threadIdx.x; e < kB * kB; e += 256) {
     const int j = e / kB, i = e % kB;
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __rest
     nib[i / 8] |= ((uint32_t)(int)c & 0xFu) << (4 * (i % 8));
   }
   *reinterpret_cast<u32x4*>(packed + n * (int64_t)(K / 2) + i1 / 2) = u32x4{nib[0], nib[1], nib[2], nib[3]};
-  float4* dp = reinterpret_cast<float4*>(D + n * kB);
+  float4* dp = reinterpret_cast<float4*>(D + n * dld + doff);
 #pragma unroll
   for (int v = 0; v < kB / 4; ++v) dp[v] = float4{d[4 * v], d[4 * v + 1], d[4 * v + 2], d[4 * v + 3]};
 }
@@ -280,7 +292,7 @@ GptqLayout gptq_layout(int64_t N, int64_t K) {
   L.R = 0;
   L.acc = up(L.R + 4 * K * K);
   L.D = up(L.acc + 4 * N * K);
-  L.bytes = up(L.D + 4 * N * kB);
+  L.bytes = up(L.D + 4 * N * kOuter);
   return L;
 }
 
@@ -309,15 +321,29 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, R, Ki, damp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 3. blocked lower Cholesky of R, in place
-  for (int k0 = 0; k0 < Ki; k0 += kB) {
-    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, stream, R, Ki, k0, info);
-    const int rest = Ki - k0 - kB;
-    if (rest > 0) {
+  // 3. blocked lower Cholesky of R, in place.  Outer blocks of 128 columns [o1, o2): 32-column
+  //    panels (diagonal block, the rows below, the update of the outer block's remaining
+  //    columns), then one update of the trailing matrix with inner dimension o2 - o1.
+  for (int o1 = 0; o1 < Ki; o1 += kOuter) {
+    const int o2 = o1 + kOuter < Ki ? o1 + kOuter : Ki;
+    for (int k0 = o1; k0 < o2; k0 += kB) {
+      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, stream, R, Ki, k0, info);
+      const int rest = Ki - k0 - kB;
+      if (rest <= 0) continue;
       hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0, stream, R, Ki, k0);
-      float* P = R + (int64_t)(k0 + kB) * K + k0;           // the panel, rest x 32
-      e = gemm<float, float>(P, K, 1, P, 1, K, R + (int64_t)(k0 + kB) * K + (k0 + kB), K, rest, rest, kB, -1.0f, 1.0f,
-                      true, stream);
+      const int cols = o2 - k0 - kB;                       // the outer block's columns still to factor
+      if (cols > 0) {
+        float* P = R + (int64_t)(k0 + kB) * K + k0;        // the panel, rest x 32
+        e = gemm<float, float>(P, K, 1, P, 1, K, R + (int64_t)(k0 + kB) * K + (k0 + kB), K, rest, cols, kB, -1.0f,
+                               1.0f, false, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    const int rest = Ki - o2;
+    if (rest > 0) {
+      float* P = R + (int64_t)o2 * K + o1;                 // rest x (o2 - o1)
+      e = gemm<float, float>(P, K, 1, P, 1, K, R + (int64_t)o2 * K + o2, K, rest, rest, o2 - o1, -1.0f, 1.0f, true,
+                             stream);
       if (e != hipSuccess) return e;
     }
   }
@@ -325,25 +351,38 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
                      dim3(256), 0, stream, R, Ki);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 4. the sweep, 32 columns at a time
+  // 4. the sweep: outer blocks of 128 columns [s1, s2), 32 columns per step.  After a step its
+  //    residuals feed the outer block's later columns (a small update); after the outer block
+  //    its residuals feed every later column (one update with inner dimension s2 - s1).
+  //    acc[:, i] = sum over earlier columns j of D_j C[j][i], C[j][i] = Lc[K-1-j][K-1-i]; the
+  //    first update to reach a column writes it (beta = 0), later ones add.
   const unsigned rows_grid = (unsigned)((N + 255) / 256);
-  for (int i1 = 0; i1 < Ki; i1 += kB) {
-    if (sym)
-      hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(256), 0, stream,
-                         static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1, static_cast<const uint16_t*>(scales),
-                         static_cast<const uint8_t*>(zeros), static_cast<uint8_t*>(packed), D);
-    else
-      hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(256), 0, stream,
-                         static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1, static_cast<const uint16_t*>(scales),
-                         static_cast<const uint8_t*>(zeros), static_cast<uint8_t*>(packed), D);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int i2 = i1 + kB;
-    if (i2 < Ki) {
-      // acc[:, i2:] (+)= D[:, 0:32] C[i1:i2, i2:], C[j][i] = Lc[K-1-j][K-1-i]
-      const float* Bc = R + (int64_t)(Ki - 1 - i1) * K + (Ki - 1 - i2);
-      e = gemm<float, float>(D, kB, 1, Bc, -K, -1, acc + i2, K, (int)N, Ki - i2, kB, 1.0f, i1 == 0 ? 0.0f : 1.0f, false,
-                      stream);
+  auto coef = [&](int j0, int i0) { return R + (int64_t)(Ki - 1 - j0) * K + (Ki - 1 - i0); };
+  for (int s1 = 0; s1 < Ki; s1 += kOuter) {
+    const int s2 = s1 + kOuter < Ki ? s1 + kOuter : Ki;
+    for (int i1 = s1; i1 < s2; i1 += kB) {
+      if (sym)
+        hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
+                           static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
+                           static_cast<uint8_t*>(packed), D, kOuter, i1 - s1);
+      else
+        hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
+                           static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
+                           static_cast<uint8_t*>(packed), D, kOuter, i1 - s1);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int i2 = i1 + kB;
+      if (i2 < s2) {
+        e = gemm<float, float>(D + (i1 - s1), kOuter, 1, coef(i1, i2), -K, -1, acc + i2, K, (int)N, s2 - i2, kB, 1.0f,
+                               (s1 == 0 && i1 == 0) ? 0.0f : 1.0f, false, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    if (s2 < Ki) {
+      e = gemm<float, float>(D, kOuter, 1, coef(s1, s2), -K, -1, acc + s2, K, (int)N, Ki - s2, s2 - s1, 1.0f,
+                             s1 == 0 ? 0.0f : 1.0f, false, stream);
       if (e != hipSuccess) return e;
     }
   }

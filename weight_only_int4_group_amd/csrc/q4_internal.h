@@ -41,7 +41,7 @@ hipError_t launch_quantize8(const void* W, int64_t N, int64_t K, int g, bool sym
                             void* scales, void* zeros, int num_cus, hipStream_t stream);
 // GPTQ (group parameters fixed up front, Cholesky of the reversed Hessian, blocked
 // error-feedback sweep).  Workspace layout: R [K, K] fp32, accumulated feedback [N, K] fp32,
-// block residuals [N, 32] fp32, each 256-byte aligned.
+// residuals of an outer block [N, 128] fp32, each 256-byte aligned.
 constexpr int64_t kGptqMaxK = 32768;
 struct GptqLayout {
   int64_t R, acc, D, bytes;
