@@ -6,8 +6,9 @@
   of row blocks compared).
 * q4_matmul_w8 meets |Y - Y_ref| <= 8e-3 * sum_k |x w_hat| + 1e-6 per element for every kernel
   that can run the shape, on codes quantized by the oracle (never by the GPU): ragged shapes,
-  M from 1 to 300, on-grid weights against the exact product, special values, the 70B MLP shape
-  at M = 1, 2, 4 and the prefill shape (sampled outputs).
+  M from 1 to 300 (decode GEMV and the general GEMM), ragged and large-tile shapes with M >= 512
+  (the register-dequantising GEMM), on-grid weights against the exact product, special values,
+  the 70B MLP shape at M = 1, 2, 4 and the prefill shape (sampled outputs).
 """
 import numpy as np
 import pytest
@@ -253,6 +254,30 @@ def test_matmul_w8_prefill():
     W_bits, X_bits = make_layer(cfg)
     quant = orc.quantize8_rtn_ref(W_bits, cfg.g, "asym")
     _check_sampled8(X_bits, quant, cfg.g, "asym", cfg.name, "auto", n_samples=4096)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(512, 64, 128, 128), (513, 300, 256, 32), (640, 256, 384, 128),
+                                     (1000, 520, 512, 64), (700, 1030, 1024, 256), (777, 136, 640, 128)])
+def test_matmul_w8_prefill_ragged(M, N, K, g):
+    """Large-M shapes on the register-dequantising GEMM with 8-bit codes: ragged M and N tiles,
+    odd step counts, every power-of-two g."""
+    rng = np.random.default_rng(M + 3 * N + 7 * K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full8(X_bits, W_bits, g, mode, "prefill-ragged", ("auto", "gemm"))
+
+
+@pytest.mark.parametrize("M,N,K,g", [(589, 22000, 384, 128), (512, 32768, 256, 32), (1024, 16384, 512, 256),
+                                     (600, 21800, 640, 64)])
+def test_matmul_w8_prefill_large_tiles(M, N, K, g):
+    """Shapes with enough 256 x 256 tiles to fill the device, so the 256-row tile runs with
+    8-bit codes: ragged M and N, every g, both modes."""
+    rng = np.random.default_rng(M + N + K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full8(X_bits, W_bits, g, mode, "prefill-large", ("auto",))
 
 
 def test_matmul_w8_m0_nondefault_stream_and_determinism():

@@ -18,6 +18,10 @@
 //   * One barrier per step, after the step's loads have landed.
 // The k order inside a step is permuted identically for both operands (lane group q takes the
 // 32 contiguous k of its codes), which leaves each output sum unchanged.
+// W8A16 ("LLM Weight Quantization ...", "Granularity and outliers") uses the same kernel with
+// 8-bit codes (B = 8): a lane loads its 32 codes per row and step as two 16-byte loads, a code
+// byte placed under the fp16 exponent byte 0x64 reads as 1024 + q (v_perm_b32, two per
+// instruction), and fma(1024 + q, s, -s (1024 + z)) = s (q - z) exactly.
 // MFMA: D[n][m] = sum_k W[n][k] X[m][k]; a lane's four accumulators are four consecutive n of
 // one m, written as one 8-byte store into row-major Y.  Blocks are numbered so that each XCD
 // (one L2) works on a rectangle of tiles that share X and W slices.
@@ -83,6 +87,44 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t dw, float s, float c1, float 
                deq_pair(b, 3, s, c1, c64)};
 }
 
+// 8-bit codes: the eight codes of a sub-step (k0..k7, one byte each) in two dwords.  Pair i of
+// the result is (k 2i, k 2i + 1); as 1024 + q in fp16: q0 = (k0, k1), q1 = (k2, k3) from the first
+// dword, q2, q3 from the second.  Symmetric codes (int8) are offset by 128, z = 128.
+template <bool SYM>
+__device__ __forceinline__ Biased deq_prep_b(uint32_t d0, uint32_t d1) {
+  if (SYM) {
+    d0 ^= 0x80808080u;
+    d1 ^= 0x80808080u;
+  }
+  return Biased{as_f16x2(__builtin_amdgcn_perm(0x64646464u, d0, 0x04010400u)),
+                as_f16x2(__builtin_amdgcn_perm(0x64646464u, d0, 0x04030402u)),
+                as_f16x2(__builtin_amdgcn_perm(0x64646464u, d1, 0x04010400u)),
+                as_f16x2(__builtin_amdgcn_perm(0x64646464u, d1, 0x04030402u))};
+}
+__device__ __forceinline__ void deq_fmas_b(const Biased& b, int i, float s, float c1, float& w0, float& w1) {
+  const f16x2 q = i == 0 ? b.q0 : (i == 1 ? b.q1 : (i == 2 ? b.q2 : b.q3));
+  w0 = __builtin_fmaf((float)q[0], s, c1);
+  w1 = __builtin_fmaf((float)q[1], s, c1);
+}
+// One sub-step's MFMA operand (8 bf16) from the code dwords of either width.
+template <bool SYM, int B>
+__device__ __forceinline__ u32x4 dequant_sub(uint32_t d0, uint32_t d1, float s, float c1, float c64) {
+  if constexpr (B == 8) {
+    const Biased b = deq_prep_b<SYM>(d0, d1);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float w0, w1;
+      deq_fmas_b(b, i, s, c1, w0, w1);
+      r[i] = pack_bf16x2(w0, w1);
+    }
+    return r;
+  } else {
+    (void)d1;
+    return dequant8<SYM>(d0, s, c1, c64);
+  }
+}
+
 // acc += a b on the matrix core with the accumulator tied to its AGPRs, so that a wave's 256
 // accumulators stay in place (the builtin lets the register allocator move them between
 // AGPRs and VGPRs around every MFMA).  The compiler does not look inside the asm, so the
@@ -141,7 +183,8 @@ __device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int,
 //
 // NBW: 16-row blocks of W per wave (4: 256-row W tiles; 2: 128-row tiles, for shapes whose
 // 256-row tiles would leave compute units idle).
-template <int TM, int NBW, bool SYM, bool EDGE>
+// B: code width, 4 (W4A16) or 8 (W8A16).
+template <int TM, int NBW, bool SYM, bool EDGE, int B>
 __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, int lg,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -161,6 +204,9 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   constexpr uint32_t kStageBytes = TM * kRowBytes;     // 32 or 64 KiB
   constexpr uint32_t kWaveDma = kStageBytes / 4;       // bytes each wave copies per step
   constexpr int kDmaOps = kWaveDma / 1024;             // 1 KiB copy instructions per wave
+  static_assert(B == 4 || B == 8, "4- or 8-bit codes");
+  constexpr int CW = B / 4;                            // 16-byte code loads per row and step
+  constexpr uint32_t kZsym = B == 8 ? 128u : 8u;       // symmetric codes are offset by this
 
   // Two X stages, then (full tiles) two stages of the scale and zero-point words of the
   // block's W rows: per stage and wave, 64 rows x 8 bytes of scales and 64 rows x 4 bytes of
@@ -231,7 +277,8 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   // plus a wave-uniform offset for the block and step; edge tiles: a lane offset per block,
   // so that a row past N is out of range on its own.
   const uint32_t rows_left = (uint32_t)min(N - n0, TN);
-  const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + (size_t)n0 * (size_t)(K / 2), rows_left * (uint32_t)(K / 2));
+  const uint32_t wrow = (uint32_t)K * B / 8;           // code bytes per W row
+  const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + (size_t)n0 * (size_t)wrow, rows_left * wrow);
   const __amdgpu_buffer_rsrc_t rs = buffer_over(scales + (size_t)n0 * G, rows_left * (uint32_t)G * 2u);
   const __amdgpu_buffer_rsrc_t rz = buffer_over(zeros + (size_t)n0 * G, rows_left * (uint32_t)G);
   const uint32_t gl = (uint32_t)((32 * lq) >> lg);
@@ -240,7 +287,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const uint32_t r = EDGE ? (uint32_t)(RPW * wave + 16 * v + li) : (uint32_t)li;
-    voff_w[v] = r * (uint32_t)(K / 2) + 16u * (uint32_t)lq;
+    voff_w[v] = r * wrow + 16u * CW * (uint32_t)lq;
     voff_z[v] = r * (uint32_t)G + gl;
     voff_s[v] = 2u * voff_z[v];
   }
@@ -262,7 +309,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wq[2][NB];                  // codes: k = 32 lq .. 32 lq + 31 of the step, per W row
+  u32x4 wq[2][NB][CW];              // codes: k = 32 lq .. 32 lq + 31 of the step, per W row
   uint32_t ws[2][NB], wz[2][NB];    // raw scale bits / zero point of that 32-k chunk
 
   auto copy_x = [&](int buf, int kt) {
@@ -296,14 +343,45 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     for (int nb = 0; nb < NB; ++nb) {
       const int v = EDGE ? nb : 0;
       const int rb = EDGE ? 0 : RPW * wave + 16 * nb;   // wave-uniform row of the block
-      wq[R][nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          rw, voff_w[v], rb * (K / 2) + ktc * (kStepK / 2), 0));
+#pragma unroll
+      for (int c = 0; c < CW; ++c)
+        wq[R][nb][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            rw, voff_w[v] + 16u * c, rb * (int)wrow + ktc * (kStepK * B / 8), 0));
       if (REGSZ) {
         ws[R][nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s[v], 2 * (rb * G + gs), 0);
-        wz[R][nb] = SYM ? 8u : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, voff_z[v], rb * G + gs, 0);
+        wz[R][nb] = SYM ? kZsym : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, voff_z[v], rb * G + gs, 0);
       }
     }
   };
+
+  // Name the W registers of slot R (codes, and scales / zeros when they come by register):
+  // the compiler then waits for those loads here, and for nothing issued after them.
+  // (One asm statement per kind, so that the compiler emits one wait for the whole set.)
+  auto keep_w = [&wq, &ws, &wz](auto S) {
+    constexpr int R = decltype(S)::value;
+    if constexpr (NB == 4 && CW == 1) {
+      asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][1][0]), "v"(wq[R][2][0]), "v"(wq[R][3][0]));
+    } else if constexpr (NB == 4) {
+      asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][0][1]), "v"(wq[R][1][0]), "v"(wq[R][1][1]), "v"(wq[R][2][0]),
+                   "v"(wq[R][2][1]), "v"(wq[R][3][0]), "v"(wq[R][3][1]));
+    } else if constexpr (CW == 1) {
+      asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][1][0]));
+    } else {
+      asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][0][1]), "v"(wq[R][1][0]), "v"(wq[R][1][1]));
+    }
+    if constexpr (REGSZ) {
+      if constexpr (NB == 4) {
+        asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
+        if constexpr (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
+      } else {
+        asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]));
+        if constexpr (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]));
+      }
+    }
+  };
+  // The two dwords of sub-step ks's codes in a row's slot (the second is unused for 4-bit).
+  auto sub_d0 = [](const u32x4* w, int ks) { return B == 8 ? w[ks >> 1][2 * (ks & 1)] : w[0][ks]; };
+  auto sub_d1 = [](const u32x4* w, int ks) { return B == 8 ? w[ks >> 1][2 * (ks & 1) + 1] : 0u; };
 
   // One step: copy X of step kt + 1 into the other buffer, load W codes of step kt + 1 into
   // the other slot, multiply step kt.
@@ -311,11 +389,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     constexpr int R = decltype(S)::value;
     // The previous barrier already waited for these registers; naming them here, before any
     // new load is issued, keeps the compiler's own wait for them from covering the new loads.
-    asm volatile("" ::"v"(wq[R][0]), "v"(wq[R][1]), "v"(wq[R][2]), "v"(wq[R][3]));
-    if (REGSZ) {
-      asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
-      if (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
-    }
+    keep_w(S);
     // This step's scale / zero words (copied during the previous step) -> registers.
     uint32_t sb[NB], zb[NB];
     if (!REGSZ) {
@@ -327,7 +401,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         sb[nb] = *reinterpret_cast<const uint16_t*>(srow + 128 * nb);
-        zb[nb] = SYM ? 8u : (uint32_t)zrow[64 * nb];
+        zb[nb] = SYM ? kZsym : (uint32_t)zrow[64 * nb];
       }
     }
     copy_x(R ^ 1, kt + 1);
@@ -343,7 +417,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       s[nb] = (float)__builtin_bit_cast(_Float16, (uint16_t)(REGSZ ? ws[R][nb] : sb[nb]));
       const float zf = (float)(REGSZ ? wz[R][nb] : zb[nb]);
       c1[nb] = -s[nb] * (1024.0f + zf);
-      c64[nb] = -s[nb] * (64.0f + zf);
+      c64[nb] = B == 8 ? c1[nb] : -s[nb] * (64.0f + zf);
     }
     const uint8_t* xs = xl + (uint32_t)R * kStageBytes;
 #pragma unroll
@@ -351,7 +425,8 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       bf16x8 a[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        a[nb] = __builtin_bit_cast(bf16x8, dequant8<SYM>(wq[R][nb][ks], s[nb], c1[nb], c64[nb]));
+        a[nb] = __builtin_bit_cast(bf16x8, dequant_sub<SYM, B>(sub_d0(wq[R][nb], ks), sub_d1(wq[R][nb], ks), s[nb],
+                                                               c1[nb], c64[nb]));
       const uint32_t ro = rd_off ^ (16u * ks);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -363,11 +438,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     }
     // Wait for the next step's W registers, and so for everything issued before them (the X
     // and scale / zero copies), before the barrier.
-    asm volatile("" ::"v"(wq[R ^ 1][0]), "v"(wq[R ^ 1][1]), "v"(wq[R ^ 1][2]), "v"(wq[R ^ 1][3]));
-    if (REGSZ) {
-      asm volatile("" ::"v"(ws[R ^ 1][0]), "v"(ws[R ^ 1][1]), "v"(ws[R ^ 1][2]), "v"(ws[R ^ 1][3]));
-      if (!SYM) asm volatile("" ::"v"(wz[R ^ 1][0]), "v"(wz[R ^ 1][1]), "v"(wz[R ^ 1][2]), "v"(wz[R ^ 1][3]));
-    }
+    keep_w(Slot<R ^ 1>{});
     step_barrier();
   };
 
@@ -375,11 +446,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     copy_x(0, 0);
     if (!REGSZ) copy_sz(0, 0);
     load_w(Slot<0>{}, 0);
-    asm volatile("" ::"v"(wq[0][0]), "v"(wq[0][1]), "v"(wq[0][2]), "v"(wq[0][3]));
-    if (REGSZ) {
-      asm volatile("" ::"v"(ws[0][0]), "v"(ws[0][1]), "v"(ws[0][2]), "v"(ws[0][3]));
-      if (!SYM) asm volatile("" ::"v"(wz[0][0]), "v"(wz[0][1]), "v"(wz[0][2]), "v"(wz[0][3]));
-    }
+    keep_w(Slot<0>{});
     step_barrier();
 
     // Straight-line body of two steps (one per buffer / register slot); an odd last step follows.
@@ -414,23 +481,16 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
           const uint8_t* st = xl + 2u * kStageBytes + (uint32_t)R * kSzStage;
           sbits = *reinterpret_cast<const uint16_t*>(st + (uint32_t)wave * 512u + (uint32_t)li * 8u + 2u * gl +
                                                      2u * (par & 1u) + 128u * nb);
-          zbits = SYM ? 8u : (uint32_t)st[2048u + (uint32_t)wave * 256u + (uint32_t)li * 4u + gl + (par & 3u) + 64u * nb];
+          zbits = SYM ? kZsym : (uint32_t)st[2048u + (uint32_t)wave * 256u + (uint32_t)li * 4u + gl + (par & 3u) + 64u * nb];
         }
         sc[R][nb] = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
         const float zf = (float)zbits;
         cc1[R][nb] = -sc[R][nb] * (1024.0f + zf);
-        cc64[R][nb] = -sc[R][nb] * (64.0f + zf);
+        cc64[R][nb] = B == 8 ? cc1[R][nb] : -sc[R][nb] * (64.0f + zf);
       }
     };
     // Wait for this wave's loads of the step in slot R (codes; everything issued before them).
-    auto wait_codes = [&wq, &ws, &wz](auto S) {
-      constexpr int R = decltype(S)::value;
-      asm volatile("" ::"v"(wq[R][0]), "v"(wq[R][1]), "v"(wq[R][2]), "v"(wq[R][3]));
-      if (REGSZ) {
-        asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
-        if (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
-      }
-    };
+    auto wait_codes = [&](auto S) { keep_w(S); };
 
     auto step_large = [&](auto S, int kt) {
       constexpr int R = decltype(S)::value;
@@ -466,13 +526,19 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
         // Slot 1: the biased fp16 pairs of a new code dword.
         mfma_acc(acc[1][mb], a[ks & 1][1], b);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (piece == 0) bq = deq_prep<SYM>(next ? wq[R ^ 1][nbw][0] : wq[R][nbw][ks + 1]);
+        if constexpr (piece == 0) {
+          constexpr int kn = next ? 0 : ks + 1;                   // the sub-step dequantised
+          const u32x4* wsrc = next ? wq[R ^ 1][nbw] : wq[R][nbw];
+          if constexpr (B == 8) bq = deq_prep_b<SYM>(sub_d0(wsrc, kn), sub_d1(wsrc, kn));
+          else bq = deq_prep<SYM>(sub_d0(wsrc, kn));
+        }
         __builtin_amdgcn_sched_barrier(0);
         // Slot 2: the two exact products of this group's pair.
         mfma_acc(acc[2][mb], a[ks & 1][2], b);
         __builtin_amdgcn_sched_barrier(0);
         float w0, w1;
-        deq_fmas(bq, piece, sc[S2][nbw], cc1[S2][nbw], cc64[S2][nbw], w0, w1);
+        if constexpr (B == 8) deq_fmas_b(bq, piece, sc[S2][nbw], cc1[S2][nbw], w0, w1);
+        else deq_fmas(bq, piece, sc[S2][nbw], cc1[S2][nbw], cc64[S2][nbw], w0, w1);
         __builtin_amdgcn_sched_barrier(0);
         // Slot 3: the pair packed into the operand; before sub-step 3, this wave's next codes
         // are waited for and the next step's scales formed.
@@ -494,7 +560,8 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     wait_codes(Slot<0>{});
     prep_scales(Slot<0>{}, 0);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) a[0][nb] = dequant8<SYM>(wq[0][nb][0], sc[0][nb], cc1[0][nb], cc64[0][nb]);
+    for (int nb = 0; nb < NB; ++nb)
+      a[0][nb] = dequant_sub<SYM, B>(sub_d0(wq[0][nb], 0), sub_d1(wq[0][nb], 0), sc[0][nb], cc1[0][nb], cc64[0][nb]);
     step_barrier();
 
     int kt = 0;
@@ -532,7 +599,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
   }
 }
 
-template <int TM, int NBW, bool SYM>
+template <int TM, int NBW, bool SYM, int B>
 hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
                      const void* scales, const void* zeros, void* Y, hipStream_t stream) {
   constexpr int TN = 64 * NBW;
@@ -543,7 +610,7 @@ hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, con
   const int64_t full_blocks = (int64_t)full_m * full_n;
   if ((int64_t)tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
   if (full_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, false>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, false, B>), dim3((unsigned)full_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, full_m, full_n, 0, vec);
     const hipError_t e = hipGetLastError();
@@ -554,7 +621,7 @@ hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, con
   const int edge_row = tiles_m != full_m;
   const int64_t edge_blocks = (edge_row ? tiles_n : 0) + (tiles_n != full_n ? full_m : 0);
   if (edge_blocks > 0) {
-    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, true>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prefill_kernel<TM, NBW, SYM, true, B>), dim3((unsigned)edge_blocks), dim3(256), 0, stream,
                        (const uint16_t*)X, (int)M, (int)N, (int)K, lg, (const uint8_t*)packed,
                        (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, tiles_m, tiles_n,
                        edge_row, vec);
@@ -563,29 +630,31 @@ hipError_t launch_tm(const void* X, int64_t M, int64_t N, int64_t K, int lg, con
   return hipSuccess;
 }
 
-template <bool SYM>
+template <bool SYM, int B>
 hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
   // The 256-row tile runs one block per compute unit: take it when its tiles fill every unit.
   const int64_t large_tiles = ((M + kTileMLarge - 1) / kTileMLarge) * ((N + kTileN - 1) / kTileN);
   if (large_tiles >= num_cus)
-    return launch_tm<kTileMLarge, 4, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+    return launch_tm<kTileMLarge, 4, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
   // 128 X rows: 256-row W tiles when they fill both block slots of every unit, else twice as
   // many 128-row tiles (M=1024 at 8192^2: 180 -> 157 us).
+  // (8-bit codes: the 128 x 256 tile would spill its doubled code registers, so they go
+  // straight to 128 x 128.)
   const int64_t small_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + kTileN - 1) / kTileN);
-  if (small_tiles >= 2 * (int64_t)num_cus)
-    return launch_tm<kTileMSmall, 4, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
-  return launch_tm<kTileMSmall, 2, SYM>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  if (B == 4 && small_tiles >= 2 * (int64_t)num_cus)
+    return launch_tm<kTileMSmall, 4, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  return launch_tm<kTileMSmall, 2, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
 }
 
 }  // namespace
 
-bool prefill_fits(int64_t M, int64_t N, int64_t K, int g) {
+bool prefill_fits(int64_t M, int64_t N, int64_t K, int g, int bits) {
   // 32-bit offsets: a block's X rows and the W codes / scales behind one buffer resource
   // must span < 2 GiB.
   const int64_t lim = int64_t(1) << 31;
   return M >= kPrefillMinM && K % kStepK == 0 && g >= 32 && (g & (g - 1)) == 0 &&
-         (int64_t)kTileMLarge * K * 2 < lim && N * (K / 2) < lim && N * (K / g) * 2 < lim;
+         (int64_t)kTileMLarge * K * 2 < lim && N * (K * bits / 8) < lim && N * (K / g) * 2 < lim;
 }
 
 hipError_t launch_prefill(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
@@ -593,8 +662,17 @@ hipError_t launch_prefill(const void* X, int64_t M, int64_t N, int64_t K, int g,
                           int num_cus, hipStream_t stream) {
   int lg = 0;
   while ((1 << lg) < g) ++lg;
-  return sym ? launch_sym<true>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream)
-             : launch_sym<false>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream);
+  return sym ? launch_sym<true, 4>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream)
+             : launch_sym<false, 4>(X, M, N, K, lg, packed, scales, zeros, Y, num_cus, stream);
+}
+
+hipError_t launch_prefill8(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
+                           const void* codes, const void* scales, const void* zeros, void* Y,
+                           int num_cus, hipStream_t stream) {
+  int lg = 0;
+  while ((1 << lg) < g) ++lg;
+  return sym ? launch_sym<true, 8>(X, M, N, K, lg, codes, scales, zeros, Y, num_cus, stream)
+             : launch_sym<false, 8>(X, M, N, K, lg, codes, scales, zeros, Y, num_cus, stream);
 }
 
 }  // namespace q4

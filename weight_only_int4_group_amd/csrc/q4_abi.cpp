@@ -314,6 +314,8 @@ int q4_matmul_w8(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int3
   const bool sym = mode == Q4_SYM;
   if (kernel == Q4_KERNEL_GEMV)
     return finish(q4::launch_gemv8(X, (int)M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
+  if (q4::prefill_fits(M, N, K, g, 8))
+    return finish(q4::launch_prefill8(X, M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm8(X, M, N, K, g, sym, codes, scales, zeros, Y, num_cus(), s));
 }
 

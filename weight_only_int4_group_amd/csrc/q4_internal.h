@@ -76,13 +76,16 @@ hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool
                          const void* packed, const void* scales, const void* zeros, void* Y,
                          int num_cus, hipStream_t stream);
 
-// Large-M GEMM (256 x 256 tiles, W dequantised once per tile into LDS): M >= kPrefillMinM,
-// K a multiple of 64, g a power of two.
+// Large-M GEMM (X staged in LDS, W dequantised in registers): M >= kPrefillMinM, K a
+// multiple of 128, g a power of two; bits = 4 (W4A16) or 8 (W8A16, launch_prefill8).
 constexpr int64_t kPrefillMinM = 512;
-bool prefill_fits(int64_t M, int64_t N, int64_t K, int g);
+bool prefill_fits(int64_t M, int64_t N, int64_t K, int g, int bits = 4);
 hipError_t launch_prefill(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
                           const void* packed, const void* scales, const void* zeros, void* Y, int num_cus,
                           hipStream_t stream);
+hipError_t launch_prefill8(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
+                           const void* codes, const void* scales, const void* zeros, void* Y,
+                           int num_cus, hipStream_t stream);
 
 // MFMA GEMM for any M >= 1.
 hipError_t launch_gemm(const void* X, int64_t M, int64_t N, int64_t K, int g, bool sym,
