@@ -177,17 +177,29 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t c, const float 
   }
 }
 
+// Min or max over each aligned group of L lanes (L a power of two, 4..64), the result in every
+// lane.  Inside a 16-lane row the partners come from DPP (quad permutes, then the half-row and
+// row mirrors: after each step every lane holds the result of a twice larger group, in any
+// order, which min and max do not mind), with no LDS traffic; wider groups add lane exchanges
+// across rows.
+template <int L, typename Op>
+__device__ __forceinline__ float lanes_reduce(float v, Op op) {
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  if constexpr (L >= 4) v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if constexpr (L >= 8) v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  if constexpr (L >= 16) v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+#pragma unroll
+  for (int o = 16; o < L; o <<= 1) v = op(v, __shfl_xor(v, o));
+  return v;
+}
+
 template <int L>
 __device__ __forceinline__ float lanes_min(float v) {
-#pragma unroll
-  for (int o = 1; o < L; o <<= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+  return lanes_reduce<L>(v, [](float a, float b) { return fminf(a, b); });
 }
 template <int L>
 __device__ __forceinline__ float lanes_max(float v) {
-#pragma unroll
-  for (int o = 1; o < L; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return lanes_reduce<L>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // g in {32, 64, 128, 256, 512}: a group is L = g/8 consecutive lanes, each holding one chunk.
