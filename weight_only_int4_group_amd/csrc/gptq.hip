@@ -19,15 +19,18 @@
 // index-reversed Hessian R = J H J (R[a][b] = H[K-1-a][K-1-b]): Ut[i][j] = L[K-1-i][K-1-j].
 //
 // Kernels (all fp32, fixed summation order, no atomics):
-//   * gemm_f32_kernel: C = alpha A B + beta C on 64 x 64 tiles with arbitrary (signed) strides;
-//     it forms R from X with the columns read in reverse, the Cholesky's trailing updates
-//     (lower tiles only) and the sweep's block updates;
+//   * gemm_f32_kernel: C = alpha A B + beta C on 64 x 64 tiles of the fp32 matrix cores with
+//     arbitrary (signed) strides; it forms R from X with the columns read in reverse, the
+//     Cholesky's updates (inside a 128-column outer block, then the trailing matrix with inner
+//     dimension 128, lower tiles only) and the sweep's feedback updates (inside an outer block
+//     after every 32 columns, then all later columns once per outer block);
 //   * damp_kernel: one block; mean of the diagonal in a fixed order, then the dampening;
-//   * potf2_kernel / trsm_kernel: the 32 x 32 diagonal block and the panel below it;
+//   * potf2_kernel / trsm_kernel: the 32 x 32 diagonal block (one lane per row, in registers)
+//     and the panel below it;
 //   * colscale_kernel: L[a][b] / L[b][b] below the diagonal (the update coefficients);
-//   * sweep_block_kernel: one thread per weight row runs the 32 columns of a block in order
-//     (error feedback inside the block from LDS, earlier blocks through the accumulated
-//     updates), writes the 16 packed bytes and the block's residuals w_j - x_hat_j.
+//   * sweep_block_kernel: one thread per weight row runs 32 columns in order (error feedback
+//     inside the step from LDS, earlier columns through the accumulated updates), writes the
+//     16 packed bytes and the step's residuals w_j - x_hat_j.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
