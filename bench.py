@@ -422,6 +422,55 @@ def measure_gptq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, reps=3, 
     return res
 
 
+def measure_dequant(torch, q4, sets, W4_bits, g=128, reps=30, with_oracle=True, oracle_rows=1024):
+    """q4_dequantize of the 70B-shaped weight W[28672, 8192] (asym, g=128) to bf16, rotating over
+    the benchmark's six quantized copies; algorithmic bytes = codes + scales + zeros read + the
+    bf16 output written.  In the CPU-baseline leg the oracle quantizes the first `oracle_rows`
+    rows, the library dequantizes those codes and must match the oracle's dequantization bit
+    for bit, and the oracle's dequantization is timed."""
+    import numpy as np
+    p0 = sets[0][0]
+    N, K = p0.shape[0], p0.shape[1] * 2
+    G = K // g
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=p0.device)
+    L = len(sets)
+    run = lambda i: q4.dequantize_into(*sets[i % L], g, "asym", out)
+    run(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    by = N * K // 2 + 3 * N * G + 2 * N * K
+    gbs = by / (ms * 1e-3) / 1e9
+    res = {"workload": f"q4_dequantize of W[{N},{K}] asym g={g} to bf16, {L} weight copies",
+           "ms": round(ms, 5), "bytes_per_launch": by, "kernel": "dequant_kernel",
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    if with_oracle:
+        from oracle import q4_oracle as orc
+        rp, rs, rz = orc.quantize_rtn_ref(W4_bits[:oracle_rows], g, "asym")
+        dev = p0.device
+        pd = torch.from_numpy(rp).to(dev)
+        sd = torch.from_numpy(rs.view(np.int16)).view(torch.float16).to(dev)
+        zd = torch.from_numpy(rz).to(dev)
+        got = q4.dequantize(pd, sd, zd, g, "asym")
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        want = orc.dequantize_rounded_ref(rp, rs, rz, g, "asym", "bf16")
+        spent = time.perf_counter() - t
+        if not np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), want):
+            raise AssertionError("dequantize parity failed")
+        res["cpu_oracle"] = {"kind": "oracle", "sample": f"oracle dequantize_rounded_ref of the first "
+                                                          f"{oracle_rows} rows (bf16 out)",
+                             "seconds": round(spent, 3),
+                             "GB/s": round(oracle_rows * (K // 2 + 3 * G + 2 * K) / spent / 1e9, 4)}
+    return res
+
+
 # --------------------------------------------------------------------------- counters
 def _counter_rows(d):
     rows = []
@@ -779,6 +828,8 @@ def main(argv=None):
     if not args.no_context:
         out["context"] = measure_context(torch, q4, sets, X5, W5, w5)
         note("context measured")
+    out["dequantize"] = measure_dequant(torch, q4, sets, W4_bits, with_oracle=not args.no_cpu_baseline)
+    note("standalone dequantize measured")
     out["gemv_llama7b_up"] = measure_gemv_7b(torch, q4)
     note("Llama-7B-shaped decode measured")
     if not args.no_w8:
