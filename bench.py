@@ -596,13 +596,15 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, q_budget_s=6.0, block=4096):
+def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, q_budget_s=6.0, block=4096, W5_bits=None,
+                 X5_bits=None, prefill_rows=256):
     """The CPU oracle, timed on this host over bounded samples of the 70B-shaped layer.
 
     matmul_ref (M=1, fp64 dequantisation + BLAS, all BLAS threads): the oracle quantizes each
     row block first (not timed), then matmul_ref is timed over the blocks, cycling through the
     layer until about budget_s seconds are spent.  quantize_ref (elementwise numpy, one
-    thread) is timed on consecutive row blocks until about q_budget_s seconds are spent.
+    thread) is timed on consecutive row blocks until about q_budget_s seconds are spent.  The
+    prefill product (M = 2048) is timed on `prefill_rows` rows of the prefill layer's W.
     """
     import numpy as np
     from oracle import q4_oracle as orc
@@ -630,7 +632,18 @@ def cpu_baseline(W_bits, X_bits, g, mode, budget_s=10.0, q_budget_s=6.0, block=4
         q_rows += min(qb, N - q_rows)
     G = K // g
     q_bytes = q_rows * (2 * K + K // 2 + G * (3 if mode == "asym" else 2))
+    prefill = None
+    if W5_bits is not None:
+        p5, s5, z5 = orc.quantize_rtn_ref(W5_bits[:prefill_rows], 128, "asym")
+        t = time.perf_counter()
+        orc.matmul_ref(X5_bits, p5, s5, z5, 128, "asym")
+        ps = time.perf_counter() - t
+        prefill = {"TFLOP/s": round(2.0 * X5_bits.shape[0] * prefill_rows * W5_bits.shape[1] / ps / 1e12, 5),
+                   "seconds": round(ps, 3),
+                   "sample": f"oracle matmul_ref, M={X5_bits.shape[0]}, the first {prefill_rows} rows of the "
+                             f"prefill layer's W (g=128 asym)"}
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "prefill_matmul_ref": prefill,
             "kind": "oracle",
             "sample": f"oracle matmul_ref (fp64 dequantisation + BLAS), M=1, the whole {N}x{K} "
                       f"layer in row blocks of {block}, {passes} passes, {spent:.1f} s",
@@ -843,7 +856,7 @@ def main(argv=None):
         out["awq"] = measure_awq(torch, q4, W5, X5, W5_bits, X5_bits, with_oracle=not args.no_cpu_baseline)
         note("AWQ search measured")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym")
+        out["cpu_baseline"] = cpu_baseline(W4_bits, X4_bits, g4, "asym", W5_bits=W5_bits, X5_bits=X5_bits)
         note("CPU baseline timed")
     print(json.dumps(out), flush=True)
     return 0
