@@ -77,18 +77,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < Kd; k0 += kStep) {
+  // Register prefetch: the global values of step k0 + kStep are loaded while step k0 is
+  // multiplied from LDS, so their latency overlaps the matrix instructions.
+  float pa[4], pb[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + 256 * e;                 // 1024 = 64 x 16 elements of each operand
       const int am = idx >> 4, ak = idx & 15;        // A: row-major over (m, k)
       const int m = m0 + am, k = k0 + ak;
-      As[ak][am] = (m < M && k < Kd) ? ld_f32(A, (int64_t)m * sam + (int64_t)k * sak) : 0.0f;
+      pa[e] = (m < M && k < Kd) ? ld_f32(A, (int64_t)m * sam + (int64_t)k * sak) : 0.0f;
       const int bk = idx >> 6, bnn = idx & 63;       // B: row-major over (k, n)
       const int kk = k0 + bk, n = n0 + bnn;
-      Bs[bk][bnn] = (kk < Kd && n < N) ? ld_f32(B, (int64_t)kk * sbk + (int64_t)n * sbn) : 0.0f;
+      pb[e] = (kk < Kd && n < N) ? ld_f32(B, (int64_t)kk * sbk + (int64_t)n * sbn) : 0.0f;
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < Kd; k0 += kStep) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e;
+      As[idx & 15][idx >> 4] = pa[e];
+      Bs[idx >> 6][idx & 63] = pb[e];
     }
     __syncthreads();
+    if (k0 + kStep < Kd) fetch(k0 + kStep);
     // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of a
     // 16 x 4 by 4 x 16 step; the 16 x 16 result sits in lane l as rows 4 (l / 16) + r, column l % 16
 #pragma unroll
