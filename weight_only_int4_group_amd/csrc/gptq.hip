@@ -21,16 +21,17 @@
 // Kernels (all fp32, fixed summation order, no atomics):
 //   * gemm_f32_kernel: C = alpha A B + beta C on 64 x 64 tiles of the fp32 matrix cores with
 //     arbitrary (signed) strides; it forms R from X with the columns read in reverse, the
-//     Cholesky's updates (inside a 128-column outer block, then the trailing matrix with inner
-//     dimension 128, lower tiles only) and the sweep's feedback updates (inside an outer block
-//     after every 32 columns, then all later columns once per outer block);
+//     Cholesky's updates (inside an outer block of kOuter columns, then the trailing matrix
+//     with inner dimension kOuter, lower tiles only) and the sweep's feedback updates (inside an
+//     outer block after every 32 columns, then all later columns once per outer block);
 //   * damp_kernel: one block; mean of the diagonal in a fixed order, then the dampening;
 //   * potf2_kernel / trsm_kernel: the 32 x 32 diagonal block (one lane per row, in registers)
 //     and the panel below it;
 //   * colscale_kernel: L[a][b] / L[b][b] below the diagonal (the update coefficients);
 //   * sweep_block_kernel: one thread per weight row runs 32 columns in order (error feedback
 //     inside the step from LDS, earlier columns through the accumulated updates), writes the
-//     16 packed bytes and the step's residuals w_j - x_hat_j.
+//     16 packed bytes and puts the step's residuals w_j - x_hat_j in place of the feedback it
+//     has consumed.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,7 +45,7 @@ namespace {
 constexpr int kTile = 64;          // GEMM output tile
 constexpr int kStep = 16;          // GEMM inner step
 constexpr int kB = 32;             // Cholesky panel and sweep step (K % 32 == 0)
-constexpr int kOuter = 128;        // columns per outer block: the width of the big updates
+constexpr int kOuter = 256;        // columns per outer block: the width of the big updates
 
 template <typename T>
 __device__ __forceinline__ float ld_f32(const T* p, int64_t i);
@@ -226,15 +227,15 @@ __global__ __launch_bounds__(256) void colscale_kernel(float* __restrict__ R, in
 
 // One step of 32 columns [i1, i1 + 32) for every weight row (one thread per row).  The step
 // lies inside one group.  Cb[j][i] = Ut[i1 + j][i1 + i] / Ut[i1 + i][i1 + i] for j < i.
-// acc holds the feedback of the earlier columns (none when i1 == 0).  Writes the 16 packed
-// bytes of the step and the residuals w_j - x_hat_j (fp32) to D[n * dld + doff + 0..31].
+// acc[n][i1 .. i1 + 31] holds the feedback of the earlier columns (not read when i1 == 0); the
+// thread reads it, then overwrites the same 32 floats with the residuals w_j - x_hat_j, which
+// the later feedback updates read from there.  Also writes the step's 16 packed bytes.
 template <bool SYM>
 __global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __restrict__ W, int64_t N, int K, int g,
-                                                          const float* __restrict__ Lc, const float* __restrict__ acc,
+                                                          const float* __restrict__ Lc, float* __restrict__ acc,
                                                           int i1, const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
-                                                          uint8_t* __restrict__ packed, float* __restrict__ D,
-                                                          int dld, int doff) {
+                                                          uint8_t* __restrict__ packed) {
   __shared__ float Cb[kB][kB + 1];
   for (int e = threadIdx.x; e < kB * kB; e += 256) {
     const int j = e / kB, i = e % kB;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __rest
     nib[i / 8] |= ((uint32_t)(int)c & 0xFu) << (4 * (i % 8));
   }
   *reinterpret_cast<u32x4*>(packed + n * (int64_t)(K / 2) + i1 / 2) = u32x4{nib[0], nib[1], nib[2], nib[3]};
-  float4* dp = reinterpret_cast<float4*>(D + n * dld + doff);
+  float4* dp = reinterpret_cast<float4*>(acc + n * (int64_t)K + i1);
 #pragma unroll
   for (int v = 0; v < kB / 4; ++v) dp[v] = float4{d[4 * v], d[4 * v + 1], d[4 * v + 2], d[4 * v + 3]};
 }
@@ -307,8 +308,7 @@ GptqLayout gptq_layout(int64_t N, int64_t K) {
   auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
   L.R = 0;
   L.acc = up(L.R + 4 * K * K);
-  L.D = up(L.acc + 4 * N * K);
-  L.bytes = up(L.D + 4 * N * kOuter);
+  L.bytes = up(L.acc + 4 * N * K);
   return L;
 }
 
@@ -319,7 +319,6 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   char* base = static_cast<char*>(workspace);
   float* R = reinterpret_cast<float*>(base + L.R);
   float* acc = reinterpret_cast<float*>(base + L.acc);
-  float* D = reinterpret_cast<float*>(base + L.D);
   const int Ki = (int)K;
   const uint16_t* Xh = static_cast<const uint16_t*>(X);
 
@@ -337,7 +336,7 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, R, Ki, damp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 3. blocked lower Cholesky of R, in place.  Outer blocks of 128 columns [o1, o2): 32-column
+  // 3. blocked lower Cholesky of R, in place.  Outer blocks of kOuter columns [o1, o2): 32-column
   //    panels (diagonal block, the rows below, the update of the outer block's remaining
   //    columns), then one update of the trailing matrix with inner dimension o2 - o1.
   for (int o1 = 0; o1 < Ki; o1 += kOuter) {
@@ -367,11 +366,13 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
                      dim3(256), 0, stream, R, Ki);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 4. the sweep: outer blocks of 128 columns [s1, s2), 32 columns per step.  After a step its
-  //    residuals feed the outer block's later columns (a small update); after the outer block
-  //    its residuals feed every later column (one update with inner dimension s2 - s1).
-  //    acc[:, i] = sum over earlier columns j of D_j C[j][i], C[j][i] = Lc[K-1-j][K-1-i]; the
-  //    first update to reach a column writes it (beta = 0), later ones add.
+  // 4. the sweep: outer blocks of kOuter columns [s1, s2), 32 columns per step.  After a step
+  //    its residuals feed the outer block's later columns (a small update); after the outer
+  //    block its residuals feed every later column (one update with inner dimension s2 - s1).
+  //    acc[:, i] = sum over earlier columns j of D_j C[j][i], C[j][i] = Lc[K-1-j][K-1-i], where
+  //    the residuals D_j sit in acc[:, j] once column j is quantized; the first update to reach
+  //    a column writes it (beta = 0), later ones add.  The updates read residual columns
+  //    [s1, s2) and write columns >= s2 (or the step's later columns), never the same ones.
   const unsigned rows_grid = (unsigned)((N + 255) / 256);
   auto coef = [&](int j0, int i0) { return R + (int64_t)(Ki - 1 - j0) * K + (Ki - 1 - i0); };
   for (int s1 = 0; s1 < Ki; s1 += kOuter) {
@@ -381,23 +382,23 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
         hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
                            static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                           static_cast<uint8_t*>(packed), D, kOuter, i1 - s1);
+                           static_cast<uint8_t*>(packed));
       else
         hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
                            static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                           static_cast<uint8_t*>(packed), D, kOuter, i1 - s1);
+                           static_cast<uint8_t*>(packed));
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int i2 = i1 + kB;
       if (i2 < s2) {
-        e = gemm<float, float>(D + (i1 - s1), kOuter, 1, coef(i1, i2), -K, -1, acc + i2, K, (int)N, s2 - i2, kB, 1.0f,
+        e = gemm<float, float>(acc + i1, K, 1, coef(i1, i2), -K, -1, acc + i2, K, (int)N, s2 - i2, kB, 1.0f,
                                (s1 == 0 && i1 == 0) ? 0.0f : 1.0f, false, stream);
         if (e != hipSuccess) return e;
       }
     }
     if (s2 < Ki) {
-      e = gemm<float, float>(D, kOuter, 1, coef(s1, s2), -K, -1, acc + s2, K, (int)N, Ki - s2, s2 - s1, 1.0f,
+      e = gemm<float, float>(acc + s1, K, 1, coef(s1, s2), -K, -1, acc + s2, K, (int)N, Ki - s2, s2 - s1, 1.0f,
                              s1 == 0 ? 0.0f : 1.0f, false, stream);
       if (e != hipSuccess) return e;
     }
