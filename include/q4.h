@@ -285,7 +285,7 @@ int q4_select_kernel_w8(int64_t M, int64_t N, int64_t K, int32_t g);
  * The matmul kernels consume the result like any q4_quantize_rtn output.
  */
 
-/* Bytes of device workspace q4_gptq needs: 4 K^2 + 4 N K bytes, each part rounded up to
+/* Bytes of device workspace q4_gptq needs: 4 K^2 + 4 N K + 128 K bytes, each part rounded up to
  * 256; or a negative status (Q4_ERR_SHAPE when M < 1 or K > 32768, the q4_quantize_rtn errors
  * otherwise).  Pure host function, no HIP call. */
 int64_t q4_gptq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t g);

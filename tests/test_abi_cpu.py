@@ -302,7 +302,7 @@ def test_gptq_workspace_bytes():
     lib = q4.library()
     N, K = 4096, 8192
     up = lambda b: (b + 255) // 256 * 256
-    assert lib.q4_gptq_workspace_bytes(512, N, K, 128) == up(4 * K * K) + up(4 * N * K)
+    assert lib.q4_gptq_workspace_bytes(512, N, K, 128) == up(4 * K * K) + up(4 * N * K) + up(128 * K)
     assert lib.q4_gptq_workspace_bytes(0, N, K, 128) == -2
     assert lib.q4_gptq_workspace_bytes(1, N, 65536, 128) == -2
     assert lib.q4_gptq_workspace_bytes(1, N, K, 48) == -3

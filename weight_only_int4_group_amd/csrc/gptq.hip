@@ -25,8 +25,9 @@
 //     with inner dimension kOuter, lower tiles only) and the sweep's feedback updates (inside an
 //     outer block after every 32 columns, then all later columns once per outer block);
 //   * damp_kernel: one block; mean of the diagonal in a fixed order, then the dampening;
-//   * potf2_kernel / trsm_kernel: the 32 x 32 diagonal block (one lane per row, in registers)
-//     and the panel below it;
+//   * panel_kernel: a 32-column panel, the 32 x 32 diagonal block (one lane per row, in
+//     registers, in every workgroup) and the rows below it (one thread per row);
+//   * diag_store_kernel: the factored diagonal blocks into R once the panels are done;
 //   * colscale_kernel: L[a][b] / L[b][b] below the diagonal (the update coefficients);
 //   * sweep_block_kernel: one thread per weight row runs 32 columns in order (error feedback
 //     inside the step from LDS, earlier columns through the accumulated updates), writes the
@@ -46,6 +47,7 @@ constexpr int kTile = 64;          // GEMM output tile
 constexpr int kStep = 16;          // GEMM inner step
 constexpr int kB = 32;             // Cholesky panel and sweep step (K % 32 == 0)
 constexpr int kOuter = 256;        // columns per outer block: the width of the big updates
+constexpr int kSweepThreads = 256; // weight rows per sweep workgroup (one thread per row)
 
 template <typename T>
 __device__ __forceinline__ float ld_f32(const T* p, int64_t i);
@@ -159,63 +161,94 @@ __global__ __launch_bounds__(1024) void damp_kernel(float* __restrict__ R, int K
   }
 }
 
-// Unblocked Cholesky of the 32 x 32 diagonal block at (k0, k0), lower part, one wave: lane i
-// holds row i in registers; the column loop is unrolled, so every pivot and every l_kj is a
-// lane read with a constant index.  A non-positive pivot records info = column + 1 (first
-// failure only) and is replaced by 1e-30 so the factorisation completes.
-__global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ R, int K, int k0, int* __restrict__ info) {
-  const int i = threadIdx.x & 31;
-  const bool own = threadIdx.x < kB;
-  float* row = R + (int64_t)(k0 + i) * K + k0;
-  float a[kB];
-#pragma unroll
-  for (int j = 0; j < kB; ++j) a[j] = (own && j <= i) ? row[j] : 0.0f;
-  int bad = 0;
-#pragma unroll
-  for (int j = 0; j < kB; ++j) {
-    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
-    if (!(d > 0.0f)) {
-      if (bad == 0) bad = j + 1;
-      d = 1e-30f;
-    }
-    d = sqrtf(d);
-    a[j] = i == j ? d : (i > j ? a[j] / d : a[j]);
-#pragma unroll
-    for (int k = j + 1; k < kB; ++k) {
-      const float lkj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), k));
-      if (i >= k) a[k] = __builtin_fmaf(-a[j], lkj, a[k]);
-    }
-  }
-  if (bad != 0 && threadIdx.x == 0 && info[0] == 0) info[0] = k0 + bad;
-  if (own) {
-#pragma unroll
-    for (int j = 0; j < kB; ++j)
-      if (j <= i) row[j] = a[j];
-  }
-}
-
-// Panel: rows r >= k0 + 32, L[r, k0:k0+32] = R[r, k0:k0+32] L_kk^-T (forward substitution with
-// the factored diagonal block), one thread per row.
-__global__ __launch_bounds__(256) void trsm_kernel(float* __restrict__ R, int K, int k0) {
+// One 32-column panel of the Cholesky factorisation at column k0.
+//  * The diagonal block: wave 0 of every workgroup factors the 32 x 32 block at (k0, k0) from
+//    R, which no thread writes during this launch.  Lane i holds row i in registers; the
+//    column loop is unrolled, so every pivot and every l_kj is a lane read with a constant
+//    index.  Workgroup 0 stores the factor to Ld[k0 * 32 ...] (row-major 32 x 32; it reaches
+//    R's diagonal block through diag_store_kernel once the factorisation is done) and records
+//    a non-positive pivot as info = column + 1 (first failure only).  Such a pivot is replaced
+//    by 1e-30 so the factorisation completes.
+//  * The rows below: one thread per row r >= k0 + 32 solves L[r, k0:k0+32] = R[r, k0:k0+32]
+//    L_kk^-T by forward substitution.  The row is loaded before the factorisation so its
+//    latency overlaps that work.
+__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ R, int K, int k0, float* __restrict__ Ld,
+                                                    int* __restrict__ info) {
   __shared__ float l[kB][kB + 1];
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
-    const int i = e / kB, j = e % kB;
-    l[i][j] = j <= i ? R[(int64_t)(k0 + i) * K + k0 + j] : 0.0f;
+  const int64_t r = (int64_t)k0 + kB + (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool has_row = r < K;
+  float x[kB];
+  if (has_row) {
+    const float4* rp = reinterpret_cast<const float4*>(R + r * K + k0);
+#pragma unroll
+    for (int v = 0; v < kB / 4; ++v) {
+      const float4 t = rp[v];
+      x[4 * v] = t.x;
+      x[4 * v + 1] = t.y;
+      x[4 * v + 2] = t.z;
+      x[4 * v + 3] = t.w;
+    }
+  }
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x & 31;
+    const bool own = threadIdx.x < kB;
+    const float* row = R + (int64_t)(k0 + i) * K + k0;
+    float a[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) a[j] = (own && j <= i) ? row[j] : 0.0f;
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
+      if (!(d > 0.0f)) {
+        if (bad == 0) bad = j + 1;
+        d = 1e-30f;
+      }
+      d = sqrtf(d);
+      a[j] = i == j ? d : (i > j ? a[j] / d : a[j]);
+#pragma unroll
+      for (int k = j + 1; k < kB; ++k) {
+        const float lkj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), k));
+        if (i >= k) a[k] = __builtin_fmaf(-a[j], lkj, a[k]);
+      }
+    }
+    if (own) {
+#pragma unroll
+      for (int j = 0; j < kB; ++j) l[i][j] = j <= i ? a[j] : 0.0f;
+    }
+    if (blockIdx.x == 0) {
+      if (own) {
+        float4* lp = reinterpret_cast<float4*>(Ld + (int64_t)k0 * kB + i * kB);
+#pragma unroll
+        for (int v = 0; v < kB / 4; ++v)
+          lp[v] = float4{4 * v <= i ? a[4 * v] : 0.0f, 4 * v + 1 <= i ? a[4 * v + 1] : 0.0f,
+                         4 * v + 2 <= i ? a[4 * v + 2] : 0.0f, 4 * v + 3 <= i ? a[4 * v + 3] : 0.0f};
+      }
+      if (bad != 0 && threadIdx.x == 0 && info[0] == 0) info[0] = k0 + bad;
+    }
   }
   __syncthreads();
-  const int64_t r = (int64_t)k0 + kB + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= K) return;
-  float* row = R + r * K + k0;
-  float x[kB];
+  if (!has_row) return;
 #pragma unroll
   for (int j = 0; j < kB; ++j) {
-    float v = row[j];
+    float v = x[j];
 #pragma unroll
     for (int t = 0; t < j; ++t) v = __builtin_fmaf(-x[t], l[j][t], v);
     x[j] = v / l[j][j];
   }
+  float4* wp = reinterpret_cast<float4*>(R + r * K + k0);
 #pragma unroll
-  for (int j = 0; j < kB; ++j) row[j] = x[j];
+  for (int v = 0; v < kB / 4; ++v) wp[v] = float4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+}
+
+// The factored diagonal blocks from Ld into R's diagonal blocks (lower part), one workgroup
+// per block.
+__global__ __launch_bounds__(256) void diag_store_kernel(float* __restrict__ R, int K, const float* __restrict__ Ld) {
+  const int64_t b0 = (int64_t)blockIdx.x * kB;
+  for (int e = threadIdx.x; e < kB * kB; e += 256) {
+    const int i = e / kB, j = e % kB;
+    if (j <= i) R[(b0 + i) * K + b0 + j] = Ld[b0 * kB + e];
+  }
 }
 
 // L[a][b] / L[b][b] for a > b: the error-feedback coefficients (in reversed indices).
@@ -231,18 +264,18 @@ __global__ __launch_bounds__(256) void colscale_kernel(float* __restrict__ R, in
 // thread reads it, then overwrites the same 32 floats with the residuals w_j - x_hat_j, which
 // the later feedback updates read from there.  Also writes the step's 16 packed bytes.
 template <bool SYM>
-__global__ __launch_bounds__(256) void sweep_block_kernel(const uint16_t* __restrict__ W, int64_t N, int K, int g,
+__global__ __launch_bounds__(kSweepThreads) void sweep_block_kernel(const uint16_t* __restrict__ W, int64_t N, int K, int g,
                                                           const float* __restrict__ Lc, float* __restrict__ acc,
                                                           int i1, const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
                                                           uint8_t* __restrict__ packed) {
   __shared__ float Cb[kB][kB + 1];
-  for (int e = threadIdx.x; e < kB * kB; e += 256) {
+  for (int e = threadIdx.x; e < kB * kB; e += kSweepThreads) {
     const int j = e / kB, i = e % kB;
     Cb[j][i] = j < i ? Lc[(int64_t)(K - 1 - i1 - j) * K + (K - 1 - i1 - i)] : 0.0f;
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)blockIdx.x * kSweepThreads + threadIdx.x;
   if (n >= N) return;
   const int G = K / g;
   const int grp = i1 / g;
@@ -308,7 +341,8 @@ GptqLayout gptq_layout(int64_t N, int64_t K) {
   auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
   L.R = 0;
   L.acc = up(L.R + 4 * K * K);
-  L.bytes = up(L.acc + 4 * N * K);
+  L.Ld = up(L.acc + 4 * N * K);
+  L.bytes = up(L.Ld + 4 * K * kB);
   return L;
 }
 
@@ -319,6 +353,7 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   char* base = static_cast<char*>(workspace);
   float* R = reinterpret_cast<float*>(base + L.R);
   float* acc = reinterpret_cast<float*>(base + L.acc);
+  float* Ld = reinterpret_cast<float*>(base + L.Ld);
   const int Ki = (int)K;
   const uint16_t* Xh = static_cast<const uint16_t*>(X);
 
@@ -342,10 +377,12 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   for (int o1 = 0; o1 < Ki; o1 += kOuter) {
     const int o2 = o1 + kOuter < Ki ? o1 + kOuter : Ki;
     for (int k0 = o1; k0 < o2; k0 += kB) {
-      hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(64), 0, stream, R, Ki, k0, info);
       const int rest = Ki - k0 - kB;
+      hipLaunchKernelGGL(panel_kernel, dim3(rest > 0 ? (unsigned)((rest + 255) / 256) : 1u), dim3(256), 0, stream, R,
+                         Ki, k0, Ld, info);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
       if (rest <= 0) continue;
-      hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0, stream, R, Ki, k0);
       const int cols = o2 - k0 - kB;                       // the outer block's columns still to factor
       if (cols > 0) {
         float* P = R + (int64_t)(k0 + kB) * K + k0;        // the panel, rest x 32
@@ -362,6 +399,9 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
       if (e != hipSuccess) return e;
     }
   }
+  hipLaunchKernelGGL(diag_store_kernel, dim3((unsigned)(K / kB)), dim3(256), 0, stream, R, Ki, Ld);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(colscale_kernel, dim3((unsigned)((K + 255) / 256 < 64 ? (K + 255) / 256 : 64), (unsigned)K),
                      dim3(256), 0, stream, R, Ki);
   e = hipGetLastError();
@@ -373,18 +413,18 @@ hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64
   //    the residuals D_j sit in acc[:, j] once column j is quantized; the first update to reach
   //    a column writes it (beta = 0), later ones add.  The updates read residual columns
   //    [s1, s2) and write columns >= s2 (or the step's later columns), never the same ones.
-  const unsigned rows_grid = (unsigned)((N + 255) / 256);
+  const unsigned rows_grid = (unsigned)((N + kSweepThreads - 1) / kSweepThreads);
   auto coef = [&](int j0, int i0) { return R + (int64_t)(Ki - 1 - j0) * K + (Ki - 1 - i0); };
   for (int s1 = 0; s1 < Ki; s1 += kOuter) {
     const int s2 = s1 + kOuter < Ki ? s1 + kOuter : Ki;
     for (int i1 = s1; i1 < s2; i1 += kB) {
       if (sym)
-        hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL(sweep_block_kernel<true>, dim3(rows_grid), dim3(kSweepThreads), 0, stream,
                            static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
                            static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
                            static_cast<uint8_t*>(packed));
       else
-        hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL(sweep_block_kernel<false>, dim3(rows_grid), dim3(kSweepThreads), 0, stream,
                            static_cast<const uint16_t*>(W), N, Ki, g, R, acc, i1,
                            static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
                            static_cast<uint8_t*>(packed));

@@ -41,11 +41,11 @@ hipError_t launch_quantize8(const void* W, int64_t N, int64_t K, int g, bool sym
                             void* scales, void* zeros, int num_cus, hipStream_t stream);
 // GPTQ (group parameters fixed up front, Cholesky of the reversed Hessian, blocked
 // error-feedback sweep).  Workspace layout: R [K, K] fp32, then the accumulated feedback
-// [N, K] fp32 (a column's residual replaces its feedback once the column is quantized), each
-// 256-byte aligned.
+// [N, K] fp32 (a column's residual replaces its feedback once the column is quantized), then
+// the factored 32 x 32 diagonal blocks [K / 32, 32, 32] fp32, each 256-byte aligned.
 constexpr int64_t kGptqMaxK = 32768;
 struct GptqLayout {
-  int64_t R, acc, bytes;
+  int64_t R, acc, Ld, bytes;
 };
 GptqLayout gptq_layout(int64_t N, int64_t K);
 hipError_t launch_gptq(const void* X, int64_t M, const void* W, int64_t N, int64_t K, int g, bool sym, float damp,
