@@ -61,8 +61,9 @@ __device__ __forceinline__ float ld_f32<uint16_t>(const uint16_t* p, int64_t i) 
 // C[m * ldc + n] = alpha * sum_k A(m, k) B(k, n) + beta * C, A(m, k) = A[m sam + k sak],
 // B(k, n) = B[k sbk + n sbn], on the fp32 matrix cores (each product exact, fp32 sums).
 // tri: only tiles with tile row >= tile column (lower part).  beta == 0 writes C without
-// reading it.
-template <typename TA, typename TB>
+// reading it.  PREC loads C before the k loop instead of after it, so that for a short inner
+// dimension its latency overlaps the operand loads (it holds 16 more registers per thread).
+template <typename TA, typename TB, bool PREC>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A, int64_t sam, int64_t sak,
                                                        const TB* __restrict__ B, int64_t sbk, int64_t sbn,
                                                        float* __restrict__ C, int64_t ldc, int M, int N, int Kd,
@@ -80,6 +81,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float cpre[2][2][4];
+  if constexpr (PREC) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+          cpre[i][j][r] = (beta != 0.0f && m < M && n < N) ? C[(int64_t)m * ldc + n] : 0.0f;
+        }
+      }
+  }
   // Register prefetch: the global values of step k0 + kStep are loaded while step k0 is
   // multiplied from LDS, so their latency overlaps the matrix instructions.
   float pa[4], pb[4];
@@ -133,7 +148,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
         const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
         if (m >= M || n >= N) continue;
         float* c = C + (int64_t)m * ldc + n;
-        *c = beta == 0.0f ? alpha * acc[i][j][r] : __builtin_fmaf(alpha, acc[i][j][r], beta * *c);
+        if (beta == 0.0f)
+          *c = alpha * acc[i][j][r];
+        else
+          *c = __builtin_fmaf(alpha, acc[i][j][r], beta * (PREC ? cpre[i][j][r] : *c));
       }
     }
 }
@@ -329,8 +347,12 @@ hipError_t gemm(const TA* A, int64_t sam, int64_t sak, const TB* B, int64_t sbk,
                 int64_t ldc, int M, int N, int Kd, float alpha, float beta, bool tri, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((M + kTile - 1) / kTile));
-  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, C, ldc, M, N, Kd,
-                     alpha, beta, tri ? 1 : 0);
+  if (beta != 0.0f && Kd <= 2 * kStep)
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, true>), grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, C, ldc, M,
+                       N, Kd, alpha, beta, tri ? 1 : 0);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, false>), grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, C, ldc,
+                       M, N, Kd, alpha, beta, tri ? 1 : 0);
   return hipGetLastError();
 }
 
