@@ -188,11 +188,13 @@ __global__ __launch_bounds__(1024) void damp_kernel(float* __restrict__ R, int K
 //    a non-positive pivot as info = column + 1 (first failure only).  Such a pivot is replaced
 //    by 1e-30 so the factorisation completes.
 //  * The rows below: one thread per row r >= k0 + 32 solves L[r, k0:k0+32] = R[r, k0:k0+32]
-//    L_kk^-T by forward substitution.  The row is loaded before the factorisation so its
-//    latency overlaps that work.
+//    L_kk^-T by forward substitution, multiplying by the reciprocals of the diagonal (taken
+//    once per workgroup) so no division sits on the chain.  The row is loaded before the
+//    factorisation so its latency overlaps that work.
 __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ R, int K, int k0, float* __restrict__ Ld,
                                                     int* __restrict__ info) {
   __shared__ float l[kB][kB + 1];
+  __shared__ float linv[kB];
   const int64_t r = (int64_t)k0 + kB + (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool has_row = r < K;
   float x[kB];
@@ -225,14 +227,15 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ R, int K
       d = sqrtf(d);
       a[j] = i == j ? d : (i > j ? a[j] / d : a[j]);
 #pragma unroll
-      for (int k = j + 1; k < kB; ++k) {
+      for (int k = j + 1; k < kB; ++k) {     // entries above the diagonal (k > i) are never used
         const float lkj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), k));
-        if (i >= k) a[k] = __builtin_fmaf(-a[j], lkj, a[k]);
+        a[k] = __builtin_fmaf(-a[j], lkj, a[k]);
       }
     }
     if (own) {
 #pragma unroll
       for (int j = 0; j < kB; ++j) l[i][j] = j <= i ? a[j] : 0.0f;
+      linv[i] = 1.0f / a[i];
     }
     if (blockIdx.x == 0) {
       if (own) {
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ R, int K
     float v = x[j];
 #pragma unroll
     for (int t = 0; t < j; ++t) v = __builtin_fmaf(-x[t], l[j][t], v);
-    x[j] = v / l[j][j];
+    x[j] = v * linv[j];
   }
   float4* wp = reinterpret_cast<float4*>(R + r * K + k0);
 #pragma unroll
