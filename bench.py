@@ -9,7 +9,8 @@ One step is one pass of the whole path over synthetic inputs resident in HBM:
   3. prefill   -- W4A16 GEMM, M = 2048, W[8192, 8192] (asym, g=128 and g=32)
 The headline value is the decode GEMV's HBM throughput: algorithmic bytes (packed codes +
 fp16 scales + uint8 zeros + X + Y) per launch / measured launch time, HIP events on the
-launch stream.  The CPU-baseline leg times the oracle on a bounded sample and asserts parity of
+launch stream.  The K timed passes run phase-major (all K quantizes, then the K x L decode
+GEMVs, then the prefill GEMMs), each phase between one pair of events.  The CPU-baseline leg times the oracle on a bounded sample and asserts parity of
 sampled GPU outputs against it before timing (both skipped with --no-cpu-baseline).
 Also reported: the W8A16 path (8-bit codes), the AWQ-style scaling search, and practical
 ceilings (a plain streaming read, a device copy, the vendor bf16 GEMM) as context.
@@ -770,17 +771,35 @@ def main(argv=None):
         copy_dst.copy_(copy_src)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    # The timed region runs the same K passes of the path phase-major: every phase's launches go
+    # back to back between one pair of events, as a decode loop runs its layers.  (An event pair
+    # between individual launches costs a few microseconds of its own on this stack, which would
+    # be charged to the 22-us GEMV.)
+    K_ = args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for t in range(args.steps):
-        step(args.warmup + t, evs[t])
+    evs[0].record()
+    for t in range(K_):
+        q4.quantize_rtn_into(W4, g4, "asym", *sets[(args.warmup + t) % L])
+    evs[1].record()
+    for t in range(K_):
+        for i in range(L):
+            p, s, z = sets[(args.warmup + t + 1 + i) % L]
+            q4.matmul_into(X4, p, s, z, g4, "asym", Y4)
+    evs[2].record()
+    for t in range(K_):
+        q4.matmul_into(X5, *w5[128], 128, "asym", Y5)
+    evs[3].record()
+    for t in range(K_):
+        q4.matmul_into(X5, *w5[32], 32, "asym", Y5)
+    evs[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     note(f"{args.steps} timed steps done")
 
     def mean_ms(i, j):
-        return sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs)
+        return evs[i].elapsed_time(evs[j]) / K_
 
     q_ms = mean_ms(0, 1)
     gemv_ms = mean_ms(1, 2) / L
