@@ -270,8 +270,8 @@ int q4_select_kernel_w8(int64_t M, int64_t N, int64_t K, int32_t g);
  * GPTQ: quantization that compensates each column's rounding error in the columns not yet
  * quantized, through the inverse Hessian of the layer's calibration inputs.
  * Source: "LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
- * "GPTQ vs AWQ: two ways to choose what error to keep" (table and toy); the overview page,
- * §2.1 (column-by-column quantization with a Cholesky factorisation of the inverse Hessian);
+ * "GPTQ vs AWQ: two ways to choose what error to keep" (table and toy); "Model Quantization",
+ * §2.1 "GPTQ" (column-by-column quantization with a Cholesky factorisation of the inverse Hessian);
  * "DL S067 · Quantization", §4 "GPTQ intuition" (the update rule).  Rules this library fixes:
  *   - H = X^T X in fp32 over the M calibration rows, plus damp * mean(diag H) on the diagonal
  *     (damp = 0.01 in the pages' toy); an all-zero X gives H = I, i.e. plain RTN;

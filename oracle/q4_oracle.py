@@ -59,7 +59,7 @@ R10 W8A16 (the INT8 weight-only format of "LLM Weight Quantization ...", "Granul
     fp16 scale, one code per byte (symmetric codes as int8 two's complement); g = K is the
     per-channel case.  [-127, 127] and [-128, 127] give the same symmetric codes, since
     |x| / s <= 127 / (1 - 2^-11) < 127.5.
-R11 GPTQ ("LLM Weight Quantization ...", "GPTQ vs AWQ" table and toy; overview page §2.1;
+R11 GPTQ ("LLM Weight Quantization ...", "GPTQ vs AWQ" table and toy; "Model Quantization" §2.1 "GPTQ";
     "DL S067" §4 "GPTQ intuition"): H = X^T X over the calibration rows (the factor 2 of
     "DL S067" cancels in every update), dampened by damp * mean(diag H) on the diagonal with
     damp = 0.01 as in the toy; columns are quantized in order and each column's error,
@@ -71,8 +71,8 @@ R11 GPTQ ("LLM Weight Quantization ...", "GPTQ vs AWQ" table and toy; overview p
     code of a compensated weight w' is clamp(rint(fl32(fl32(w') / scale)) + z): the same fp32
     decision as RTN.  The row updates use the upper Cholesky factor U of H^-1 (U^T U = H^-1),
     whose row i is the current inverse's row i divided by the square root of its diagonal
-    entry (the overview page's "Cholesky decomposition of the inverse Hessian"); the toy's
-    explicit downdates give the same updates.  An all-zero calibration set (mean diag H = 0)
+    entry ("Model Quantization" §2.1: a Cholesky decomposition of the inverse Hessian); the
+    toy's route (gptq_toy, closed-form solves on the trailing block of H) gives the same updates.  An all-zero calibration set (mean diag H = 0)
     carries no information: H = I, and GPTQ reduces to RTN.
 """
 from __future__ import annotations
@@ -82,7 +82,8 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f32", "quantize_groups", "quantize_rtn_ref", "unpack_codes_ref",
     "dequantize_ref", "round_to_bf16_bits_ref", "dequantize_rounded_ref", "matmul_ref",
-    "f32_to_bf16_bits_ref", "awq_search", "channel_absmean_ref", "awq_scales_ref",
+    "f32_to_bf16_bits_ref", "awq_alpha_grid", "awq_toy", "channel_absmean_ref", "awq_scale_rule",
+    "awq_scales_ref",
     "scale_columns_ref", "quantize_rtn_scaled_ref", "awq_search_ref",
     "quantize8_rtn_ref", "codes8_ref", "dequantize8_ref", "matmul8_ref", "matmul_entries_ref", "tol_ref", "check_matmul",
     "gptq_toy", "gptq_hessian_ref", "gptq_ref", "pack_codes_ref",
@@ -340,28 +341,32 @@ def matmul8_ref(X_bits, codes, scales, zeros, g: int, mode: str):
 
 
 # --------------------------------------------------------------------------- AWQ-style scaling
-def awq_search(W, X, qdq, alphas=np.linspace(0, 1, 11)):
-    """Activation-aware scaling search of the pages' toy (R9), in fp64, for any quantizer.
+def awq_alpha_grid(n_alpha: int) -> list:
+    """The search grid of R9: alpha_i = i / (n_alpha - 1), i = 0 .. n_alpha - 1 (0 alone when
+    n_alpha = 1); 11 points give the toy's grid 0, 0.1, ..., 1."""
+    if n_alpha < 1:
+        raise ValueError("n_alpha >= 1")
+    return [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]
 
-    W [rows, d], X [m, d] calibration activations, qdq(Ws) -> quantized-dequantized Ws.
-    For each alpha: s = a^alpha with a_j = mean |X[:, j]|, normalised by sqrt(max s min s);
-    Q = qdq(W * s) / s (the 1/s folded back); error = ||X W^T - X Q^T||.  Returns
-    (Q of the best alpha, best alpha, errors per alpha); the first smallest error wins.
+
+def awq_toy(W, X, qdq, n_alpha: int = 11):
+    """Activation-aware scaling of the pages' toy (R9) in fp64, for any quantizer.
+
+    W [rows, d] weights, X [m, d] calibration activations, qdq(Ws) -> the quantized then
+    dequantized Ws.  Every alpha of the grid is scored: the channel scales come from the same
+    rule as the library-format search (awq_scale_rule on the mean |x| of each channel), the
+    candidate weights are qdq(W s) with 1/s folded back onto them, and the score is the
+    calibration output error ||X W^T - X Q^T||.  The first alpha with the smallest score wins.
+    Returns (Q of the winner, its alpha, the scores).
     """
     W = np.asarray(W, dtype=np.float64)
     X = np.asarray(X, dtype=np.float64)
-    a_mag = np.abs(X).mean(axis=0)
-    Y = X @ W.T
-    best, errs = None, []
-    for a in alphas:
-        s = a_mag ** a
-        s = s / np.sqrt(s.max() * s.min())
-        Q = qdq(W * s) / s
-        err = np.linalg.norm(Y - X @ Q.T)
-        errs.append(err)
-        if best is None or err < best[0]:
-            best = (err, float(a), Q)
-    return best[2], best[1], np.array(errs)
+    grid = awq_alpha_grid(n_alpha)
+    a = np.abs(X).mean(axis=0)
+    cands = [qdq(W * s) / s for s in (awq_scale_rule(a, al) for al in grid)]
+    scores = np.array([np.linalg.norm(X @ (W - Q).T) for Q in cands])
+    k = int(np.argmin(scores))                                 # first smallest
+    return cands[k], grid[k], scores
 
 
 def f32_to_bf16_bits_ref(x32) -> np.ndarray:
@@ -384,17 +389,22 @@ def channel_absmean_ref(X_bits) -> np.ndarray:
 AWQ_FLOOR = 2.0 ** -20
 
 
-def awq_scales_ref(a, alpha: float) -> np.ndarray:
-    """s = a^alpha / sqrt(max(a^alpha) min(a^alpha)) with a floored at 2^-20 max(a) (R9), in
-    fp64, rounded to fp32."""
+def awq_scale_rule(a, alpha: float) -> np.ndarray:
+    """fp64 channel scales of R9: a floored at 2^-20 max(a), raised to alpha and divided by the
+    geometric mean of the largest and smallest, sqrt(max(a^alpha) min(a^alpha)), so the scales
+    sit around 1 ("DL S067" §5 "AWQ intuition": weight columns of salient channels scaled up,
+    activations down).  An all-zero a gives 1 everywhere."""
     a = np.asarray(a, dtype=np.float64)
     amax = a.max()
     if amax == 0.0:
-        return np.ones(a.shape, np.float32)
-    a = np.maximum(a, AWQ_FLOOR * amax)
-    s = a ** alpha
-    s = s / np.sqrt(s.max() * s.min())
-    return s.astype(np.float32)
+        return np.ones(a.shape, np.float64)
+    p = np.maximum(a, AWQ_FLOOR * amax) ** alpha
+    return p / np.sqrt(p.max() * p.min())
+
+
+def awq_scales_ref(a, alpha: float) -> np.ndarray:
+    """The library's channel scales: awq_scale_rule rounded to fp32 (R9)."""
+    return awq_scale_rule(a, alpha).astype(np.float32)
 
 
 def scale_columns_ref(A_bits, s32, op: str) -> np.ndarray:
@@ -426,11 +436,9 @@ def awq_search_ref(W_bits, X_bits, Yref_bits, g: int = 128, mode: str = "asym", 
     index (first smallest error), alphas, errors, the scales of every alpha (fp32) and the
     best alpha's packed / scales / zeros.
     """
-    if n_alpha < 1:
-        raise ValueError("n_alpha >= 1")
     a = channel_absmean_ref(X_bits)
     Yref = bf16_bits_to_f32(Yref_bits).astype(np.float64)
-    alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]
+    alphas = awq_alpha_grid(n_alpha)
     errs, svals, quants = [], [], []
     for al in alphas:
         s = awq_scales_ref(a, al)
@@ -446,29 +454,31 @@ def awq_search_ref(W_bits, X_bits, Yref_bits, g: int = 128, mode: str = "asym", 
 
 
 # --------------------------------------------------------------------------- GPTQ
-def gptq_toy(W, X, quant, damp=0.01):
-    """The pages' toy GPTQ (R11), in fp64, for any per-element quantizer.
+def gptq_toy(W, X, quant_col, damp=0.01):
+    """GPTQ of the pages' toy (R11) in fp64, for any column quantizer.
 
-    W [rows, d], X [m, d] calibration activations; quant(r, i, v) -> the quantized-dequantized
-    value of v in column i of row r (its scale fixed up front by the caller).  H = X^T X plus
-    damp * mean(diag H) on the diagonal; for each row, from the full inverse: quantize column i,
-    err = (w_i - Q_i) / Hinv[i, i], w[i+1:] -= err * Hinv[i, i+1:], then drop column i from the
-    inverse: Hinv -= Hinv[:, i] Hinv[i, :] / Hinv[i, i].  Returns Q [rows, d].
+    W [rows, d] weights, X [m, d] calibration activations, quant_col(i, v) -> the quantized then
+    dequantized values v of column i (one per row, scales fixed up front by the caller).
+    H = X^T X with damp * mean(diag H) added to its diagonal.  Columns are fixed in order.
+    Once column i is fixed with rounding error e = w_i - q_i, the columns F = i+1 .. d-1 not
+    yet fixed move by the minimiser of the calibration output error ||X delta||^2 =
+    delta^T H delta under delta_i = -e ("DL S067" §4 "GPTQ intuition"): setting the gradient
+    in delta_F to zero gives H_FF delta_F = e H_Fi, so w_F += e * solve(H_FF, H_Fi).  By the
+    block-inverse identity this is the pages' update through the inverse Hessian of the
+    columns i.. (its row i divided by its diagonal entry equals -H_iF H_FF^-1).  The solve
+    vectors depend only on H, so every row moves at once.  Returns Q [rows, d].
     """
-    W = np.asarray(W, dtype=np.float64)
+    w = np.array(W, dtype=np.float64)                # compensated in place
     X = np.asarray(X, dtype=np.float64)
-    d = W.shape[1]
     H = X.T @ X
-    H = H + damp * np.mean(np.diag(H)) * np.eye(d)
-    Q = np.zeros_like(W)
-    for r in range(W.shape[0]):
-        w = W[r].copy()
-        Hinv = np.linalg.inv(H)
-        for i in range(d):
-            Q[r, i] = quant(r, i, w[i])
-            err = (w[i] - Q[r, i]) / Hinv[i, i]
-            w[i + 1:] -= err * Hinv[i, i + 1:]
-            Hinv = Hinv - np.outer(Hinv[:, i], Hinv[i, :]) / Hinv[i, i]
+    H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))
+    d = w.shape[1]
+    Q = np.empty_like(w)
+    for i in range(d):
+        Q[:, i] = quant_col(i, w[:, i])
+        if i + 1 < d:
+            v = np.linalg.solve(H[i + 1:, i + 1:], H[i + 1:, i])
+            w[:, i + 1:] += np.outer(w[:, i] - Q[:, i], v)
     return Q
 
 

@@ -34,7 +34,7 @@ def toy_data():
 def toy_awq(o):
     """(alpha, held-out relative output error) of the toy's AWQ with oracle module o."""
     W, xcal, xtest = toy_data()
-    Q, alpha, _ = o.awq_search(W, xcal, lambda w: _qdq_sym(w, 3, (W.shape[0], 1, W.shape[1])))
+    Q, alpha, _ = o.awq_toy(W, xcal, lambda w: _qdq_sym(w, 3, (W.shape[0], 1, W.shape[1])))
     err = np.linalg.norm(xtest @ W.T - xtest @ Q.T) / np.linalg.norm(xtest @ W.T)
     return alpha, err
 
@@ -153,10 +153,48 @@ def test_awq_search_beats_rtn_on_salient_channels(mode):
     assert np.array_equal(r["absmean"], np.abs(orc.bf16_bits_to_f32(X_bits).astype(np.float64)).mean(axis=0))
 
 
+@pytest.mark.parametrize("mode,g,seed", [("asym", 128, 6), ("sym", 32, 9), ("asym", 64, 11)])
+def test_awq_search_ref_picks_the_toy_search_alpha(mode, g, seed):
+    """The library-format search (fp32 scales, bf16(W s) and bf16(X / s), squared error against
+    a bf16 reference) and the toy's search (fp64, 1/s folded onto the weights, exact products)
+    run with the library's group quantizer pick the same alpha on layers with salient
+    channels."""
+    W_bits, X_bits, Yref_bits = _salient_layer(seed=seed)
+    r = orc.awq_search_ref(W_bits, X_bits, Yref_bits, g, mode, n_alpha=11)
+
+    def qdq(ws):
+        q = orc.quantize_rtn_ref(f64_to_bf16_bits(ws), g, mode)
+        return orc.dequantize_ref(*q, g, mode)
+
+    W = orc.bf16_bits_to_f32(W_bits).astype(np.float64)
+    X = orc.bf16_bits_to_f32(X_bits).astype(np.float64)
+    _, alpha, scores = orc.awq_toy(W, X, qdq)
+    assert r["best"] > 0
+    assert r["alphas"][r["best"]] == alpha
+    # the two scorings agree on the shape of the curve, not only on its minimum
+    ratio = np.sqrt(r["errors"]) / scores
+    assert ratio.max() / ratio.min() < 1.2
+
+
+def test_awq_toy_equal_channels_first_alpha_wins():
+    """Channels of equal mean magnitude give s = 1 for every alpha, so every candidate scores the
+    same and the first alpha of the grid (0) must win."""
+    rng = np.random.default_rng(12)
+    X = rng.choice([-1.0, 1.0], size=(40, 64))
+    W = rng.normal(0, 0.05, (8, 64))
+    _, alpha, scores = orc.awq_toy(W, X, lambda w: _qdq_sym(w, 3, (8, 1, 64)))
+    assert np.all(scores == scores[0]) and alpha == 0.0
+
+
 def awq_pins_hold(o) -> bool:
     """The pins above in compact form (used by the mutation tests)."""
     alpha, err = toy_awq(o)
     if round(alpha, 1) != 0.3 or round(err, 4) != 0.2128:
+        return False
+    rng = np.random.default_rng(12)
+    Xe = rng.choice([-1.0, 1.0], size=(40, 64))
+    We = rng.normal(0, 0.05, (8, 64))
+    if o.awq_toy(We, Xe, lambda w: _qdq_sym(w, 3, (8, 1, 64)))[1] != 0.0:
         return False
     rng = np.random.default_rng(4)
     a = np.abs(rng.standard_normal(512)) + 0.01
@@ -168,4 +206,13 @@ def awq_pins_hold(o) -> bool:
         return False
     W_bits, X_bits, Yref_bits = _salient_layer()
     r = o.awq_search_ref(W_bits, X_bits, Yref_bits, 128, "asym", n_alpha=11)
-    return r["alphas"][-1] == 1.0 and 0 < r["best"] and r["errors"][r["best"]] < 0.9 * r["errors"][0]
+    if not (r["alphas"][-1] == 1.0 and 0 < r["best"] and r["errors"][r["best"]] < 0.9 * r["errors"][0]):
+        return False
+
+    def qdq(ws):
+        q = o.quantize_rtn_ref(f64_to_bf16_bits(ws), 128, "asym")
+        return o.dequantize_ref(*q, 128, "asym")
+
+    _, alpha, _ = o.awq_toy(o.bf16_bits_to_f32(W_bits).astype(np.float64),
+                            o.bf16_bits_to_f32(X_bits).astype(np.float64), qdq)
+    return r["alphas"][r["best"]] == alpha

@@ -1,8 +1,8 @@
 """Pins of the oracle's GPTQ (reading R11 of the oracle), CPU only.
 
 * The pages' toy: the printed GPTQ output error and weight-space error.
-* The library-format gptq_ref (Cholesky factor of H^-1) against the toy's own route (explicit
-  inverse and downdates) with the library's group quantizer: identical codes.
+* The library-format gptq_ref (Cholesky factor of H^-1) against the toy's route (closed-form
+  updates on the trailing block of H) with the library's group quantizer: identical codes.
 * Against an independent algebraic form written here: with H = Ut Ut^T (Ut upper triangular,
   the Cholesky factorisation of H in reversed order), the compensated weight of column i is
   w_i + sum_{j<i} (w_j - x_hat_j) Ut[j, i] / Ut[i, i] with the ORIGINAL w_j: identical codes.
@@ -27,8 +27,8 @@ def toy_gptq(o):
     """(held-out output error, weight error, RTN weight error) of the toy with oracle module o."""
     W, xcal, xtest = toy_data()
     scales = np.abs(W).max(axis=1) / QMAX3
-    quant = lambda r, i, v: np.clip(np.round(v / scales[r]), -QMAX3 - 1, QMAX3) * scales[r]
-    Q = o.gptq_toy(W, xcal, quant)
+    quant_col = lambda i, v: np.clip(np.round(v / scales), -QMAX3 - 1, QMAX3) * scales
+    Q = o.gptq_toy(W, xcal, quant_col)
     out = np.linalg.norm(xtest @ W.T - xtest @ Q.T) / np.linalg.norm(xtest @ W.T)
     Q_rtn = np.clip(np.round(W / scales[:, None]), -QMAX3 - 1, QMAX3) * scales[:, None]
     return out, np.linalg.norm(W - Q) / np.linalg.norm(W), np.linalg.norm(W - Q_rtn) / np.linalg.norm(W)
@@ -56,21 +56,21 @@ def _code(v32, s32, z, mode):
 
 
 def toy_route_codes(o, W_bits, X_bits, g, mode):
-    """Codes of o.gptq_toy (explicit downdates) with the library's group quantizer."""
+    """Codes of o.gptq_toy (closed-form updates on the trailing block of H) with the library's
+    group quantizer."""
     s32, z = _group_params(W_bits, g, mode)
-    codes = {}
-
-    def quant(r, i, v):
-        G = i // g
-        c = _code(np.float32(v), s32[r, G], z[r, G], mode)
-        codes[(r, i)] = c
-        return float(s32[r, G]) * (c - z[r, G])
-
     X = bf16_bits_to_f32(X_bits).astype(np.float64)
     W = bf16_bits_to_f32(W_bits).astype(np.float64)
-    o.gptq_toy(W, X, quant)
     N, K = W.shape
-    return np.array([[codes[(r, i)] for i in range(K)] for r in range(N)])
+    codes = np.empty((N, K), dtype=np.int64)
+
+    def quant_col(i, v):
+        G = i // g
+        codes[:, i] = [_code(np.float32(v[r]), s32[r, G], z[r, G], mode) for r in range(N)]
+        return s32[:, G].astype(np.float64) * (codes[:, i] - z[:, G])
+
+    o.gptq_toy(W, X, quant_col)
+    return codes
 
 
 def feedback_form_codes(W_bits, X_bits, g, mode, damp=0.01):

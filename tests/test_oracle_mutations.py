@@ -32,16 +32,18 @@ MUTATIONS = {
     "bf16 ties away from zero": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m))"),
     "bf16 7 significant bits": ("np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)", "np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)"),
     "bf16 truncation": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
-    "AWQ magnitude is the max": ("a_mag = np.abs(X).mean(axis=0)", "a_mag = np.abs(X).max(axis=0)"),
-    "AWQ 1/s not folded back": ("        Q = qdq(W * s) / s\n", "        Q = qdq(W * s)\n"),
-    "AWQ scored on weight error": ("err = np.linalg.norm(Y - X @ Q.T)", "err = np.linalg.norm(W - Q)"),
-    "AWQ scales not normalised": ("    s = s / np.sqrt(s.max() * s.min())\n    return s.astype(np.float32)", "    return s.astype(np.float32)"),
-    "AWQ grid misses alpha 1": ("alphas = [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]", "alphas = [i / n_alpha for i in range(n_alpha)]"),
+    "AWQ magnitude is the max": ("    a = np.abs(X).mean(axis=0)\n    cands", "    a = np.abs(X).max(axis=0)\n    cands"),
+    "AWQ 1/s not folded back": ("cands = [qdq(W * s) / s for s", "cands = [qdq(W * s) for s"),
+    "AWQ scored on weight error": ("np.linalg.norm(X @ (W - Q).T)", "np.linalg.norm(W - Q)"),
+    "AWQ scales not normalised": ("    return p / np.sqrt(p.max() * p.min())", "    return p"),
+    "AWQ grid misses alpha 1": ("return [i / (n_alpha - 1) if n_alpha > 1 else 0.0 for i in range(n_alpha)]", "return [i / n_alpha for i in range(n_alpha)]"),
+    "AWQ last alpha wins ties": ("    k = int(np.argmin(scores))", "    k = len(scores) - 1 - int(np.argmin(scores[::-1]))"),
     "INT8 asym range 254": ('Q8_RANGE = {"asym": (0, 255), "sym": (-127, 127)}', 'Q8_RANGE = {"asym": (0, 254), "sym": (-127, 127)}'),
     "INT8 sym codes offset binary": ("return np.where(c >= 128, c - 256, c) if mode == \"sym\" else c", "return c - 128 if mode == \"sym\" else c"),
-    "GPTQ toy without damping": ("    H = H + damp * np.mean(np.diag(H)) * np.eye(d)\n    Q = np.zeros_like(W)", "    Q = np.zeros_like(W)"),
-    "GPTQ toy error not divided by the diagonal": ("err = (w[i] - Q[r, i]) / Hinv[i, i]", "err = (w[i] - Q[r, i])"),
-    "GPTQ toy inverse not downdated": ("            Hinv = Hinv - np.outer(Hinv[:, i], Hinv[i, :]) / Hinv[i, i]\n", ""),
+    "GPTQ toy without damping": ("    H[np.diag_indices_from(H)] += damp * np.mean(np.diag(H))\n    d = w.shape[1]", "    d = w.shape[1]"),
+    "GPTQ toy compensation sign": ("w[:, i + 1:] += np.outer(w[:, i] - Q[:, i], v)", "w[:, i + 1:] -= np.outer(w[:, i] - Q[:, i], v)"),
+    "GPTQ toy solves on all later rows of H": ("v = np.linalg.solve(H[i + 1:, i + 1:], H[i + 1:, i])", "v = np.linalg.lstsq(H[:, i + 1:], H[:, i], rcond=None)[0]"),
+    "GPTQ toy error from the original weight": ("w[:, i + 1:] += np.outer(w[:, i] - Q[:, i], v)", "w[:, i + 1:] += np.outer(W[:, i] - Q[:, i], v)"),
     "GPTQ Cholesky of H instead of its inverse": ("np.linalg.cholesky(np.linalg.inv(H)).T", "np.linalg.cholesky(H).T"),
     "GPTQ codes from the original weights": ("quot = w[:, i].astype(np.float32) / s32[:, G]", "quot = W32[:, i] / s32[:, G]"),
     "bf16 bit rounding truncates": ("(u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)", "u >> np.uint64(16)"),

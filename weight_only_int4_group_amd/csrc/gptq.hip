@@ -1,7 +1,7 @@
 // GPTQ quantization on the GPU (gfx950), in the library's INT4 group format.
 //
 // Method ("LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
-// "GPTQ vs AWQ: two ways to choose what error to keep"; overview page §2.1; "DL S067 ·
+// "GPTQ vs AWQ: two ways to choose what error to keep"; "Model Quantization" §2.1 "GPTQ"; "DL S067 ·
 // Quantization" §4 "GPTQ intuition"): H = X^T X over calibration rows, dampened on the
 // diagonal by damp * mean(diag H); the columns of each weight row are quantized in order and
 // each column's rounding error is pushed onto the columns not yet quantized through the
