@@ -320,3 +320,72 @@ def test_gptq_workspace_bytes():
 ])
 def test_gptq_validation(kw, status):
     assert _gptq(**kw) == status
+
+
+# ---------------------------------------------------------------- binding: shapes and dtypes
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _cases():
+    """(call, name of the argument that must be rejected) with host tensors: each call has
+    exactly one argument of the wrong dtype or shape, so the binding's host checks must name it
+    before anything reaches the library."""
+    import torch
+    bf, f16, u8, f32, f64, i32 = torch.bfloat16, torch.float16, torch.uint8, torch.float32, torch.float64, torch.int32
+    N, K, g, M = 8, 256, 64, 3
+    G = K // g
+    W, X, Y = _t((N, K), bf), _t((M, K), bf), _t((M, N), bf)
+    p, s, z = _t((N, K // 2), u8), _t((N, G), f16), _t((N, G), u8)
+    c8 = _t((N, K), u8)
+    s32 = _t((K,), f32)
+    ws = _t((64,), u8)
+    yield lambda: q4.quantize_rtn_into(W, g, "asym", p, _t((N, G + 1), f16), z), "scales"
+    yield lambda: q4.quantize_rtn_into(W, g, "asym", p, s, _t((N, G), f16)), "zeros"
+    yield lambda: q4.quantize_rtn_into(W, g, "asym", _t((N, K), u8), s, z), "packed"
+    yield lambda: q4.quantize_rtn_into(W.float(), g, "asym", p, s, z), "W"
+    yield lambda: q4.matmul_into(X, p, _t((N, K // 32), f16), z, g, "asym", Y), "scales"   # scales of g=32 with g=64
+    yield lambda: q4.matmul_into(X, p, s, _t((N, G), i32), g, "asym", Y), "zeros"
+    yield lambda: q4.matmul_into(X, p, s, None, g, "asym", Y), "zeros"                   # asym needs zeros
+    yield lambda: q4.matmul_into(X, p, s, z, g, "asym", _t((M, N + 1), bf)), "Y"
+    yield lambda: q4.matmul_into(X, _t((N, K // 2 + 1), u8), s, z, g, "asym", Y), "packed"
+    yield lambda: q4.dequantize_into(p, _t((N, G), f32), z, g, "asym", _t((N, K), bf)), "scales"
+    yield lambda: q4.dequantize_into(p, s, z, g, "asym", _t((N, K - 2), bf)), "out"
+    yield lambda: q4.dequantize_into(p, s, z, g, "asym", _t((N, K), f32)), "out"
+    yield lambda: q4.quantize_rtn_scaled_into(W, _t((K + 8,), f32), g, "asym", p, s, z), "s"
+    yield lambda: q4.quantize_rtn_scaled_into(W, s32, g, "asym", p, s, _t((N - 1, G), u8)), "zeros"
+    yield lambda: q4.scale_columns_into(X, _t((K,), f16), "div", X), "s"
+    yield lambda: q4.scale_columns_into(X, s32, "div", _t((M + 1, K), bf)), "out"
+    yield lambda: q4.awq_search_into(X, Y, W, g, "asym", 5, ws, s32, p, s, z, _t((4,), f64), _t((1,), i32)), "errors"
+    yield lambda: q4.awq_search_into(X, Y, W, g, "asym", 5, ws, s32, p, s, z, _t((5,), f64), _t((1,), torch.int64)), "best"
+    yield lambda: q4.awq_search_into(X, Y, W, g, "asym", 5, ws, _t((K,), f64), p, s, z, _t((5,), f64), _t((1,), i32)), "s_out"
+    yield lambda: q4.awq_search_into(X, _t((M, N - 1), bf), W, g, "asym", 5, ws, s32, p, s, z, _t((5,), f64), _t((1,), i32)), "Yref"
+    yield lambda: q4.quantize_rtn8_into(W, g, "sym", p, s, z), "codes"
+    yield lambda: q4.matmul_w8_into(X, c8, _t((N, G - 1), f16), z, g, "sym", Y), "scales"
+    yield lambda: q4.matmul_w8_into(X, c8, s, z, g, "sym", _t((M, N), f16)), "Y"
+    yield lambda: q4.gptq_into(X, W, g, "asym", 0.01, ws, p, s, z, _t((2,), i32)), "info"
+    yield lambda: q4.gptq_into(X, W, g, "asym", 0.01, ws, p, _t((N, G), bf), z, _t((1,), i32)), "scales"
+
+
+@pytest.mark.parametrize("i", range(25))
+def test_binding_rejects_wrong_dtype_or_shape(i):
+    call, what = list(_cases())[i]
+    with pytest.raises(ValueError, match=rf"\b{what}\b"):
+        call()
+
+
+def test_binding_case_count():
+    assert len(list(_cases())) == 25
+
+
+def test_binding_rejects_host_tensors_of_the_right_form():
+    """All dtypes and shapes right, but the tensors live on the host: rejected by the device check."""
+    import torch
+    N, K, g = 8, 256, 64
+    W = _t((N, K), torch.bfloat16)
+    p, s, z = _t((N, K // 2), torch.uint8), _t((N, K // g), torch.float16), _t((N, K // g), torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        q4.quantize_rtn_into(W, g, "asym", p, s, z)
+    with pytest.raises(ValueError, match="GPU"):
+        q4.matmul_into(_t((2, K), torch.bfloat16), p, s, z, g, "asym", _t((2, N), torch.bfloat16))

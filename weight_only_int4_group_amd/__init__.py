@@ -114,30 +114,65 @@ def _mode(mode: str) -> int:
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
 
 
-def _stream(device):
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _need(t, dtype, shape, what: str) -> None:
+    """t must be a tensor of this dtype and shape (checked on the host before any launch: the C
+    ABI receives bare pointers and cannot see a buffer's extent)."""
+    if t is None or t.dtype != dtype or t.shape != shape:
+        got = "None" if t is None else f"{tuple(t.shape)} {t.dtype}"
+        raise ValueError(f"{what} must be a {dtype} tensor of shape {shape}, got {got}")
 
 
-def _check_cuda(*ts):
+def _on_gpu(what: str, *ts) -> None:
+    """Every tensor given (None skipped) is contiguous and on a GPU.  Checked after the dtypes and
+    shapes, so host tensors of the wrong form are rejected by those checks first."""
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("tensors must be contiguous and on the GPU")
+            raise ValueError(f"{what}: tensors must be contiguous and on the GPU, got one on {t.device}")
+
+
+def _groups(K: int, g: int):
+    """K / g when g splits K into whole groups, else None (the C ABI then rejects the call with
+    its group-size status before touching memory)."""
+    return K // g if g > 0 and K % g == 0 else None
+
+
+def _call(t, fn, *args):
+    """fn(*args, stream) on t's device, with the raw handle of that device's current stream."""
+    import torch
+    idx = t.get_device()
+    if idx == torch._C._cuda_getDevice():
+        return fn(*args, torch._C._cuda_getCurrentRawStream(idx))
+    with torch.cuda.device(idx):
+        return fn(*args, torch._C._cuda_getCurrentRawStream(idx))
+
+
+def _need_group_params(packed_or_codes, scales, zeros, N, G, mode, what):
+    import torch
+    if G is None:
+        return
+    _need(scales, torch.float16, (N, G), f"{what}: scales")
+    if mode == "asym" or zeros is not None:
+        _need(zeros, torch.uint8, (N, G), f"{what}: zeros")
 
 
 def quantize_rtn_into(W, g: int, mode: str, packed, scales, zeros) -> None:
     """q4_quantize_rtn on caller-provided outputs (no allocation)."""
     import torch
-    _check_cuda(W, packed, scales, zeros)
-    if W.dtype != torch.bfloat16 or W.dim() != 2:
+    if W is None or W.dim() != 2:
         raise ValueError("W must be a 2-D bfloat16 tensor")
     N, K = W.shape
-    with torch.cuda.device(W.device):
-        st = library().q4_quantize_rtn(_ptr(W), N, K, g, _mode(mode), _ptr(packed), _ptr(scales),
-                                       _ptr(zeros), _stream(W.device))
+    _need(W, torch.bfloat16, (N, K), "quantize_rtn: W")
+    _need(packed, torch.uint8, (N, K // 2), "quantize_rtn: packed")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "quantize_rtn: scales")
+        _need(zeros, torch.uint8, (N, G), "quantize_rtn: zeros")
+    _on_gpu("quantize_rtn", W, packed, scales, zeros)
+    st = _call(W, library().q4_quantize_rtn, W.data_ptr(), N, K, g, _mode(mode), packed.data_ptr(),
+               _ptr(scales), _ptr(zeros))
     if st != 0:
         raise Q4Error(st, "q4_quantize_rtn")
 
@@ -159,19 +194,19 @@ def quantize_rtn(W, g: int = 128, mode: str = "asym"):
 def matmul_into(X, packed, scales, zeros, g: int, mode: str, Y, kernel: str = "auto") -> None:
     """q4_matmul_kernel on a caller-provided Y (no allocation)."""
     import torch
-    _check_cuda(X, packed, scales, zeros, Y)
-    if X.dtype != torch.bfloat16 or X.dim() != 2 or Y.dtype != torch.bfloat16:
-        raise ValueError("X and Y must be 2-D bfloat16 tensors")
-    if kernel not in KERNELS:
-        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    if X is None or X.dim() != 2 or packed is None or packed.dim() != 2:
+        raise ValueError("X and packed must be 2-D tensors")
     M, K = X.shape
     N = packed.shape[0]
-    if packed.shape[1] * 2 != K or tuple(Y.shape) != (M, N):
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, packed {tuple(packed.shape)}, Y {tuple(Y.shape)}")
-    with torch.cuda.device(packed.device):
-        st = library().q4_matmul_kernel(_ptr(X), M, N, K, g, _mode(mode), _ptr(packed),
-                                        _ptr(scales), _ptr(zeros), _ptr(Y), KERNELS[kernel],
-                                        _stream(packed.device))
+    _need(X, torch.bfloat16, (M, K), "matmul: X")
+    _need(packed, torch.uint8, (N, K // 2), "matmul: packed")
+    _need(Y, torch.bfloat16, (M, N), "matmul: Y")
+    _need_group_params(packed, scales, zeros, N, _groups(K, g), mode, "matmul")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    _on_gpu("matmul", X, packed, scales, zeros, Y)
+    st = _call(packed, library().q4_matmul_kernel, X.data_ptr(), M, N, K, g, _mode(mode), packed.data_ptr(),
+               _ptr(scales), _ptr(zeros), Y.data_ptr(), KERNELS[kernel])
     if st != 0:
         raise Q4Error(st, "q4_matmul")
 
@@ -195,15 +230,18 @@ def _out_dtype(dtype) -> int:
 
 def dequantize_into(packed, scales, zeros, g: int, mode: str, out) -> None:
     """q4_dequantize on a caller-provided out[N, K] (bfloat16 or float16; no allocation)."""
-    _check_cuda(packed, scales, zeros, out)
-    if packed.dim() != 2:
+    if packed is None or packed.dim() != 2:
         raise ValueError("packed must be 2-D")
+    import torch
     N, K = packed.shape[0], packed.shape[1] * 2
-    if tuple(out.shape) != (N, K):
-        raise ValueError(f"shape mismatch: packed {tuple(packed.shape)}, out {tuple(out.shape)}")
-    with __import__("torch").cuda.device(packed.device):
-        st = library().q4_dequantize(N, K, g, _mode(mode), _ptr(packed), _ptr(scales), _ptr(zeros),
-                                     _ptr(out), _out_dtype(out.dtype), _stream(packed.device))
+    _need(packed, torch.uint8, (N, K // 2), "dequantize: packed")
+    if out is None or out.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("dequantize: out must be a bfloat16 or float16 tensor")
+    _need(out, out.dtype, (N, K), "dequantize: out")
+    _need_group_params(packed, scales, zeros, N, _groups(K, g), mode, "dequantize")
+    _on_gpu("dequantize", packed, scales, zeros, out)
+    st = _call(packed, library().q4_dequantize, N, K, g, _mode(mode), packed.data_ptr(), _ptr(scales),
+               _ptr(zeros), out.data_ptr(), _out_dtype(out.dtype))
     if st != 0:
         raise Q4Error(st, "q4_dequantize")
 
@@ -220,15 +258,19 @@ def dequantize(packed, scales, zeros, g: int = 128, mode: str = "asym", dtype=No
 def quantize_rtn_scaled_into(W, s, g: int, mode: str, packed, scales, zeros) -> None:
     """q4_quantize_rtn_scaled (RTN of bf16(W * s)) on caller-provided outputs."""
     import torch
-    _check_cuda(W, s, packed, scales, zeros)
-    if W.dtype != torch.bfloat16 or W.dim() != 2 or s.dtype != torch.float32 or s.dim() != 1:
-        raise ValueError("W must be a 2-D bfloat16 tensor and s a 1-D float32 tensor")
+    if W is None or W.dim() != 2:
+        raise ValueError("W must be a 2-D bfloat16 tensor")
     N, K = W.shape
-    if s.shape[0] != K:
-        raise ValueError(f"s has {s.shape[0]} entries, W has {K} columns")
-    with torch.cuda.device(W.device):
-        st = library().q4_quantize_rtn_scaled(_ptr(W), _ptr(s), N, K, g, _mode(mode), _ptr(packed),
-                                              _ptr(scales), _ptr(zeros), _stream(W.device))
+    _need(W, torch.bfloat16, (N, K), "quantize_rtn_scaled: W")
+    _need(s, torch.float32, (K,), "quantize_rtn_scaled: s")
+    _need(packed, torch.uint8, (N, K // 2), "quantize_rtn_scaled: packed")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "quantize_rtn_scaled: scales")
+        _need(zeros, torch.uint8, (N, G), "quantize_rtn_scaled: zeros")
+    _on_gpu("quantize_rtn_scaled", W, s, packed, scales, zeros)
+    st = _call(W, library().q4_quantize_rtn_scaled, W.data_ptr(), s.data_ptr(), N, K, g, _mode(mode),
+               packed.data_ptr(), _ptr(scales), _ptr(zeros))
     if st != 0:
         raise Q4Error(st, "q4_quantize_rtn_scaled")
 
@@ -248,17 +290,17 @@ def quantize_rtn_scaled(W, s, g: int = 128, mode: str = "asym"):
 def scale_columns_into(A, s, op: str, out) -> None:
     """q4_scale_columns: out = bf16(A * s) or bf16(A / s) per column (out may be A)."""
     import torch
-    _check_cuda(A, s, out)
-    if A.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or A.dim() != 2 or s.dtype != torch.float32:
-        raise ValueError("A and out must be 2-D bfloat16 tensors and s float32")
+    if A is None or A.dim() != 2:
+        raise ValueError("A must be a 2-D bfloat16 tensor")
+    rows, cols = A.shape
+    _need(A, torch.bfloat16, (rows, cols), "scale_columns: A")
+    _need(s, torch.float32, (cols,), "scale_columns: s")
+    _need(out, torch.bfloat16, (rows, cols), "scale_columns: out")
     if op not in SCALE_OPS:
         raise ValueError(f"op must be one of {sorted(SCALE_OPS)}")
-    rows, cols = A.shape
-    if tuple(out.shape) != (rows, cols) or s.shape != (cols,):
-        raise ValueError("shape mismatch between A, s and out")
-    with torch.cuda.device(A.device):
-        st = library().q4_scale_columns(_ptr(A), rows, cols, _ptr(s), SCALE_OPS[op], _ptr(out),
-                                        _stream(A.device))
+    _on_gpu("scale_columns", A, s, out)
+    st = _call(A, library().q4_scale_columns, A.data_ptr(), rows, cols, s.data_ptr(), SCALE_OPS[op],
+               out.data_ptr())
     if st != 0:
         raise Q4Error(st, "q4_scale_columns")
 
@@ -281,20 +323,28 @@ def awq_search_into(X, Yref, W, g: int, mode: str, n_alpha: int, workspace, s_ou
                     zeros, errors, best) -> None:
     """q4_awq_search on caller-provided workspace and outputs (no allocation)."""
     import torch
-    _check_cuda(X, Yref, W, workspace, s_out, packed, scales, zeros, errors, best)
-    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or Yref.dtype != torch.bfloat16:
-        raise ValueError("X, Yref and W must be bfloat16")
+    if X is None or X.dim() != 2 or W is None or W.dim() != 2:
+        raise ValueError("X and W must be 2-D bfloat16 tensors")
     M, K = X.shape
     N = W.shape[0]
-    if W.shape[1] != K or tuple(Yref.shape) != (M, N):
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, Yref {tuple(Yref.shape)}")
-    if errors.dtype != torch.float64 or best.dtype != torch.int32 or s_out.dtype != torch.float32:
-        raise ValueError("errors must be float64, best int32 and s_out float32")
-    with torch.cuda.device(W.device):
-        st = library().q4_awq_search(_ptr(X), M, _ptr(Yref), _ptr(W), N, K, g, _mode(mode), n_alpha,
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _ptr(s_out), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(errors),
-                                     _ptr(best), _stream(W.device))
+    _need(X, torch.bfloat16, (M, K), "awq_search: X")
+    _need(W, torch.bfloat16, (N, K), "awq_search: W")
+    _need(Yref, torch.bfloat16, (M, N), "awq_search: Yref")
+    if workspace is None:
+        raise ValueError("awq_search: workspace is required")
+    _need(s_out, torch.float32, (K,), "awq_search: s_out")
+    _need(packed, torch.uint8, (N, K // 2), "awq_search: packed")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "awq_search: scales")
+        _need(zeros, torch.uint8, (N, G), "awq_search: zeros")
+    if n_alpha >= 1:
+        _need(errors, torch.float64, (n_alpha,), "awq_search: errors")
+    _need(best, torch.int32, (1,), "awq_search: best")
+    _on_gpu("awq_search", X, Yref, W, workspace, s_out, packed, scales, zeros, errors, best)
+    st = _call(W, library().q4_awq_search, X.data_ptr(), M, Yref.data_ptr(), W.data_ptr(), N, K, g,
+               _mode(mode), n_alpha, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+               s_out.data_ptr(), packed.data_ptr(), _ptr(scales), _ptr(zeros), _ptr(errors), best.data_ptr())
     if st != 0:
         raise Q4Error(st, "q4_awq_search")
 
@@ -325,13 +375,18 @@ def awq_search(X, Yref, W, g: int = 128, mode: str = "asym", n_alpha: int = 11):
 def quantize_rtn8_into(W, g: int, mode: str, codes, scales, zeros) -> None:
     """q4_quantize_rtn8 (8-bit codes, W8A16) on caller-provided outputs (no allocation)."""
     import torch
-    _check_cuda(W, codes, scales, zeros)
-    if W.dtype != torch.bfloat16 or W.dim() != 2:
+    if W is None or W.dim() != 2:
         raise ValueError("W must be a 2-D bfloat16 tensor")
     N, K = W.shape
-    with torch.cuda.device(W.device):
-        st = library().q4_quantize_rtn8(_ptr(W), N, K, g, _mode(mode), _ptr(codes), _ptr(scales),
-                                        _ptr(zeros), _stream(W.device))
+    _need(W, torch.bfloat16, (N, K), "quantize_rtn8: W")
+    _need(codes, torch.uint8, (N, K), "quantize_rtn8: codes")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "quantize_rtn8: scales")
+        _need(zeros, torch.uint8, (N, G), "quantize_rtn8: zeros")
+    _on_gpu("quantize_rtn8", W, codes, scales, zeros)
+    st = _call(W, library().q4_quantize_rtn8, W.data_ptr(), N, K, g, _mode(mode), codes.data_ptr(),
+               _ptr(scales), _ptr(zeros))
     if st != 0:
         raise Q4Error(st, "q4_quantize_rtn8")
 
@@ -353,18 +408,19 @@ def quantize_rtn8(W, g: int = 128, mode: str = "sym"):
 def matmul_w8_into(X, codes, scales, zeros, g: int, mode: str, Y, kernel: str = "auto") -> None:
     """q4_matmul_w8 on a caller-provided Y (no allocation)."""
     import torch
-    _check_cuda(X, codes, scales, zeros, Y)
-    if X.dtype != torch.bfloat16 or X.dim() != 2 or Y.dtype != torch.bfloat16:
-        raise ValueError("X and Y must be 2-D bfloat16 tensors")
-    if kernel not in KERNELS:
-        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    if X is None or X.dim() != 2 or codes is None or codes.dim() != 2:
+        raise ValueError("X and codes must be 2-D tensors")
     M, K = X.shape
     N = codes.shape[0]
-    if codes.shape[1] != K or tuple(Y.shape) != (M, N):
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, codes {tuple(codes.shape)}, Y {tuple(Y.shape)}")
-    with torch.cuda.device(codes.device):
-        st = library().q4_matmul_w8(_ptr(X), M, N, K, g, _mode(mode), _ptr(codes), _ptr(scales),
-                                    _ptr(zeros), _ptr(Y), KERNELS[kernel], _stream(codes.device))
+    _need(X, torch.bfloat16, (M, K), "matmul_w8: X")
+    _need(codes, torch.uint8, (N, K), "matmul_w8: codes")
+    _need(Y, torch.bfloat16, (M, N), "matmul_w8: Y")
+    _need_group_params(codes, scales, zeros, N, _groups(K, g), mode, "matmul_w8")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    _on_gpu("matmul_w8", X, codes, scales, zeros, Y)
+    st = _call(codes, library().q4_matmul_w8, X.data_ptr(), M, N, K, g, _mode(mode), codes.data_ptr(),
+               _ptr(scales), _ptr(zeros), Y.data_ptr(), KERNELS[kernel])
     if st != 0:
         raise Q4Error(st, "q4_matmul_w8")
 
@@ -387,17 +443,24 @@ def gptq_workspace_bytes(M: int, N: int, K: int, g: int) -> int:
 def gptq_into(X, W, g: int, mode: str, damp: float, workspace, packed, scales, zeros, info) -> None:
     """q4_gptq on caller-provided workspace and outputs (no allocation)."""
     import torch
-    _check_cuda(X, W, workspace, packed, scales, zeros, info)
-    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or X.dim() != 2 or W.dim() != 2:
+    if X is None or X.dim() != 2 or W is None or W.dim() != 2:
         raise ValueError("X and W must be 2-D bfloat16 tensors")
     M, K = X.shape
     N = W.shape[0]
-    if W.shape[1] != K:
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}")
-    with torch.cuda.device(W.device):
-        st = library().q4_gptq(_ptr(X), M, _ptr(W), N, K, g, _mode(mode), float(damp), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _ptr(packed), _ptr(scales),
-                               _ptr(zeros), _ptr(info), _stream(W.device))
+    _need(X, torch.bfloat16, (M, K), "gptq: X")
+    _need(W, torch.bfloat16, (N, K), "gptq: W")
+    if workspace is None:
+        raise ValueError("gptq: workspace is required")
+    _need(packed, torch.uint8, (N, K // 2), "gptq: packed")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "gptq: scales")
+        _need(zeros, torch.uint8, (N, G), "gptq: zeros")
+    _need(info, torch.int32, (1,), "gptq: info")
+    _on_gpu("gptq", X, W, workspace, packed, scales, zeros, info)
+    st = _call(W, library().q4_gptq, X.data_ptr(), M, W.data_ptr(), N, K, g, _mode(mode), float(damp),
+               workspace.data_ptr(), workspace.numel() * workspace.element_size(), packed.data_ptr(),
+               _ptr(scales), _ptr(zeros), info.data_ptr())
     if st != 0:
         raise Q4Error(st, "q4_gptq")
 
