@@ -66,7 +66,9 @@ typedef enum {
     Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M (M >= 512 with K % 128
                               == 0 and a power-of-two g: X staged in LDS, W dequantised in
                               registers; otherwise W dequantised into LDS)                        */
-    Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z), fp32 per-group scaling  */
+    Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z) and exactly scaled X (bf16
+                              MFMA where X's range inside a K part exceeds fp16's), fp32 per-group
+                              scaling                                                             */
 } q4_kernel_t;
 
 typedef enum {
@@ -216,9 +218,14 @@ int q4_awq_search(const void* X, int64_t M, const void* Yref, const void* W, int
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
  * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,
- * g in {32, 64} or g % 128 == 0, and X staged in at most 160 KiB of LDS:
- * 2 M K + 64 K / min(g, 128) + 8192 bytes.  Otherwise Q4_ERR_UNSUPPORTED.  Every kernel
- * satisfies the same accuracy bound; callers use this to pin a kernel. */
+ * g in {32, 64, 128}, N * K / 2 < 2^32, and K split into at most 8 equal ranges of KR
+ * weights: KR = 32 P S with P = 4, 2 or 1 parts for M <= 4, <= 8 or <= 16, S = 16 slices (8
+ * for g = 32 at M <= 8 and for g = 64 at M <= 4), S halved (down to P S = 16) while K is
+ * not a multiple of KR or holds fewer than 4 ranges; K % KR == 0, KR >= 512, and two stages
+ * of 16 rows x KR weights per range fitting 160 KiB of LDS.  So K must be a multiple of 512,
+ * at most 4096 for M > 8 (and for g = 32 at M > 4) and at most 8192 otherwise.  Other shapes
+ * return Q4_ERR_UNSUPPORTED.  Every kernel satisfies the same accuracy bound; callers use
+ * this to pin a kernel. */
 int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,
                      const void* packed, const void* scales, const void* zeros, void* Y,
                      int32_t kernel, void* stream);

@@ -119,14 +119,19 @@ def test_select_kernel():
     assert q4.select_kernel(1, 28672, 8192, 128) == "gemv"
     assert q4.select_kernel(1, 11008, 4096, 128) == "gemv"
     assert q4.select_kernel(1, 4096, 16384, 128) == "gemv"
-    assert q4.select_kernel(1, 4096, 32768, 128) == "decode"
-    assert q4.select_kernel(1, 4096, 131072, 128) == "gemm"      # X would not fit in LDS
+    assert q4.select_kernel(1, 4096, 32768, 128) == "gemm"      # more than 8 K ranges of 2048
+    assert q4.select_kernel(1, 4096, 131072, 128) == "gemm"
     for M in (2, 3, 4, 8):
         assert q4.select_kernel(M, 28672, 8192, 128) == "decode"
+    assert q4.select_kernel(4, 11008, 4096, 128) == "decode"
     assert q4.select_kernel(16, 4096, 4096, 128) == "decode"
-    assert q4.select_kernel(16, 8192, 8192, 128) == "gemm"      # X would not fit in LDS
-    assert q4.select_kernel(2, 100, 96, 32) == "decode"
-    assert q4.select_kernel(4, 100, 96, 32) == "decode"
+    assert q4.select_kernel(16, 8192, 8192, 128) == "gemm"      # 16 ranges of 512
+    assert q4.select_kernel(8, 4096, 4096, 32) == "decode"
+    assert q4.select_kernel(8, 4096, 8192, 32) == "gemm"        # g = 32 takes ranges of 512 at M > 4
+    assert q4.select_kernel(3, 4096, 1536, 64) == "decode"      # K = 3 x 512
+    assert q4.select_kernel(2, 100, 96, 32) == "gemv"           # K not a multiple of 512
+    assert q4.select_kernel(4, 100, 96, 32) == "gemm"
+    assert q4.select_kernel(4, 100, 1024, 256) == "gemm"        # g above 128
     assert q4.select_kernel(4, 100, 480, 160) == "gemm"         # group straddles a 128 tile
     assert q4.select_kernel(4, 100, 480, 96) == "gemm"
     assert q4.select_kernel(17, 4096, 4096, 128) == "gemm"

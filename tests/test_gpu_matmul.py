@@ -19,13 +19,28 @@ def _gpu():
     require_gpu()
 
 
+def decode_fits(M, N, K, g, mode="asym"):
+    """Whether Q4_KERNEL_DECODE runs this shape (the rule stated in include/q4.h)."""
+    if not (1 <= M <= 16 and g in (32, 64, 128)) or N * (K // 2) >= 2 ** 32:
+        return False
+    P = 4 if M <= 4 else (2 if M <= 8 else 1)
+    S = 8 if (g == 32 and P >= 2) or (g == 64 and P == 4) else 16
+    while S > 4 and P * (S // 2) >= 16 and (K % (32 * P * S) != 0 or K // (32 * P * S) < 4):
+        S //= 2
+    KR = 32 * P * S
+    if K % KR != 0 or KR < 512 or KR // g < 4 or K // KR > 8:
+        return False
+    NG = KR // g
+    stage = 16 * (KR // 2) + 256 * ((8 * NG + 63) // 64) + 256 * ((4 * NG + 63) // 64)
+    return 2 * (K // KR) * stage + 2 * (K // KR) * 1024 <= 160 * 1024
+
+
 def kernels_for(M, N, K, g):
     """Every kernel that can run this shape (mirrors the rules stated in include/q4.h)."""
     ks = ["auto", "gemm"]
     if (M == 1 and K <= 16384) or (M == 2 and K <= 4096):
         ks.append("gemv")
-    lds = 2 * M * K + 64 * (K // min(g, 128)) + 8192
-    if 1 <= M <= 16 and (g in (32, 64) or g % 128 == 0) and lds <= 160 * 1024:
+    if decode_fits(M, N, K, g):
         ks.append("decode")
     return tuple(ks)
 
@@ -67,23 +82,6 @@ def test_configs_full(idx):
     _check_full(X_bits, W_bits, cfg.g, cfg.mode, cfg.name, kernels)
 
 
-def _check_sampled(X_bits, qw_host, g, mode, label, n_samples=4096, kernel="auto", seed=0):
-    from tests.gpu_util import log
-    packed, scales, zeros = qw_host
-    Y = _gpu_matmul(X_bits, _upload(packed, scales, zeros), g, mode, kernel)
-    M, N = Y.shape
-    rng = np.random.default_rng(seed)
-    mi = rng.integers(0, M, n_samples)
-    ni = rng.integers(0, N, n_samples)
-    mi = np.concatenate([mi, [0, M - 1, 0, M - 1]])
-    ni = np.concatenate([ni, [0, 0, N - 1, N - 1]])
-    Y_ref, A = orc.matmul_entries_ref(X_bits, packed, scales, zeros, g, mode, mi, ni)
-    ok, usage = orc.check_matmul(Y[mi, ni], Y_ref, A)
-    log(f"matmul parity (sampled) {label} kernel={kernel} M={M} N={N} g={g} {mode}: "
-        f"max tolerance usage {usage:.3e}")
-    assert ok, f"{label}: tolerance exceeded (usage {usage})"
-
-
 @pytest.fixture(scope="module")
 def layer70b():
     cfg = CONFIGS[3]
@@ -91,19 +89,88 @@ def layer70b():
     return cfg, X_bits, orc.quantize_rtn_ref(W_bits, cfg.g, cfg.mode)
 
 
+def _check_every_element(Y, X_bits, qw_host, g, mode, label, kernel, row_block=4096):
+    """Every element of a full-size Y against the oracle, W rows in blocks (bounded memory)."""
+    from tests.gpu_util import log
+    packed, scales, zeros = qw_host
+    worst = 0.0
+    for r0 in range(0, packed.shape[0], row_block):
+        r1 = min(r0 + row_block, packed.shape[0])
+        Y_ref, A = orc.matmul_ref(X_bits, packed[r0:r1], scales[r0:r1], zeros[r0:r1], g, mode)
+        ok, usage = orc.check_matmul(Y[:, r0:r1], Y_ref, A)
+        worst = max(worst, usage)
+        assert ok, f"{label} kernel={kernel} rows {r0}..{r1}: tolerance exceeded (usage {usage})"
+    log(f"matmul parity (every element) {label} kernel={kernel} M={Y.shape[0]} N={Y.shape[1]} g={g} "
+        f"{mode}: max tolerance usage {worst:.3e}")
+
+
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_70b_mlp_decode(layer70b, M):
+    """The 70B-shaped layer at M = 1, 4, 8: every element of Y, for every kernel that runs it."""
     cfg, X_bits, qw = layer70b
     for kernel in kernels_for(M, cfg.N, cfg.K, cfg.g):
-        _check_sampled(X_bits[:M], qw, cfg.g, cfg.mode, cfg.name, n_samples=3000, kernel=kernel)
+        Y = _gpu_matmul(X_bits[:M], _upload(*qw), cfg.g, cfg.mode, kernel)
+        _check_every_element(Y, X_bits[:M], qw, cfg.g, cfg.mode, cfg.name, kernel)
+
+
+@pytest.fixture(scope="module")
+def prefill_runs():
+    """The prefill workload's Y (bench launch configuration: auto kernel) for g = 128 and 32."""
+    cfg = CONFIGS[4]
+    W_bits, X_bits = make_layer(cfg)
+    out = {}
+    for g in (128, 32):
+        qw = orc.quantize_rtn_ref(W_bits, g, cfg.mode)
+        out[g] = (qw, _gpu_matmul(X_bits, _upload(*qw), g, cfg.mode))
+    return cfg, X_bits, out
 
 
 @pytest.mark.parametrize("g", [128, 32])
-def test_prefill(g):
-    cfg = CONFIGS[4]
-    W_bits, X_bits = make_layer(cfg)
-    qw = orc.quantize_rtn_ref(W_bits, g, cfg.mode)
-    _check_sampled(X_bits, qw, g, cfg.mode, cfg.name, n_samples=4096)
+@pytest.mark.parametrize("block", [0, 1, 2, 3])
+def test_prefill(prefill_runs, g, block):
+    """The prefill workload (M = 2048, 8192 x 8192), every element of Y: one quarter of the W
+    rows per test."""
+    cfg, X_bits, out = prefill_runs
+    (packed, scales, zeros), Y = out[g]
+    q = packed.shape[0] // 4
+    r0, r1 = block * q, (block + 1) * q
+    _check_every_element(Y[:, r0:r1], X_bits, (packed[r0:r1], scales[r0:r1], zeros[r0:r1]), g, cfg.mode,
+                         f"{cfg.name} rows {r0}..{r1}", "auto", row_block=1024)
+
+
+def adversarial_layer(N, K, M, log2_ratio, seed=0):
+    """Activations of one sign and small magnitude, and in every 128-weight block one activation
+    2^log2_ratio times larger that meets a zero weight (its code equals the zero point, so it
+    adds nothing to Y or to the tolerance's sum |x x_hat|): a kernel that scales X per block
+    into fp16 would lose the small activations, which carry all of Y."""
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0, 0.02, (N, K))
+    big = np.arange(5, K, 128)
+    W[:, big] = 0.0
+    X = np.abs(rng.normal(0, 1e-3, (M, K))) + 1e-4
+    X[:, big] = 1e-3 * 2.0 ** log2_ratio
+    return f64_to_bf16_bits(W), f64_to_bf16_bits(X)
+
+
+@pytest.mark.parametrize("log2_ratio", [12, 20, 24, 28, 36, 60])
+@pytest.mark.parametrize("N,K,g", [(256, 4096, 128), (96, 1024, 32), (80, 2048, 64)])
+def test_adversarial_dynamic_range(log2_ratio, N, K, g):
+    for M in (1, 2, 4, 8, 16):
+        W_bits, X_bits = adversarial_layer(N, K, M, log2_ratio, seed=log2_ratio + M)
+        for mode in ("asym", "sym"):
+            _check_full(X_bits, W_bits, g, mode, f"adversarial 2^{log2_ratio}", kernels_for(M, N, K, g))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 16])
+@pytest.mark.parametrize("N,K,g", [(100, 1536, 64), (300, 2048, 128), (33, 4096, 32), (129, 8192, 64),
+                                   (50, 3072, 128), (17, 512, 32), (257, 4096, 128)])
+def test_decode_shapes(M, N, K, g):
+    """Shapes the matrix-core decode kernel takes (K a multiple of 512, ragged N), every kernel."""
+    rng = np.random.default_rng(M * 17 + N + K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full(X_bits, W_bits, g, mode, "decode-shapes", kernels_for(M, N, K, g))
 
 
 @pytest.mark.parametrize("M,N,K,g", [(512, 64, 128, 128), (513, 300, 256, 32), (640, 256, 384, 128),

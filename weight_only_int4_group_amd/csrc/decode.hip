@@ -1,32 +1,47 @@
-// W4A16 decode for 1 <= M <= 16 on the fp16 matrix cores of gfx950
-// (v_mfma_f32_16x16x32_f16).
+// W4A16 decode for 1 <= M <= 16 on the matrix cores of gfx950 (v_mfma_f32_16x16x32).
 //
 // W4A16: 4-bit weights dequantised inside the kernel, products on 16-bit operands
 // ("LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
 // "The vocabulary"); decode reads every weight once and is bound by HBM ("Overview").
-// Dequantisation x_hat = scale * (q - z) ("DL S067 · Quantization", §1).
+// Dequantisation x_hat = scale * (q - z) ("DL S067 · Quantization", §1), groups of g weights
+// along K ("Model Quantization", §1).
 //
-// Arithmetic (exact up to fp32 summation and the final bf16 rounding):
-//   * (q - z) is formed exactly in fp16 (nibble OR-ed into the mantissa of 1024.0, minus
-//     1024 + z; nibbles in bits 4..7 give 16 (q - z));
-//   * X is converted to fp16 exactly after scaling each (row m, k tile) by a power of two 2^e
+// Roles.  D[m][n] = sum_k A[m][k] B[k][n] with A = X (16 token slots m) and B = (q - z) of 16 W
+// rows n.  Lane l holds A row m = l % 16 and B column n = l % 16, eight k values of the
+// quarter kq = l / 16, and D rows 4 (l / 16) .. + 3 of column n.
+//
+// Work split.  A workgroup (one per compute unit, persistent) walks 16-row blocks of W.  Its WS
+// waves split K: wave w owns the K range [w KR, (w + 1) KR).  A wave keeps its X range in
+// registers for the whole kernel (the A operand of every row block) and streams its W range of
+// each row block through LDS; the WS partial sums of a row block meet in LDS in wave order.
+// With M <= 8 (or <= 4) tokens, the 16 token slots carry P = 2 (or 4) parts of the wave's
+// K range: slot m holds token m % (16 / P) of part m / (16 / P), and part p's weights go to
+// their own accumulator, whose rows of part p are the only ones kept.  So the same registers
+// cover a P times longer K range.
+//
+// Loads.  Each 1 KiB LDS-DMA instruction reads 4 rows x 256 contiguous bytes of codes
+// (requests of whole cache lines and more per row: as fast as contiguous streaming), written
+// to LDS with the 16-byte chunk c of row r at position (c ^ r) within its row, so that the
+// fragment reads of 16 rows at one chunk hit 16 distinct bank groups.  The fp16 scales and
+// uint8 zero-points of the stage come the same way, one dword per lane.  A wave keeps S stages
+// in flight and waits for the oldest with an explicit vmcnt: every global load of the main
+// loop is one of these LDS-DMA copies.
+//
+// Arithmetic (fast path, exact up to fp32 summation and the final bf16 rounding):
+//   * (q - z) is formed exactly in fp16: the nibble OR-ed into the mantissa of 1024.0, minus
+//     1024 + z (nibbles in bits 4..7 give 16 (q - z));
+//   * X is converted to fp16 exactly after scaling each (token, part) by a power of two 2^e
 //     that puts its largest |x| in [2^14, 2^15); the positions that meet a 16 (q - z) weight
-//     carry 2^(e-4);
-//   * the MFMA sums the products of one tile (exact products, fp32 accumulation); each tile's
-//     partial is multiplied by scale * 2^-e in fp32 and accumulated.
-// Roles: D[m][n] = sum_k X[m][k] W[n][k], A = X (rows m, zero beyond M), B = dequantised W
-// (16 rows n).  A tile is TK = min(g, 128) weights wide along K, so it never straddles a group.
-// In tile t, lane (j, q) = (lane % 16, lane / 16) owns the TK/4 weights that start at
-// k = t TK + q TK/4 in row n0 + j (TK/32 dwords); slice u of the tile is the u-th dword of every
-// lane, i.e. one MFMA.  K inside a tile is permuted identically for both operands.
-//
-// Work split.  A block holds up to 8 waves and stays resident: it stages X once, then walks
-// groups of RB blocks of 16 output rows.  Each row block is shared by KS waves that split K
-// into KS contiguous ranges of tiles (RB x KS waves per block); with KS > 1 the partial sums
-// meet in LDS and one wave stores.  A wave keeps 32 dwords of packed weights per lane in
-// flight.  Scales and zero points: with one group per tile (g <= 128) a lane loads the scales
-// and zeros of a whole window of tiles at once, one window ahead, instead of two small loads
-// per tile.
+//     carry 2^(e - 4);
+//   * the MFMA takes exact products and sums them in fp32; each tile's sum is multiplied by its
+//     group's scale and accumulated in fp32; 2^-e is applied once per row block.
+// The fp16 conversion is exact only while every nonzero |x| 2^(e-4) of the part is at least
+// 2^-14 (the matrix cores flush fp16 subnormal inputs).  A wave whose X range has a smaller
+// element (a dynamic range above about 2^24 inside one part) runs the exact path instead:
+// X and (q - z) as bf16 (exact: bf16 holds 8 significant bits, (q - z) needs 4, 16 (q - z) 8),
+// the bf16 matrix instruction, and no power-of-two scaling.
+#include <utility>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -35,361 +50,407 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kMaxWaves = 8;        // waves sharing one row block at most (K split), and
-                                    // LDS slots for their partial sums
-constexpr int kWideWaves = 16;      // waves per block of the lean (window) variant
+constexpr int kMaxWaves = 8;
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr int kRedBytes = 1024;          // one f32x4 per lane: a wave's partial of a row block
 
-// Four 32-bit registers of fp16 pairs (q - z) (x16 for odd positions) from 8 nibbles: a
-// nibble OR-ed into the mantissa of fp16 1024.0 reads 1024 + q, and subtracting 1024 + z
-// (1024 + 16 z for nibbles in bits 4..7) leaves q - z (16 (q - z)) exactly, so a weight whose
-// code equals its zero point contributes exactly 0.  Slot order (k0, k4, k1, k5, k2, k6, k3,
-// k7); X is staged in the same order with the factor 2^-4 on the slots that meet 16 (q - z).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most k * L of this wave's vector memory operations are outstanding (k <= 3;
+// the launch keeps (S - 1) L <= 63, the counter's range).
+template <int L>
+__device__ __forceinline__ void wait_stages(int k) {
+  constexpr int L2 = 2 * L <= 63 ? 2 * L : 63, L3 = 3 * L <= 63 ? 3 * L : 63;
+  if (k <= 0) wait_vm<0>();
+  else if (k == 1) wait_vm<L>();
+  else if (k == 2) wait_vm<L2>();
+  else wait_vm<L3>();
+}
+
+// f(0), f(1), ..., f(N - 1) with compile-time arguments: straight-line code that does not
+// depend on the unroller's size limits.
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS-DMA copies through a buffer resource (an offset at or past the resource's end reads 0):
+// 16 bytes per lane, non-temporal, lane i writing LDS bytes [lds + 16 i, + 16); or 4 bytes per
+// lane, lane i writing [lds + 4 i, + 4).  The address is the resource base + voff + soff.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), (uint32_t)kBufferFlags};
+}
+
+// Eight fp16 (q - z) from 8 nibbles (one dword of codes): nibble OR-ed into 1024.0 minus
+// 1024 + z (1024 + 16 z for nibbles in bits 4..7).  Slot order (k0, k4, k1, k5, k2, k6, k3,
+// k7); the odd k carry 16 (q - z).
 template <bool SYM>
-__device__ __forceinline__ f16x8 dequant_q_minus_z(uint32_t dw, uint32_t bias, f16x2 b1, f16x2 b16) {
+__device__ __forceinline__ f16x8 dequant_f16(uint32_t dw, uint32_t bias, f16x2 b1, f16x2 b16) {
   if (SYM) dw ^= 0x88888888u;                         // two's complement nibble -> q + 8
   const uint32_t d8 = dw >> 8;
-  const f16x2 h0 = as_f16x2((dw & 0x000F000Fu) | bias) - b1;    // k0, k4
-  const f16x2 h1 = as_f16x2((dw & 0x00F000F0u) | bias) - b16;   // k1, k5 (x16)
-  const f16x2 h2 = as_f16x2((d8 & 0x000F000Fu) | bias) - b1;    // k2, k6
-  const f16x2 h3 = as_f16x2((d8 & 0x00F000F0u) | bias) - b16;   // k3, k7 (x16)
+  const f16x2 h0 = as_f16x2((dw & 0x000F000Fu) | bias) - b1;
+  const f16x2 h1 = as_f16x2((dw & 0x00F000F0u) | bias) - b16;
+  const f16x2 h2 = as_f16x2((d8 & 0x000F000Fu) | bias) - b1;
+  const f16x2 h3 = as_f16x2((d8 & 0x00F000F0u) | bias) - b16;
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// Maximum over each aligned group of L lanes (L = 4, 8 or 16, inside one 16-lane DPP row),
-// returned to every lane of the group: DPP moves, no LDS round trips.
-template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  static_assert(L == 4 || L == 8 || L == 16, "4, 8 or 16 lanes");
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
-  if (L >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
-  if (L >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
-  return v;
+// The same eight values as bf16 (small integers: exact).
+__device__ __forceinline__ bf16x8 to_bf16(f16x8 h) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)h[i];
+  return r;
 }
 
-// The weights are read 64 bytes per row at a time, the rest of each line one tile later:
-// plain loads keep the line in the cache for that second half.
-template <int DPT>
-__device__ __forceinline__ void load_dwords(uint32_t (&d)[DPT], const uint8_t* p) {
-  if constexpr (DPT == 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-  } else if constexpr (DPT == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    d[0] = v[0]; d[1] = v[1];
-  } else {
-    d[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
+// Stage geometry of one wave: 16 rows of KR weights (codes), their scales and zero-points.
+template <int P, int NSL, int TK, bool SYM>
+struct Geo {
+  static constexpr int MP = 16 / P;                  // token slots per part
+  static constexpr int PW = NSL * 32;                // k per part
+  static constexpr int KR = P * PW;                  // k per wave
+  static constexpr int RBY = KR / 2;                 // code bytes per row per stage
+  static constexpr int SEG = RBY / 256;              // 256-byte segments per row
+  static constexpr int NCI = 4 * SEG;                // 1 KiB code copies per stage
+  static constexpr int NG = KR / TK;                 // groups (= tiles) per row per stage
+  static constexpr int NSI = (8 * NG + 63) / 64;     // scale dword copies (64 dwords each)
+  static constexpr int NZI = SYM ? 0 : (4 * NG + 63) / 64;
+  static constexpr int L = NCI + NSI + NZI;          // vector memory operations per stage
+  static constexpr uint32_t SOFF = 16u * RBY;        // scales inside the stage
+  static constexpr uint32_t ZOFF = SOFF + 256u * NSI;
+  static constexpr uint32_t STAGE = ZOFF + 256u * NZI;
+  static constexpr int DPT = TK / 32;                // dwords per lane per tile
+  static constexpr int TPP = PW / TK;                // tiles per part
+  static_assert(RBY % 256 == 0, "whole 256-byte segments per row");
+  static_assert(NG >= 4 && (NG & (NG - 1)) == 0, "at least four groups per stage");
+  static_assert(L <= 63, "one stage's copies fit vmcnt");
+};
 
-size_t lds_tail(int64_t K, int g);
-size_t lds_bytes(int64_t M, int64_t K, int g) { return (size_t)(2 * M * K) + lds_tail(K, g); }
-
-// Bytes of LDS after the staged X: the 2^-e factors and the K-split partial sums.
-size_t lds_tail(int64_t K, int g) {
-  const int64_t TK = g < 128 ? g : 128;
-  return (size_t)(64 * (K / TK)) + (size_t)kMaxWaves * kWave * 16;
-}
-
-// WIN: one group per tile, window loads of scales / zeros (needs aligned windows, see launch).
-// MAXW: waves per block at most (the lean WIN variant fits 16 waves' registers).
-template <int DPT, bool SYM, bool WIN, int MAXW>
-__global__ __launch_bounds__(MAXW * kWave) void decode_kernel(
-    const uint16_t* __restrict__ X, int M, int N, int K, int g,
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y, int RB, int KS) {
-  constexpr int TK = 32 * DPT;
-  constexpr int P = 32 / DPT;                   // tiles in flight per wave (32 dwords per lane)
-  extern __shared__ u32x4 lds4[];
-  const int T = K / TK;                         // tiles along K
-  const int G = K / g;
-  const int TPG = g / TK;                       // tiles per group
-  const int MP = M;
-  const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int lane = tid & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int j = lane & 15, q = lane >> 4;
+// At most 8 waves per workgroup: two waves per SIMD, 256 registers each (the X range takes 64).
+template <int P, int NSL, int TK, bool SYM>
+__global__ __launch_bounds__(8 * 64) void decode_kernel(
+    const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y,
+    int S) {
+  using Gm = Geo<P, NSL, TK, SYM>;
+  constexpr int MP = Gm::MP, DPT = Gm::DPT, KR = Gm::KR, NG = Gm::NG;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int WS = blockDim.x / kWave;
+  const int m = lane & 15, kq = lane >> 4;           // A row / B column, k quarter
+  const int G = K / TK;                              // groups per row (g = TK)
   const int NB = (N + 15) >> 4;
+  const int K0 = w * KR;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const uint32_t my_stages = lds0 + (uint32_t)(w * S) * Gm::STAGE;
+  const uint32_t red0 = lds0 + (uint32_t)(WS * S) * Gm::STAGE;
 
-  u32x4* xs = lds4;                                                       // [T][DPT][4][MP]
-  float* fx = reinterpret_cast<float*>(lds4 + (size_t)T * DPT * 4 * MP);  // [T][16]: 2^-e
-  f32x4* red = reinterpret_cast<f32x4*>(fx + (size_t)T * 16);             // [waves][64]
-
-  // This wave: row-block slot r of each group of RB row blocks, tiles [t_beg, t_end) of K.
-  const int r = w / KS, part = w - r * KS;
-  const int TPP = (T + KS - 1) / KS;
-  const int t_beg = min(part * TPP, T), t_end = min(t_beg + TPP, T);
-  const int NT = t_end - t_beg;
-  const int NGR = (NB + RB - 1) / RB;
-  const size_t rowbytes = (size_t)K >> 1;
-
-  // Ring of P tiles.  Loads are unconditional, from clamped tiles (t <= t_end - 1): a load
-  // under a branch would make the compiler wait for every load in flight before the next use.
-  uint32_t wb[P][DPT];
-  uint32_t sb[P], zb[P];
-  const uint8_t* pr = packed;
-  const uint16_t* sr = scales;
-  const uint8_t* zr = zeros;
-  int lt = 0, lg = 0, lgi = 0;
-  auto load_next = [&](int i) {
-    const int t = min(lt, t_end - 1);
-    load_dwords<DPT>(wb[i], pr + (size_t)t * (TK / 2));
-    if (!WIN) {
-      const int gg = lt < t_end ? lg : (t_end - 1) / TPG;
-      sb[i] = sr[gg];
-      if (!SYM) zb[i] = zr[gg];
-    }
-    ++lt;
-    if (++lgi == TPG) { lgi = 0; ++lg; }
-  };
-  // Windows (WIN): the scales / zeros of the P tiles (= P groups) of one chunk; the next
-  // chunk's window is loaded at the start of the current one.
-  constexpr int SW = WIN ? P / 2 : 1, ZW = WIN ? P / 4 : 1;
-  uint32_t cs[SW], cz[ZW], ns[SW], nz[ZW];
-  auto load_window = [&](uint32_t (&ds)[SW], uint32_t (&dz)[ZW], int c) {
-    const int t = min(t_beg + c * P, t_end - P);
-    const uint32_t* s4 = reinterpret_cast<const uint32_t*>(sr + t);
+  // ---- X range -> registers: slot m = (part, token), slices s = (tile, dword) ----
+  const int part = m / MP, tok = m % MP;
+  const __amdgpu_buffer_rsrc_t rx = buffer_over(X, (uint32_t)M * (uint32_t)K * 2u);
+  u32x4 xr[NSL];
 #pragma unroll
-    for (int v = 0; v < SW; v += 4) {
-      const u32x4 x4 = *reinterpret_cast<const u32x4*>(s4 + v);
-      ds[v] = x4[0]; ds[v + 1] = x4[1]; ds[v + 2] = x4[2]; ds[v + 3] = x4[3];
-    }
-    if (!SYM) {
-      const uint32_t* z4 = reinterpret_cast<const uint32_t*>(zr + t);
-      if constexpr (ZW == 2) {
-        const u32x2 x2 = *reinterpret_cast<const u32x2*>(z4);
-        dz[0] = x2[0]; dz[1] = x2[1];
-      } else {
-#pragma unroll
-        for (int v = 0; v < ZW; v += 4) {
-          const u32x4 x4 = *reinterpret_cast<const u32x4*>(z4 + v);
-          dz[v] = x4[0]; dz[v + 1] = x4[1]; dz[v + 2] = x4[2]; dz[v + 3] = x4[3];
-        }
-      }
-    }
-  };
-  // Point the ring at row block nb = gi RB + r and request its first P tiles (wave-uniform).
-  auto begin_group = [&](int gi) {
-    const int nb = gi * RB + r;
-    if (nb < NB && NT > 0) {
-      // Rows past N (ragged last block) read row N - 1; their outputs are not stored.
-      const int n = min(nb * 16 + j, N - 1);
-      pr = packed + (size_t)n * rowbytes + q * (TK / 8);
-      sr = scales + (size_t)n * G;
-      zr = zeros + (size_t)n * G;
-      lt = t_beg;
-      lg = t_beg / TPG;
-      lgi = t_beg - lg * TPG;
-      if (WIN) load_window(cs, cz, 0);
-#pragma unroll
-      for (int i = 0; i < P; ++i) load_next(i);
-    }
-  };
-
-  // The first group's weights are requested before X is staged, so that HBM latency overlaps
-  // the staging.
-  if (blockIdx.x < NGR) begin_group(blockIdx.x);
-
-  // ---- X -> LDS: TK/8 threads per (m, tile) of the M rows, one octet of 8 values each, four
-  // octets per thread in flight; rows M..15 get the factor 0. ----
-  constexpr int OPT = TK / 8;                 // octets per tile
-  for (int u0 = tid; u0 < T * (16 - MP); u0 += nthreads) fx[(u0 % T) * 16 + MP + u0 / T] = 0.0f;
-  const int total = MP * T * OPT;             // a multiple of OPT: lanes leave the loop in whole groups
-  for (int base = tid; base < total; base += 4 * nthreads) {
-    u32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u0 = min(base + i * nthreads, total - 1);
-      const int o = u0 & (OPT - 1);
-      const int mt = u0 / OPT;
-      const int m = mt / T, t = mt - m * T;
-      v[i] = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)t * TK + 8 * o);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u0 = base + i * nthreads;     // uniform per aligned group of OPT lanes
-      const int o = u0 & (OPT - 1);           // octet o = q DPT + u covers k = t TK + 8 o
-      const int mt = u0 / OPT;
-      const int m = mt / T, t = mt - m * T;
-      float amax = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][c])), fabsf(bf16_hi(v[i][c]))));
-      amax = group_max<OPT>(amax);            // aligned groups of OPT lanes = one (m, tile)
-      int e = 0;
-      if (amax > 0.0f) {
-        int E;
-        frexpf(amax, &E);
-        e = min(15 - E, 100);                 // amax * 2^e in [2^14, 2^15)
-      }
-      if (u0 < total) {
-        const u32x4 w = v[i];
-        const f16x2 p0 = {(_Float16)ldexpf(bf16_lo(w[0]), e), (_Float16)ldexpf(bf16_lo(w[2]), e)};
-        const f16x2 p1 = {(_Float16)ldexpf(bf16_hi(w[0]), e - 4), (_Float16)ldexpf(bf16_hi(w[2]), e - 4)};
-        const f16x2 p2 = {(_Float16)ldexpf(bf16_lo(w[1]), e), (_Float16)ldexpf(bf16_lo(w[3]), e)};
-        const f16x2 p3 = {(_Float16)ldexpf(bf16_hi(w[1]), e - 4), (_Float16)ldexpf(bf16_hi(w[3]), e - 4)};
-        const int kq = o / DPT, u = o - kq * DPT;
-        xs[((size_t)(t * DPT + u) * 4 + kq) * MP + m] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
-        if (o == 0) fx[t * 16 + m] = ldexpf(1.0f, -e);
-      }
-    }
+  for (int s = 0; s < NSL; ++s) {
+    const int j = s / DPT, u = s % DPT;
+    const int k = K0 + part * Gm::PW + j * TK + kq * (TK / 4) + 8 * u;
+    xr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rx, 2u * ((uint32_t)tok * (uint32_t)K + (uint32_t)k), 0, 0));
   }
-  __syncthreads();
+  float amax = 0.0f, amin = __builtin_inff();
+#pragma unroll
+  for (int s = 0; s < NSL; ++s)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float a = fabsf(bf16_lo(xr[s][c])), b = fabsf(bf16_hi(xr[s][c]));
+      amax = fmaxf(amax, fmaxf(a, b));
+      amin = fminf(amin, fminf(a > 0.0f ? a : __builtin_inff(), b > 0.0f ? b : __builtin_inff()));
+    }
+  // the part of one token is spread over the four quarters kq: lanes m, m + 16, m + 32, m + 48
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amin = fminf(amin, __shfl_xor(amin, 16));
+  amin = fminf(amin, __shfl_xor(amin, 32));
+  int e = 0;
+  if (amax > 0.0f) e = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);   // amax 2^e in [2^14, 2^15)
+  // exact in fp16 (normal, as the matrix cores need) iff every nonzero |x| 2^(e-4) >= 2^-14
+  const bool lossy = amin < __builtin_inff() && __builtin_ldexpf(amin, e) < 0x1p-10f;
+  const bool exact = __builtin_amdgcn_ballot_w64(lossy) != 0;              // wave-uniform
+  const float my_fac = exact ? 1.0f : __builtin_ldexpf(1.0f, -e);
+#pragma unroll
+  for (int s = 0; s < NSL; ++s) {
+    const u32x4 v = xr[s];
+    // k0..k7 = lo/hi halves of v[0..3]; slots (k0, k4, k1, k5, k2, k6, k3, k7), odd k x 2^-4
+    const float x[8] = {bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1]),
+                        bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+    const int ord[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    uint32_t o[4];
+    if (!exact) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = ord[2 * q], k1 = ord[2 * q + 1];
+        const f16x2 h = {(_Float16)__builtin_ldexpf(x[k0], (k0 & 1) ? e - 4 : e),
+                         (_Float16)__builtin_ldexpf(x[k1], (k1 & 1) ? e - 4 : e)};
+        o[q] = as_u32(h);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = ord[2 * q], k1 = ord[2 * q + 1];
+        o[q] = pack_bf16x2((k0 & 1) ? x[k0] * 0.0625f : x[k0], (k1 & 1) ? x[k1] * 0.0625f : x[k1]);
+      }
+    }
+    xr[s] = u32x4{o[0], o[1], o[2], o[3]};
+  }
 
+  // ---- stage copies ----
+  // Codes: copy i covers rows 4 (i % 4) + lane / 16 and the 256-byte segment i / 4; lane l
+  // reads chunk (l % 16) ^ row of it.  The per-lane part of the offset is the same for every
+  // copy up to an XOR of 64 (i % 4) (rows are a multiple of 256 bytes long); the rest is
+  // wave-uniform.  Rows past N lie past the resource's end and read as 0.
+  const uint32_t rowbytes = (uint32_t)K / 2u;
+  const u32x4 rw = buffer_words(packed, (uint32_t)N * rowbytes);
+  const u32x4 rs = buffer_words(scales, (uint32_t)N * (uint32_t)G * 2u);
+  const u32x4 rz = buffer_words(zeros, SYM ? 0u : (uint32_t)N * (uint32_t)G);
+  const uint32_t code_lane = (uint32_t)(lane >> 4) * rowbytes + 16u * (uint32_t)((lane & 15) ^ (lane >> 4));
+  // scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2); zeros:
+  // dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
+  // stage's 16 rows in LDS)
+  const uint32_t s_lane = (uint32_t)(lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
+  const uint32_t z_lane = (uint32_t)(lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
+  auto issue = [&](int slot, int rb) {
+    const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
+    const uint32_t n0 = (uint32_t)rb * 16u;
+#pragma unroll
+    for (int i = 0; i < Gm::NCI; ++i)
+      dma16(rw, code_lane ^ (64u * (uint32_t)(i & 3)),
+            (n0 + 4u * (uint32_t)(i & 3)) * rowbytes + (uint32_t)K0 / 2u + 256u * (uint32_t)(i >> 2),
+            st + 1024u * (uint32_t)i);
+#pragma unroll
+    for (int q = 0; q < Gm::NSI; ++q)
+      dma4(rs, s_lane, ((n0 + (uint32_t)(q * (128 / NG))) * (uint32_t)G + (uint32_t)(K0 / TK)) * 2u,
+           st + Gm::SOFF + 256u * (uint32_t)q);
+#pragma unroll
+    for (int q = 0; q < Gm::NZI; ++q)
+      dma4(rz, z_lane, (n0 + (uint32_t)(q * (256 / NG))) * (uint32_t)G + (uint32_t)(K0 / TK),
+           st + Gm::ZOFF + 256u * (uint32_t)q);
+  };
+
+  const int stride = gridDim.x;
+  for (int s = 0; s < S; ++s)
+    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+
+  // fragment reads: B column n = m (row of the block), quarter kq
+  const int n = m;
   uint32_t bias = 0x64006400u;
   asm volatile("" : "+v"(bias));   // keep in a VGPR: (x & mask) | bias -> one v_and_or_b32
-  const int jx = min(j, MP - 1);
 
-  for (int gi = blockIdx.x; gi < NGR; gi += gridDim.x) {            // block-uniform
-    if (gi != (int)blockIdx.x) begin_group(gi);
-    const int nb = gi * RB + r;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (nb < NB && NT > 0) {                                          // wave-uniform
-      for (int t0 = 0; t0 < NT; t0 += P) {
-        if (WIN) load_window(ns, nz, t0 / P + 1);
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-          const int t = t_beg + t0 + i;
-          if (WIN || t < t_end) {             // wave-uniform; WIN: NT is a multiple of P
-            uint32_t z, sbits;
-            if (WIN) {
-              sbits = (cs[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-              z = SYM ? 8u : (cz[i >> 2] >> (8 * (i & 3))) & 0xffu;
-            } else {
-              sbits = sb[i];
-              z = SYM ? 8u : zb[i];
-            }
-            const f16x2 b1 = as_f16x2((0x6400u + z) * 0x00010001u);
-            const f16x2 b16 = as_f16x2((0x6400u + 16u * z) * 0x00010001u);
-            f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < DPT; ++u) {
-              const f16x8 bw = dequant_q_minus_z<SYM>(wb[i][u], bias, b1, b16);
-              // rows j >= M read row M - 1: their results land in rows that are never stored
-              const f16x8 ax = __builtin_bit_cast(f16x8, xs[((size_t)(t * DPT + u) * 4 + q) * MP + jx]);
-              pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, pacc, 0, 0, 0);
-            }
-            const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
-            const f32x4 f = *reinterpret_cast<const f32x4*>(fx + t * 16 + 4 * q);   // 2^-e, rows 4q..4q+3
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(pacc[rr], s * f[rr], acc[rr]);
-          }
-          load_next(i);
+  auto run = [&](auto exact_tag) {
+    constexpr bool EX = decltype(exact_tag)::value;
+    int it = 0;
+    for (int rb = blockIdx.x; rb < NB; rb += stride, ++it) {          // block-uniform
+      const int slot = it % S;
+      const int later = min(S - 1, (NB - 1 - rb) / stride);           // stages issued after this one
+      wait_stages<Gm::L>(later);
+      const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
+      // One part at a time: its accumulator collects the part's tiles, then the lanes whose D rows
+      // belong to that part (4 kq / MP == p) keep it.  The tiles are generated at compile time
+      // (a fold over an index sequence), so every X register index is a constant.
+      f32x4 res = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      auto tile = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int p = t / Gm::TPP, j = t % Gm::TPP;
+        if constexpr (j == 0) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        // codes of tile t, row n, quarter kq: bytes t TK/2 + kq TK/8 of the row's stage range
+        const int byte = t * (TK / 2) + kq * (TK / 8);
+        const int c = byte >> 4;
+        const uint32_t pos = (uint32_t)((c >> 4) * 256 + n * 16 + ((c & 15) ^ n));
+        const uint32_t off = (st - lds0) + 16u * pos + (uint32_t)(byte & 15);
+        uint32_t dw[DPT];
+        if constexpr (DPT == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(lds + off);
+          dw[0] = v[0]; dw[1] = v[1]; dw[2] = v[2]; dw[3] = v[3];
+        } else if constexpr (DPT == 2) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(lds + off);
+          dw[0] = v[0]; dw[1] = v[1];
+        } else {
+          dw[0] = *reinterpret_cast<const uint32_t*>(lds + off);
         }
-        if (WIN) {
+        const uint32_t sbits = *reinterpret_cast<const uint16_t*>(lds + (st - lds0) + Gm::SOFF + 2 * (n * NG + t));
+        const uint32_t z = SYM ? 8u : (uint32_t)lds[(st - lds0) + Gm::ZOFF + n * NG + t];
+        const f16x2 b1 = as_f16x2((0x6400u + z) * 0x00010001u);
+        const f16x2 b16 = as_f16x2((0x6400u + 16u * z) * 0x00010001u);
+        f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < SW; ++v) cs[v] = ns[v];
+        for (int u = 0; u < DPT; ++u) {
+          const f16x8 bw = dequant_f16<SYM>(dw[u], bias, b1, b16);
+          const u32x4 a = xr[j * DPT + u];
+          if constexpr (EX)
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), to_bf16(bw), pacc, 0, 0, 0);
+          else
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), bw, pacc, 0, 0, 0);
+        }
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
 #pragma unroll
-          for (int v = 0; v < ZW; ++v) cz[v] = nz[v];
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pacc[r], sc, acc[r]);
+        if constexpr (j == Gm::TPP - 1) {
+          if ((4 * kq) / MP == p) res = acc;
+        }
+      };
+      for_each_index(tile, std::make_integer_sequence<int, P * Gm::TPP>{});
+      // this slot's LDS reads are done: refill it with the row block S strides ahead
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (rb + S * stride < NB) issue(slot, rb + S * stride);
+
+      // factor of output rows 4 kq + r (token slots of this lane's D fragment)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) res[r] *= __shfl(my_fac, 4 * kq + r);
+      // add the parts: slot 4 kq + r is token (4 kq + r) % MP of part (4 kq + r) / MP
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (P == 4) res[r] += __shfl_xor(res[r], 16);
+        if constexpr (P >= 2) res[r] += __shfl_xor(res[r], 32);
+      }
+      // the waves' partials meet in LDS (two buffers, alternating row blocks)
+      const uint32_t red = red0 + (uint32_t)(it & 1) * (uint32_t)(WS * kRedBytes);
+      *reinterpret_cast<f32x4*>(lds + (red - lds0) + w * kRedBytes + 16 * lane) = res;
+      lds_barrier();
+      if (w == it % WS && kq < MP / 4) {                              // wave-uniform / lane mask
+        f32x4 sum = *reinterpret_cast<const f32x4*>(lds + (red - lds0) + 16 * lane);
+        for (int ww = 1; ww < WS; ++ww)
+          sum += *reinterpret_cast<const f32x4*>(lds + (red - lds0) + ww * kRedBytes + 16 * lane);
+        const int row = rb * 16 + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tk = 4 * kq + r;
+          if (row < N && tk < M) Y[(size_t)tk * N + row] = f32_to_bf16_bits(sum[r]);
         }
       }
     }
-    if (KS > 1) {                                                     // block-uniform
-      // Parts 1..KS-1 of row-block slot r leave their sums in slots r (KS - 1) + part - 1
-      // (RB (KS - 1) <= kMaxWaves of them); part 0 adds them in part order.
-      if (part > 0) red[(r * (KS - 1) + part - 1) * kWave + lane] = acc;
-      __syncthreads();
-      if (part == 0) {
-#pragma unroll 1
-        for (int pp = 1; pp < KS; ++pp) acc += red[(r * (KS - 1) + pp - 1) * kWave + lane];
-      }
-      __syncthreads();
-    }
-    // lane (j, q): rows m = 4 q + rr of output column 16 nb + j
-    const int ncol = nb * 16 + j;
-    if (part == 0 && nb < NB && ncol < N) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = 4 * q + rr;
-        if (m < MP) Y[(size_t)m * N + ncol] = f32_to_bf16_bits(acc[rr]);
-      }
-    }
-  }
+  };
+  if (exact) run(std::true_type{});
+  else run(std::false_type{});
 }
 
-template <int DPT, bool SYM>
-hipError_t launch_cfg(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
+// Launch geometry of a shape: parts P, slices NSL, waves WS and stages S.
+struct Plan {
+  int P = 0, NSL = 0, WS = 0, S = 0;
+  size_t lds = 0;
+};
+
+// Bytes of one stage and vector memory operations per stage (as Geo computes them).
+size_t stage_bytes(int P, int NSL, int g, bool sym, int* ops) {
+  const int KR = P * NSL * 32, NG = KR / g;
+  const int NSI = (8 * NG + 63) / 64, NZI = sym ? 0 : (4 * NG + 63) / 64;
+  *ops = 4 * (KR / 512) + NSI + NZI;
+  return (size_t)16 * (KR / 2) + 256u * NSI + 256u * NZI;
+}
+
+Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym) {
+  Plan pl;
+  if (M < 1 || M > 16 || !(g == 32 || g == 64 || g == 128)) return pl;
+  if (N * (K / 2) >= ((int64_t)1 << 32) || M * K * 2 >= ((int64_t)1 << 32)) return pl;
+  const int P = M <= 4 ? 4 : (M <= 8 ? 2 : 1);
+  // slices per part: 16 (64 registers of X), fewer for small groups at several parts (their
+  // many tiles per stage would not fit the registers), fewer again when K is short, so that
+  // a workgroup has four waves where K allows
+  int NSL = 16;
+  if ((g == 32 && P >= 2) || (g == 64 && P == 4)) NSL = 8;
+  while (NSL > 4 && P * (NSL / 2) >= 16 && (K % (P * NSL * 32) != 0 || K / (P * NSL * 32) < 4)) NSL /= 2;
+  const int64_t KR = (int64_t)P * NSL * 32;
+  if (K % KR != 0 || KR < 512 || KR / g < 4) return pl;
+  const int64_t WS = K / KR;
+  if (WS < 1 || WS > kMaxWaves) return pl;
+  int ops = 0;
+  const size_t st = stage_bytes(P, NSL, g, sym, &ops);
+  const size_t red = (size_t)2 * WS * kRedBytes;
+  int S = (int)((kLdsMax - red) / ((size_t)WS * st));
+  if (S > 4) S = 4;
+  while (S > 2 && (S - 1) * ops > 63) --S;             // the stage waits fit the counter
+  if (S < 2) return pl;
+  pl.P = P; pl.NSL = NSL; pl.WS = (int)WS; pl.S = S;
+  pl.lds = (size_t)WS * S * st + red;
+  return pl;
+}
+
+template <int P, int NSL, int TK, bool SYM>
+hipError_t launch_one(const Plan& pl, const void* X, int M, int64_t N, int64_t K, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
-  constexpr int TK = 32 * DPT, P = 32 / DPT;
-  const size_t lds = lds_bytes(M, K, g);
-  // More than 64 KiB of dynamic LDS has to be enabled per kernel (thread-safe one-time init).
-  static const hipError_t attr = [] {
-    const void* kernels[] = {reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true, kWideWaves>),
-                             reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, true, kMaxWaves>),
-                             reinterpret_cast<const void*>(&decode_kernel<DPT, SYM, false, kMaxWaves>)};
-    for (const void* k : kernels) {
-      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }();
+  const auto kernel = decode_kernel<P, NSL, TK, SYM>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
   if (attr != hipSuccess) return attr;
   const int64_t NB = (N + 15) / 16;
-  const int64_t T = K / TK;
-  const int64_t G = K / g;
-  // Row blocks per resident block (RB) and waves splitting each one's K (KS), for a block of at
-  // most maxw waves: with fewer row blocks than waves, the spare waves split K, at most
-  // kMaxWaves ways, with at most kMaxWaves partial sums in LDS.
-  auto split = [&](int maxw, int& RB, int& KS) {
-    const int64_t rb = (NB + num_cus - 1) / num_cus;
-    if (rb >= maxw) {
-      RB = maxw;
-      KS = 1;
-      return;
-    }
-    RB = (int)rb;
-    KS = min(maxw / RB, kMaxWaves);
-    while (KS > 1 && (T % KS != 0 || T / KS < 2 || RB * (KS - 1) > kMaxWaves)) --KS;
-  };
-  // Window loads: one group per tile, every wave's tile range a whole number of windows, and
-  // 4-byte-aligned windows of scales and zeros in every row.
-  auto windows = [&](int KS) {
-    return (g == TK) && ((T / KS) % P == 0) && (T % KS == 0) && (G % (P < 16 ? P : 16) == 0);
-  };
-  int RB, KS;
-  split(kWideWaves, RB, KS);
-  const bool wide = windows(KS);
-  if (!wide) split(kMaxWaves, RB, KS);
-  const bool win = wide || windows(KS);
-  const int64_t groups = (NB + RB - 1) / RB;
-  const int64_t blocks = groups < num_cus ? groups : num_cus;
-  const int threads = RB * KS * kWave;
-#define Q4_DECODE_LAUNCH(WINV, MAXWV)                                                              \
-  hipLaunchKernelGGL((decode_kernel<DPT, SYM, WINV, MAXWV>), dim3((unsigned)blocks), dim3((unsigned)threads), \
-                     lds, stream, (const uint16_t*)X, M, (int)N, (int)K, g, (const uint8_t*)packed,          \
-                     (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y, RB, KS)
-  if (wide) Q4_DECODE_LAUNCH(true, kWideWaves);
-  else if (win) Q4_DECODE_LAUNCH(true, kMaxWaves);
-  else Q4_DECODE_LAUNCH(false, kMaxWaves);
-#undef Q4_DECODE_LAUNCH
+  const int64_t blocks = NB < num_cus ? NB : num_cus;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3((unsigned)(pl.WS * kWave)), pl.lds, stream,
+                     (const uint16_t*)X, M, (int)N, (int)K, (const uint8_t*)packed, (const uint16_t*)scales,
+                     (const uint8_t*)zeros, (uint16_t*)Y, pl.S);
   return hipGetLastError();
 }
 
+// (plan_for never picks 16 slices for g = 32 at two or four parts, or for g = 64 at four parts)
+template <int P, int NSL, bool SYM>
+hipError_t launch_tk(const Plan& pl, int g, const void* X, int M, int64_t N, int64_t K, const void* packed,
+                     const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
+  if constexpr (!(NSL == 16 && P >= 2))
+    if (g == 32) return launch_one<P, NSL, 32, SYM>(pl, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
+  if constexpr (!(NSL == 16 && P == 4))
+    if (g == 64) return launch_one<P, NSL, 64, SYM>(pl, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
+  if (g == 128) return launch_one<P, NSL, 128, SYM>(pl, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
+  return hipErrorInvalidValue;
+}
+
 template <bool SYM>
-hipError_t launch_mode(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
+hipError_t launch_mode(const Plan& pl, int g, const void* X, int M, int64_t N, int64_t K, const void* packed,
                        const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
-  if (g == 32) return launch_cfg<1, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
-  if (g == 64) return launch_cfg<2, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
-  return launch_cfg<4, SYM>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+#define Q4_DECODE(PV, NV)                                                                                    \
+  if (pl.P == PV && pl.NSL == NV)                                                                            \
+    return launch_tk<PV, NV, SYM>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
+  Q4_DECODE(1, 16)
+  Q4_DECODE(2, 16)
+  Q4_DECODE(2, 8)
+  Q4_DECODE(4, 16)
+  Q4_DECODE(4, 8)
+  Q4_DECODE(4, 4)
+#undef Q4_DECODE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t decode_lds_bytes(int64_t M, int64_t K, int g) { return lds_bytes(M, K, g); }
-
 bool decode_fits(int64_t M, int64_t N, int64_t K, int g) {
-  (void)N;
-  if (M < 1 || M > 16) return false;
-  if (!(g == 32 || g == 64 || g % 128 == 0)) return false;
-  return decode_lds_bytes(M, K, g) <= 160 * 1024;
+  // the symmetric format needs fewer bytes per stage, so an asymmetric fit covers both
+  return plan_for(M, N, K, g, false).P != 0;
 }
 
 hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                          const void* packed, const void* scales, const void* zeros, void* Y,
                          int num_cus, hipStream_t stream) {
-  return sym ? launch_mode<true>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream)
-             : launch_mode<false>(X, M, N, K, g, packed, scales, zeros, Y, num_cus, stream);
+  const Plan pl = plan_for(M, N, K, g, sym);
+  if (pl.P == 0) return hipErrorInvalidValue;
+  return sym ? launch_mode<true>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream)
+             : launch_mode<false>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
 }
 
 }  // namespace q4

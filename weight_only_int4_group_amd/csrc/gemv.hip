@@ -4,31 +4,33 @@
 // operands ("LLM Weight Quantization - GPTQ, AWQ, SmoothQuant, FP8 & INT4/INT8 Trade-offs",
 // "The vocabulary"); decode is bound by the bytes of the weights ("Overview": every output
 // token reads every weight).  Dequantisation is x_hat = scale * (q - z) ("DL S067 ·
+// Quantization", §1), with one scale and zero-point per group of g weights along K ("Model
 // Quantization", §1).
 //
-// Arithmetic.  Y[m, n] = sum_chunks scale * (sum_{k in chunk} x[m, k] q[n, k] - z sum_k x[m, k]),
-// chunks of 32 weights never straddling a group, with
-//   * the codes q used as exact fp16 subnormals: a nibble masked into the low bits of a 16-bit
-//     half is the fp16 value q * 2^-24 (a nibble in bits 4..7 gives 16 q * 2^-24), two weights
-//     per instruction and no bias to remove;
-//   * x converted to fp16 exactly, per (row of X, chunk), after scaling by a power of two 2^e
-//     that puts the chunk's largest |x| in [2^14, 2^15) (positions that meet a 16 q weight carry
-//     2^(e-4)); the chunk sums of the scaled x are precomputed once per block;
-//   * products x q are exact; v_dot2 sums them in fp32; the zero-point enters as one fma per
-//     chunk (sum x q - z sum x), the chunk result is multiplied by 2^24, 2^-e and the scale in
-//     fp32 and accumulated per lane; lanes are combined by an fp32 wave reduction and Y is rounded to
-//     bf16 once.
-// Beyond fp32 summation and the bf16 output, the rounding of the two chunk sums adds at most
-// about 2^-24 * 30 * scale * sum|x| per chunk (the q and z terms are each at most 15 sum|x|);
-// x elements smaller than 2^-27 of their chunk's maximum lose low bits in fp16.
+// Work split.  A wave owns one output row n at a time.  Each 1 KiB of the row's codes is one
+// load instruction (64 lanes x 16 bytes, contiguous); lane l = kq * 16 + n reads the 16-byte
+// chunk 4 n + kq of it (32 weights), so the four lanes n, n + 16, n + 32, n + 48 together hold
+// 128 consecutive weights.  One persistent block of 12 or 16 waves per compute unit converts X
+// once into LDS; with M = 1 a lane meets the same chunks of X in every row, so it keeps them
+// in registers.  Each wave keeps two or three rows in flight: the loads of the next rows are
+// issued before a row is computed, and the first rows are requested before the conversion of
+// X, so HBM latency overlaps it.
 //
-// Work split.  A wave owns one output row n at a time; lane l owns the 16-byte packed chunks
-// c = l + 64 j (32 weights each), so one load instruction reads 1 KiB of a row contiguously.
-// One persistent block of 16 waves per compute unit converts X once into LDS (laid out in
-// four planes so that a lane's 16-byte reads of consecutive chunks hit distinct banks).
-// Each wave keeps three rows in flight: the loads of rows n + nw and n + 2 nw are issued
-// before row n is computed, and the first three rows are requested before the conversion of
-// X, so HBM latency overlaps it.  Row sums are reduced with DPP row operations and lane reads.
+// Arithmetic (every product exact, sums in fp32, Y rounded once to bf16):
+//   * (q - z) is formed exactly in fp16: the nibble OR-ed into the mantissa of 1024.0, minus
+//     1024 + z (nibbles in bits 4..7 give 16 (q - z));
+//   * x is converted to fp16 exactly after scaling each (row of X, 128-weight block) by a
+//     power of two 2^e that puts its largest |x| in [2^14, 2^15); the positions that meet a
+//     16 (q - z) weight carry 2^(e - 4);
+//   * g a multiple of 128: one v_mfma_f32_16x16x32_f16 per dword of codes, with each lane's A
+//     operand the x of its own weights: the diagonal D[n][n] sums the exact products of the
+//     four lanes of a 128-weight block (one group), and the other entries are not used; the
+//     block's sum is multiplied by its scale and 2^-e and accumulated in fp32;
+//   * other g (32, 64, 96): v_dot2_f32_f16 of the same exact operands per 32-weight chunk;
+//   * X whose fp16 conversion would lose a bit (a nonzero |x| 2^(e-4) below 2^-14, fp16's
+//     smallest normal: a dynamic range above about 2^24 inside one 128-weight block) takes an
+//     exact fp32 path instead: (q - z) and x converted to fp32, one fma per weight.  The
+//     choice is one flag for the whole launch (every block stages the same X).
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -36,6 +38,8 @@
 
 namespace q4 {
 namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Sum over the 64 lanes of a wave, returned uniformly.
 __device__ __forceinline__ float dpp_row_sum(float v) {
@@ -54,6 +58,30 @@ __device__ __forceinline__ float wave_total(float v) {
   return (a + b) + (c + d);
 }
 
+// Max (or min) over each aligned quad of lanes, returned to every lane of the quad.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  return fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+
+// Four fp16 pairs (q - z) of one dword of codes (8 nibbles): nibble OR-ed into 1024.0 minus
+// 1024 + z (1024 + 16 z for the nibbles in bits 4..7).  Slot order (k0, k4, k1, k5, k2, k6,
+// k3, k7); the odd k carry 16 (q - z).
+template <bool SYM>
+__device__ __forceinline__ f16x8 dequant(uint32_t dw, uint32_t bias, f16x2 b1, f16x2 b16) {
+  if (SYM) dw ^= 0x88888888u;                         // two's complement nibble -> q + 8
+  const uint32_t d8 = dw >> 8;
+  const f16x2 h0 = as_f16x2((dw & 0x000F000Fu) | bias) - b1;
+  const f16x2 h1 = as_f16x2((dw & 0x00F000F0u) | bias) - b16;
+  const f16x2 h2 = as_f16x2((d8 & 0x000F000Fu) | bias) - b1;
+  const f16x2 h3 = as_f16x2((d8 & 0x00F000F0u) | bias) - b16;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 // Loaded values stay untouched until use, so the loads of later rows remain in flight.
 // SHARE (a row has at most 64 groups): lane l loads the scale and zero of group l only, and a
 // lane reads the values of its chunks' groups from the owning lanes (ds_bpermute), i.e. two
@@ -66,7 +94,8 @@ struct RowBuf {
   uint32_t z[SHARE ? 1 : J];      // zero-point
 };
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
+// DIAG: g is a multiple of 128 (the matrix-core diagonal form); else v_dot2 per chunk.
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING, bool DIAG>
 __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -76,6 +105,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   const int G = K / g;
   const int cpg = g >> 5;                     // chunks per group
   const int lane = threadIdx.x & (kWave - 1);
+  const int pi = 4 * (lane & 15) + (lane >> 4);   // this lane's chunk inside each 1 KiB
   const int64_t wpb = BLOCK / kWave;
   const int64_t nw = (int64_t)gridDim.x * wpb;
   const int64_t n0 = (int64_t)blockIdx.x * wpb +
@@ -85,15 +115,14 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   bool cval[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int c = lane + kWave * j;
+    const int c = pi + kWave * j;
     cval[j] = FULL || c < C;
     goff[j] = (cval[j] ? c : C - 1) / cpg;
   }
 
-  // Loads are unconditional, from clamped (always valid) chunks: a load under a branch makes the
-  // compiler wait for every load in flight, prefetched rows included, before the next use.  A
-  // row past the end gets an empty buffer resource, so its loads read no memory and return 0;
-  // chunks past the row end are skipped when computed and rows past N are not stored.
+  // Loads are unconditional.  A row past the end gets an empty buffer resource, so its loads
+  // read no memory and return 0; chunks past the row end lie past the resource's end (read 0
+  // and meet x = 0), and rows past N are not stored.
   const int gown = min(lane, G - 1);           // SHARE: the group this lane loads
   auto load = [&](RowBuf<J, SHARE>& b, int64_t row) {
     const bool live = row < N;                  // wave-uniform
@@ -103,7 +132,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const __amdgpu_buffer_rsrc_t rz = buffer_over(zeros + r * G, live ? (uint32_t)G : 0u);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+      const int c = pi + kWave * j;
       b.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * c, 0, kBufferNT));
       if (!SHARE) {
         b.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * goff[j], 0, 0);
@@ -122,119 +151,209 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   load(b1, n0 + nw);
   if constexpr (RING == 3) load(b2, n0 + 2 * nw);
 
-  // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, chunk), four planes of 16 bytes ----
-  // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t;
-  // fs holds 2^-e and sx the chunk sum of the scaled x times 2^-24.
-  u32x4* xs = lds4;                                           // [M][4][C]
+  // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, 128-weight block), four planes ----
+  // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t; fs
+  // holds 2^-e per chunk (the same for the four chunks of a block).  One thread per chunk; the
+  // four chunks of a block are an aligned quad of lanes (C is a multiple of 4 or the block is
+  // the row's last), so the block's range is a quad reduction.
+  u32x4* xs = lds4;                                                 // [M][4][C]
   float* fs = reinterpret_cast<float*>(lds4 + (size_t)M * 4 * C);   // [M][C]
-  float* sx = fs + (size_t)M * C;                                   // [M][C]
-  for (int idx = threadIdx.x; idx < M * C; idx += BLOCK) {
-    const int m = idx / C;
-    const int c = idx - m * C;
-    const u32x4* xp = reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)c * 32);
+  int lossy = 0;
+  const int total = M * C;
+  const int trips = (total + BLOCK - 1) / BLOCK;
+  for (int it = 0; it < trips; ++it) {          // all lanes take part in every quad reduction
+    const int idx = it * BLOCK + (int)threadIdx.x;
+    const bool act = idx < total;
+    const int m = act ? idx / C : 0;
+    const int c = act ? idx - m * C : 0;
     u32x4 v[4];
 #pragma unroll
-    for (int o = 0; o < 4; ++o) v[o] = xp[o];
-    float amax = 0.0f;
+    for (int o = 0; o < 4; ++o) v[o] = act ? reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)c * 32)[o]
+                                           : u32x4{0u, 0u, 0u, 0u};
+    float amax = 0.0f, amin = __builtin_inff();
 #pragma unroll
     for (int o = 0; o < 4; ++o)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[o][i])), fabsf(bf16_hi(v[o][i]))));
+      for (int i = 0; i < 4; ++i) {
+        const float a = fabsf(bf16_lo(v[o][i])), bb = fabsf(bf16_hi(v[o][i]));
+        amax = fmaxf(amax, fmaxf(a, bb));
+        amin = fminf(amin, fminf(a > 0.0f ? a : __builtin_inff(), bb > 0.0f ? bb : __builtin_inff()));
+      }
+    // the block of chunk c is chunks 4 (c / 4) .. + 3 of the same row m: lanes 4 (idx / 4) .. + 3
+    // when C is a multiple of 4 (the rows then start on quad boundaries); otherwise per chunk
+    if ((C & 3) == 0) {
+      amax = quad_max(amax);
+      amin = quad_min(amin);
+    }
     int e = 0;
-    if (amax > 0.0f) {
-      int E;
-      frexpf(amax, &E);                       // amax = f * 2^E, f in [0.5, 1)
-      e = min(15 - E, 100);                   // amax * 2^e in [2^14, 2^15)
-    }
-    float sum = 0.0f;
+    if (amax > 0.0f) e = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);   // amax 2^e in [2^14, 2^15)
+    lossy |= (int)(act && amin < __builtin_inff() && __builtin_ldexpf(amin, e) < 0x1p-10f);
+    if (act) {
 #pragma unroll
-    for (int o = 0; o < 4; ++o) {
-      // octet o: x0..x7 = lo/hi halves of v[o][0..3]
-      const u32x4 q = v[o];
-      const f16x2 p0 = {(_Float16)ldexpf(bf16_lo(q[0]), e), (_Float16)ldexpf(bf16_lo(q[2]), e)};
-      const f16x2 p1 = {(_Float16)ldexpf(bf16_hi(q[0]), e - 4), (_Float16)ldexpf(bf16_hi(q[2]), e - 4)};
-      const f16x2 p2 = {(_Float16)ldexpf(bf16_lo(q[1]), e), (_Float16)ldexpf(bf16_lo(q[3]), e)};
-      const f16x2 p3 = {(_Float16)ldexpf(bf16_hi(q[1]), e - 4), (_Float16)ldexpf(bf16_hi(q[3]), e - 4)};
-      xs[((size_t)m * 4 + o) * C + c] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
-      // sum of the scaled x as the dot products see them (the x16 positions count 16 times)
-      sum += (float)p0[0] + (float)p0[1] + (float)p2[0] + (float)p2[1] +
-             16.0f * ((float)p1[0] + (float)p1[1] + (float)p3[0] + (float)p3[1]);
+      for (int o = 0; o < 4; ++o) {
+        const u32x4 q = v[o];
+        const f16x2 p0 = {(_Float16)__builtin_ldexpf(bf16_lo(q[0]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[2]), e)};
+        const f16x2 p1 = {(_Float16)__builtin_ldexpf(bf16_hi(q[0]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[2]), e - 4)};
+        const f16x2 p2 = {(_Float16)__builtin_ldexpf(bf16_lo(q[1]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[3]), e)};
+        const f16x2 p3 = {(_Float16)__builtin_ldexpf(bf16_hi(q[1]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[3]), e - 4)};
+        xs[((size_t)m * 4 + o) * C + c] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
+      }
+      fs[idx] = __builtin_ldexpf(1.0f, -e);
     }
-    fs[idx] = ldexpf(1.0f, -e);
-    sx[idx] = ldexpf(sum, -24);
   }
-  __syncthreads();
+  // one flag for the launch: every block stages the same X
+  const bool exact = __syncthreads_or(lossy) != 0;
 
   // XREG (one row of X): a lane meets the same J chunks of X in every row of W, so it copies
-  // them, with their factors, from LDS into registers once and reads no LDS per row.
+  // them, with their factors, from LDS into registers once and reads no LDS per row.  Chunks
+  // past the row end are 0.
   constexpr bool XREG = MT == 1 && (J <= 2 || (J == 4 && (BLOCK <= 768 || RING <= 2)));   // register budget
   u32x4 xr[XREG ? J : 1][4];
-  float xf[XREG ? J : 1], xsum[XREG ? J : 1];
+  float xf[XREG ? J : 1];
   if constexpr (XREG) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+      const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
 #pragma unroll
-      for (int o = 0; o < 4; ++o) xr[j][o] = xs[(size_t)o * C + c];
+      for (int o = 0; o < 4; ++o) xr[j][o] = cval[j] ? xs[(size_t)o * C + c] : u32x4{0u, 0u, 0u, 0u};
       xf[j] = fs[c];
-      xsum[j] = sx[c];
     }
   }
+  uint32_t bias = 0x64006400u;
+  asm volatile("" : "+v"(bias));   // keep in a VGPR: (x & mask) | bias -> one v_and_or_b32
+  // the lanes whose D fragment holds a diagonal entry D[n][n]: rows 4 (l / 16) .. + 3 of column
+  // l % 16 contain n when l / 16 == (l % 16) / 4; the entry is element (l % 16) % 4
+  const bool diag_lane = (lane >> 4) == ((lane & 15) >> 2);
 
-  auto process = [&](const RowBuf<J, SHARE>& b, int64_t row) {
-    float acc[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    // SHARE: every lane takes part in the exchange (all 64 lanes active), before any branch.
-    uint32_t shared[SHARE ? J : 1];
+  auto group_sz = [&](const RowBuf<J, SHARE>& b, uint32_t (&sb)[J], uint32_t (&zb)[J]) {
     if (SHARE) {
       const uint32_t sz = SYM ? b.s[0] : (b.s[0] | (b.z[0] << 16));   // one word per group
 #pragma unroll
-      for (int j = 0; j < J; ++j) shared[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * goff[j], (int)sz);
-    }
+      for (int j = 0; j < J; ++j) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * goff[j], (int)sz);
+        sb[j] = w & 0xffffu;
+        zb[j] = SYM ? 8u : w >> 16;
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (cval[j]) {
-        const int c = lane + kWave * j;
-        uint32_t sbits, zbits;
-        if (SHARE) {
-          sbits = shared[j] & 0xffffu;
-          zbits = shared[j] >> 16;
-        } else {
-          sbits = b.s[j];
-          zbits = SYM ? 8u : b.z[j];
+      for (int j = 0; j < J; ++j) {
+        sb[j] = b.s[j];
+        zb[j] = SYM ? 8u : b.z[j];
+      }
+    }
+  };
+
+  auto process_fast = [&](const RowBuf<J, SHARE>& b, int64_t row) {
+    uint32_t sb[J], zb[J];
+    group_sz(b, sb, zb);
+    float tot[MT];
+    if constexpr (DIAG) {
+      f32x4 acc[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
+        const f16x2 b1 = as_f16x2((0x6400u + zb[j]) * 0x00010001u);
+        const f16x2 b16 = as_f16x2((0x6400u + 16u * zb[j]) * 0x00010001u);
+        f32x4 pacc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          const f16x8 bw = dequant<SYM>(b.w[j][o], bias, b1, b16);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 xv = XREG ? xr[XREG ? j : 0][o]
+                                  : (cval[j] ? xs[((size_t)m * 4 + o) * C + c] : u32x4{0u, 0u, 0u, 0u});
+            pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, xv), bw, pacc[m], 0, 0, 0);
+          }
         }
-        const float zf = SYM ? 8.0f : (float)zbits;
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float f = s * (XREG ? xf[XREG ? j : 0] : fs[m * C + c]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[m][r] = __builtin_fmaf(pacc[m][r], f, acc[m][r]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int el = lane & 3;
+        const float dv = el == 0 ? acc[m][0] : (el == 1 ? acc[m][1] : (el == 2 ? acc[m][2] : acc[m][3]));
+        tot[m] = wave_total(diag_lane ? dv : 0.0f);
+      }
+    } else {
+      float acc[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
+        const f16x2 b1 = as_f16x2((0x6400u + zb[j]) * 0x00010001u);
+        const f16x2 b16 = as_f16x2((0x6400u + 16u * zb[j]) * 0x00010001u);
         // four independent partial sums per row of X (one per dword) keep the dot2 chains short
         float d[MT][4];
 #pragma unroll
         for (int o = 0; o < 4; ++o) {
-          uint32_t dw = b.w[j][o];
-          if (SYM) dw ^= 0x88888888u;          // two's complement nibble -> q + 8
-          const uint32_t d8 = dw >> 8;
-          const f16x2 h0 = as_f16x2(dw & 0x000F000Fu);   // q k0, k4   (x 2^-24)
-          const f16x2 h1 = as_f16x2(dw & 0x00F000F0u);   // 16 q k1, k5
-          const f16x2 h2 = as_f16x2(d8 & 0x000F000Fu);   // q k2, k6
-          const f16x2 h3 = as_f16x2(d8 & 0x00F000F0u);   // 16 q k3, k7
+          const f16x8 bw = dequant<SYM>(b.w[j][o], bias, b1, b16);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = XREG ? xr[XREG ? j : 0][o] : xs[((size_t)m * 4 + o) * C + c];
-            float t = __builtin_amdgcn_fdot2(h0, as_f16x2(xv[0]), 0.0f, false);
-            t = __builtin_amdgcn_fdot2(h1, as_f16x2(xv[1]), t, false);
-            t = __builtin_amdgcn_fdot2(h2, as_f16x2(xv[2]), t, false);
-            d[m][o] = __builtin_amdgcn_fdot2(h3, as_f16x2(xv[3]), t, false);
+            const u32x4 xv = XREG ? xr[XREG ? j : 0][o]
+                                  : (cval[j] ? xs[((size_t)m * 4 + o) * C + c] : u32x4{0u, 0u, 0u, 0u});
+            float t = __builtin_amdgcn_fdot2(f16x2{bw[0], bw[1]}, as_f16x2(xv[0]), 0.0f, false);
+            t = __builtin_amdgcn_fdot2(f16x2{bw[2], bw[3]}, as_f16x2(xv[1]), t, false);
+            t = __builtin_amdgcn_fdot2(f16x2{bw[4], bw[5]}, as_f16x2(xv[2]), t, false);
+            d[m][o] = __builtin_amdgcn_fdot2(f16x2{bw[6], bw[7]}, as_f16x2(xv[3]), t, false);
           }
         }
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const float sxv = XREG ? xsum[XREG ? j : 0] : sx[m * C + c];
-          const float fsv = XREG ? xf[XREG ? j : 0] : fs[m * C + c];
-          const float r = __builtin_fmaf(-zf, sxv, (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]));
-          // 2^24 and 2^-e applied as two exact power-of-two products: no overflow unless the
-          // chunk's dot product itself overflows
-          acc[m] = __builtin_fmaf((r * 16777216.0f) * fsv, s, acc[m]);
+          const float f = s * (XREG ? xf[XREG ? j : 0] : fs[m * C + c]);
+          acc[m] = __builtin_fmaf((d[m][0] + d[m][1]) + (d[m][2] + d[m][3]), f, acc[m]);
         }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) tot[m] = wave_total(acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (lane == m && m < M) Y[(size_t)m * N + row] = f32_to_bf16_bits(tot[m]);
+  };
+
+  // Exact path: (q - z) and x in fp32, one fma per weight (exact products), x read from X.
+  const __amdgpu_buffer_rsrc_t rx = buffer_over(X, (uint32_t)M * (uint32_t)K * 2u);
+  auto process_exact = [&](const RowBuf<J, SHARE>& b, int64_t row) {
+    uint32_t sb[J], zb[J];
+    group_sz(b, sb, zb);
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = pi + kWave * j;
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
+      const float zf = (float)zb[j];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float part = 0.0f;
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          uint32_t dw = b.w[j][o];
+          if (SYM) dw ^= 0x88888888u;
+          // chunks past the row end lie past the resource's end (X row m, or beyond M rows): 0
+          const uint32_t off = cval[j] ? 2u * ((uint32_t)m * (uint32_t)K + (uint32_t)c * 32u + 8u * (uint32_t)o)
+                                       : 0xffffffc0u;
+          const u32x4 xv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float q = (float)((dw >> (4 * i)) & 15u);
+            const float x = (i & 1) ? bf16_hi(xv[i >> 1]) : bf16_lo(xv[i >> 1]);
+            part = __builtin_fmaf(x, q - zf, part);
+          }
+        }
+        acc[m] = __builtin_fmaf(part, s, acc[m]);
       }
     }
 #pragma unroll
@@ -242,6 +361,11 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
       const float tot = wave_total(acc[m]);
       if (lane == m && m < M) Y[(size_t)m * N + row] = f32_to_bf16_bits(tot);
     }
+  };
+
+  auto process = [&](const RowBuf<J, SHARE>& b, int64_t row) {
+    if (exact) process_exact(b, row);           // block-uniform
+    else process_fast(b, row);
   };
 
   // sched_barrier keeps the compiler from hoisting one row's work into another's, which would
@@ -282,14 +406,14 @@ int64_t resident_blocks(Kernel kernel, int block, size_t lds, std::atomic<uint64
   return nb;
 }
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING, bool DIAG>
 hipError_t launch_one(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus,
                       hipStream_t stream) {
   static std::atomic<uint64_t> memo{0};
-  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING>;
+  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING, DIAG>;
   const int64_t C = K >> 5;
-  const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 8;
+  const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 4;
   const int64_t wpb = BLOCK / kWave;
   int64_t blocks = (N + wpb - 1) / wpb;
   const int64_t cap = (int64_t)num_cus * resident_blocks(kernel, BLOCK, lds, memo);
@@ -306,9 +430,13 @@ hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sy
                       int num_cus, hipStream_t stream) {
   const bool full = (K >> 5) == kWave * J;
   const bool share = K / g <= kWave;
-#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                     \
-  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING>(X, M, N, K, g, packed, scales, \
-                                                             zeros, Y, num_cus, stream)
+  const bool diag = g % 128 == 0;
+#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                            \
+  if (diag) return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING, true>(X, M, N, K, g, packed, \
+                                                                            scales, zeros, Y,       \
+                                                                            num_cus, stream);       \
+  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING, false>(X, M, N, K, g, packed, scales,  \
+                                                                    zeros, Y, num_cus, stream)
 #define Q4_GEMV_SHARE(SYMV, FULLV)                                                           \
   if (share) { Q4_GEMV_ONE(SYMV, FULLV, true); } else { Q4_GEMV_ONE(SYMV, FULLV, false); }
   if (sym) {

@@ -69,9 +69,9 @@ hipError_t launch_gemv(const void* X, int M, int64_t N, int64_t K, int g, bool s
                        const void* packed, const void* scales, const void* zeros, void* Y,
                        int num_cus, hipStream_t stream);
 
-// Decode on fp16 MFMA for 1 <= M <= 16 (K <= 8192, g in {32, 64} or a multiple of 128, X staged
-// in LDS).
-size_t decode_lds_bytes(int64_t M, int64_t K, int g);
+// Decode on the matrix cores for 1 <= M <= 16: g in {32, 64, 128}; K a whole number of the
+// waves' K ranges (512 k at 9 <= M <= 16, 1024 at M <= 8, 2048 at M <= 4, shorter ranges
+// when K is small), at most 16 ranges.
 bool decode_fits(int64_t M, int64_t N, int64_t K, int g);
 hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                          const void* packed, const void* scales, const void* zeros, void* Y,
