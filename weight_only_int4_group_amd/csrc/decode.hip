@@ -224,36 +224,42 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   }
 
   // ---- stage copies ----
+  // Each row block's copies go through resources based at its first row and this wave's K
+  // range, holding the bytes up to the end of the matrix: rows past N then lie past the
+  // resource's end and read as 0.  The range check covers the vector offset only, so every
+  // row offset goes there; the scalar offset carries the 256-byte segment inside the row.
   // Codes: copy i covers rows 4 (i % 4) + lane / 16 and the 256-byte segment i / 4; lane l
-  // reads chunk (l % 16) ^ row of it.  The per-lane part of the offset is the same for every
-  // copy up to an XOR of 64 (i % 4) (rows are a multiple of 256 bytes long); the rest is
-  // wave-uniform.  Rows past N lie past the resource's end and read as 0.
+  // reads chunk (l % 16) ^ row of it, i.e. the chunk bits XOR 64 (i % 4) bytes (rows are a
+  // multiple of 256 bytes long).
   const uint32_t rowbytes = (uint32_t)K / 2u;
-  const u32x4 rw = buffer_words(packed, (uint32_t)N * rowbytes);
-  const u32x4 rs = buffer_words(scales, (uint32_t)N * (uint32_t)G * 2u);
-  const u32x4 rz = buffer_words(zeros, SYM ? 0u : (uint32_t)N * (uint32_t)G);
   const uint32_t code_lane = (uint32_t)(lane >> 4) * rowbytes + 16u * (uint32_t)((lane & 15) ^ (lane >> 4));
+  uint32_t cv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cv[q] = (code_lane ^ (64u * (uint32_t)q)) + 4u * (uint32_t)q * rowbytes;
   // scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2); zeros:
   // dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
   // stage's 16 rows in LDS)
-  const uint32_t s_lane = (uint32_t)(lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
-  const uint32_t z_lane = (uint32_t)(lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
+  uint32_t sv[Gm::NSI], zv[Gm::NZI > 0 ? Gm::NZI : 1];
+#pragma unroll
+  for (int q = 0; q < Gm::NSI; ++q)
+    sv[q] = (uint32_t)(q * (128 / NG) + lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
+#pragma unroll
+  for (int q = 0; q < Gm::NZI; ++q)
+    zv[q] = (uint32_t)(q * (256 / NG) + lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
   auto issue = [&](int slot, int rb) {
     const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
-    const uint32_t n0 = (uint32_t)rb * 16u;
+    const uint32_t n0 = (uint32_t)rb * 16u;                          // rb < NB
+    const uint32_t g0 = n0 * (uint32_t)G + (uint32_t)(K0 / TK);      // first group of the range
+    const u32x4 rw = buffer_words(packed + (size_t)n0 * rowbytes + (size_t)(K0 / 2),
+                                  ((uint32_t)N - n0) * rowbytes - (uint32_t)(K0 / 2));
+    const u32x4 rs = buffer_words(scales + g0, ((uint32_t)N * (uint32_t)G - g0) * 2u);
+    const u32x4 rz = buffer_words(zeros + g0, SYM ? 0u : (uint32_t)N * (uint32_t)G - g0);
 #pragma unroll
-    for (int i = 0; i < Gm::NCI; ++i)
-      dma16(rw, code_lane ^ (64u * (uint32_t)(i & 3)),
-            (n0 + 4u * (uint32_t)(i & 3)) * rowbytes + (uint32_t)K0 / 2u + 256u * (uint32_t)(i >> 2),
-            st + 1024u * (uint32_t)i);
+    for (int i = 0; i < Gm::NCI; ++i) dma16(rw, cv[i & 3], 256u * (uint32_t)(i >> 2), st + 1024u * (uint32_t)i);
 #pragma unroll
-    for (int q = 0; q < Gm::NSI; ++q)
-      dma4(rs, s_lane, ((n0 + (uint32_t)(q * (128 / NG))) * (uint32_t)G + (uint32_t)(K0 / TK)) * 2u,
-           st + Gm::SOFF + 256u * (uint32_t)q);
+    for (int q = 0; q < Gm::NSI; ++q) dma4(rs, sv[q], 0u, st + Gm::SOFF + 256u * (uint32_t)q);
 #pragma unroll
-    for (int q = 0; q < Gm::NZI; ++q)
-      dma4(rz, z_lane, (n0 + (uint32_t)(q * (256 / NG))) * (uint32_t)G + (uint32_t)(K0 / TK),
-           st + Gm::ZOFF + 256u * (uint32_t)q);
+    for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
   };
 
   const int stride = gridDim.x;
