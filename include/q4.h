@@ -260,7 +260,7 @@ int q4_quantize_rtn8(const void* W, int64_t N, int64_t K, int32_t g, int32_t mod
  * aligned) in place of packed.  kernel:
  *   Q4_KERNEL_AUTO  Q4_KERNEL_GEMV when it fits, else Q4_KERNEL_GEMM (see q4_select_kernel_w8);
  *   Q4_KERNEL_GEMV  decode GEMV for 1 <= M <= 4 with X staged in LDS, which needs
- *                   2.25 M K <= 160 KiB (e.g. M <= 4 at K = 16384, M <= 2 at K = 28672): exact
+ *                   2.25 M K + 16 <= 160 KiB (e.g. M <= 4 at K = 16384, M <= 2 at K = 28672): exact
  *                   (q - z) in fp16 against x scaled by a power of two per 16 weights;
  *   Q4_KERNEL_GEMM  bf16 MFMA GEMM on dequantised bf16 tiles, any M;
  *   Q4_KERNEL_DECODE  not provided for 8-bit codes.

@@ -28,7 +28,7 @@ def _gpu():
 def kernels_w8(M, K):
     """Every kernel that can run this shape (the rules stated in include/q4.h)."""
     ks = ["auto", "gemm"]
-    if 1 <= M <= 4 and 2 * M * K + 4 * M * (K // 16) <= 160 * 1024:
+    if 1 <= M <= 4 and 2 * M * K + 4 * M * (K // 16) + 16 <= 160 * 1024:
         ks.append("gemv")
     return tuple(ks)
 
@@ -162,6 +162,19 @@ def test_matmul_w8_ragged(M, N, K, g):
     X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
     for mode in ("asym", "sym"):
         _check_full8(X_bits, W_bits, g, mode, "ragged", kernels_w8(M, K))
+
+
+@pytest.mark.parametrize("log2_ratio", [12, 24, 31, 36, 60])
+@pytest.mark.parametrize("N,K,g", [(256, 4096, 128), (80, 1024, 32)])
+def test_matmul_w8_adversarial_dynamic_range(log2_ratio, N, K, g):
+    """Small same-sign activations and, in every 128-weight block, one activation 2^log2_ratio
+    larger that meets a zero weight (code equal to the zero point): the small ones carry all of
+    Y, so none may be lost to the fp16 staging of X."""
+    from tests.test_gpu_matmul import adversarial_layer
+    for M in (1, 2, 4, 5):
+        W_bits, X_bits = adversarial_layer(N, K, M, log2_ratio, seed=log2_ratio + M)
+        for mode in ("asym", "sym"):
+            _check_full8(X_bits, W_bits, g, mode, f"adversarial 2^{log2_ratio}", kernels_w8(M, K))
 
 
 @pytest.mark.parametrize("M,K", [(1, 65536), (2, 28672), (4, 16384), (3, 16384)])

@@ -11,9 +11,12 @@
 //     Symmetric codes (int8) are offset by 128 (XOR of the sign bit) and taken with z = 128.
 //   * x is staged in LDS as fp16 after scaling each (row, 16-weight chunk) by the power of two
 //     2^e that puts its largest |x| in [2^14, 2^15): exact for every x down to 2^-31 of that
-//     largest value, and off by at most 2^-39 of it below (fp16 subnormal rounding).
+//     largest value (2^-17 in fp16, subnormals included);
 //   * v_dot2_f32_f16 takes exact products with fp32 sums; each chunk's dot is multiplied by
-//     scale * 2^-e and accumulated in fp32; the row total is rounded once to bf16.
+//     scale * 2^-e and accumulated in fp32; the row total is rounded once to bf16;
+//   * X with a smaller nonzero element in some chunk (whose fp16 conversion would lose bits)
+//     takes an exact fp32 path instead: (q - z) and x converted to fp32, one fma per weight.
+//     The choice is one flag for the whole launch (every block stages the same X).
 //
 // Work split.  Persistent blocks of 4 waves; a wave owns whole rows (rows w, w + waves, ...).
 // Lane l owns the 16-byte chunks c = l + 64 u of a row; a row is walked in segments of four
@@ -31,8 +34,10 @@ constexpr int kBlock = 256;
 constexpr int kSeg = 4;                  // chunks per lane per segment
 constexpr size_t kLdsMax = 160 * 1024;
 
-// fp16 x [M][K] and one fp32 2^-e per (row, chunk) [M][K / 16]
-size_t gemv8_lds(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 2 + (size_t)M * (size_t)(K / 16) * 4; }
+// fp16 x [M][K], one fp32 2^-e per (row, chunk) [M][K / 16] and one flag word per wave
+size_t gemv8_lds(int64_t M, int64_t K) {
+  return (size_t)M * (size_t)K * 2 + (size_t)M * (size_t)(K / 16) * 4 + (kBlock / kWave) * 4;
+}
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
@@ -111,6 +116,7 @@ __global__ __launch_bounds__(kBlock) void gemv8_kernel(const u32x4* __restrict__
   // ---- X -> LDS: per (row, chunk) i, x 2^e as fp16 and 2^-e ----
   u32x4* xh = lds8;                                                     // [MT * C][2]
   float* xe = reinterpret_cast<float*>(lds8 + 2 * (size_t)MT * C);      // [MT * C]
+  int lossy = 0;
   for (int i = threadIdx.x; i < MT * C; i += kBlock) {
     const u32x4 p0 = X[2 * i], p1 = X[2 * i + 1];
     float v[16];
@@ -121,10 +127,16 @@ __global__ __launch_bounds__(kBlock) void gemv8_kernel(const u32x4* __restrict__
       v[8 + 2 * d] = bf16_lo(p1[d]);
       v[8 + 2 * d + 1] = bf16_hi(p1[d]);
     }
-    float mx = 0.0f;
+    float mx = 0.0f, mn = __builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    for (int e = 0; e < 16; ++e) {
+      const float a = fabsf(v[e]);
+      mx = fmaxf(mx, a);
+      mn = fminf(mn, a > 0.0f ? a : __builtin_inff());
+    }
     const int e = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;   // mx 2^e in [2^14, 2^15)
+    // x 2^e holds its 8 significant bits in fp16 (subnormals included) while |x| 2^e >= 2^-17
+    lossy |= (int)(mn < __builtin_inff() && __builtin_ldexpf(mn, e) < 0x1p-17f);
     uint32_t h[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -135,14 +147,61 @@ __global__ __launch_bounds__(kBlock) void gemv8_kernel(const u32x4* __restrict__
     xh[2 * i + 1] = u32x4{h[4], h[5], h[6], h[7]};
     xe[i] = __builtin_ldexpf(1.0f, -e);
   }
+  // one flag for the launch: every block stages the same X.  Each wave writes its own flag word
+  // (so none needs clearing first); the block's OR is read after the barrier.  The exact path
+  // reads the raw bf16 X from the same LDS words (bf16 is as wide as fp16).
+  uint32_t* wflag = reinterpret_cast<uint32_t*>(xe + (size_t)MT * C);   // [kBlock / kWave]
+  const uint64_t wl = __builtin_amdgcn_ballot_w64(lossy != 0);
+  if (lane == 0) wflag[threadIdx.x / kWave] = wl != 0 ? 1u : 0u;
   __syncthreads();
+  uint32_t any = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) any |= wflag[w];
+  const bool exact = any != 0;
+  if (exact) {
+    for (int i = threadIdx.x; i < MT * C; i += kBlock) {
+      xh[2 * i] = X[2 * i];
+      xh[2 * i + 1] = X[2 * i + 1];
+    }
+    __syncthreads();
+  }
   if (row >= N) return;
 
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 
-  auto compute = [&](const Seg& sg, int sgi) {
+  // Exact path (X whose fp16 conversion would lose bits): (q - z) and x in fp32, one fma per
+  // weight, x the raw bf16 X from LDS.
+  auto compute_exact = [&](const Seg& sg, int sgi) {
+#pragma unroll
+    for (int u = 0; u < kSeg; ++u) {
+      const int c = sgi * kSeg * kWave + u * kWave + lane;
+      const int cc = c < C ? c : C - 1;                 // LDS index clamp (the codes are 0 there)
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sg.s[u]);
+      const float zf = (float)sg.z[u];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const size_t i = (size_t)m * C + cc;
+        const u32x4 xv[2] = {xh[2 * i], xh[2 * i + 1]};
+        float part = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t dw = SYM ? sg.w[u][d] ^ 0x80808080u : sg.w[u][d];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int k = 4 * d + b;                    // element k of the chunk: dword k / 2 of X
+            const uint32_t xd = xv[k >> 3][(k >> 1) & 3];
+            const float x = (k & 1) ? bf16_hi(xd) : bf16_lo(xd);
+            part = __builtin_fmaf(x, (float)((dw >> (8 * b)) & 0xffu) - zf, part);
+          }
+        }
+        acc[m] = __builtin_fmaf(part, s, acc[m]);
+      }
+    }
+  };
+
+  auto compute_fast = [&](const Seg& sg, int sgi) {
 #pragma unroll
     for (int u = 0; u < kSeg; ++u) {
       const int c = sgi * kSeg * kWave + u * kWave + lane;
@@ -171,6 +230,10 @@ __global__ __launch_bounds__(kBlock) void gemv8_kernel(const u32x4* __restrict__
         acc[m] = __builtin_fmaf(t0 + t1, s * xe[i], acc[m]);
       }
     }
+  };
+  auto compute = [&](const Seg& sg, int sgi) {
+    if (exact) compute_exact(sg, sgi);            // block-uniform
+    else compute_fast(sg, sgi);
   };
   auto finish_row = [&](int64_t r) {
 #pragma unroll
@@ -231,7 +294,7 @@ hipError_t launch_mt(const void* X, int M, int64_t N, int64_t K, int g, const vo
   } else {
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kLdsMax);
+                                               (int)lds);
       if (e != hipSuccess) return e;
     }
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, lds) != hipSuccess) {
