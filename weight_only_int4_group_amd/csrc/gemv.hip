@@ -8,27 +8,27 @@
 // Quantization", §1).
 //
 // Work split.  A wave owns one output row n at a time.  Each 1 KiB of the row's codes is one
-// load instruction (64 lanes x 16 bytes, contiguous); lane l = kq * 16 + n reads the 16-byte
-// chunk 4 n + kq of it (32 weights), so the four lanes n, n + 16, n + 32, n + 48 together hold
-// 128 consecutive weights.  One persistent block of 12 or 16 waves per compute unit converts X
-// once into LDS; with M = 1 a lane meets the same chunks of X in every row, so it keeps them
-// in registers.  Each wave keeps two or three rows in flight: the loads of the next rows are
-// issued before a row is computed, and the first rows are requested before the conversion of
-// X, so HBM latency overlaps it.
+// load instruction (64 lanes x 16 bytes, contiguous): lane l reads chunk l of it (32 weights).
+// One persistent block of 12 or 16 waves per compute unit converts X once into LDS; with M = 1
+// a lane meets the same chunks of X in every row, so it keeps them in registers.  Each wave
+// keeps two or three rows in flight: the loads of the next rows are issued before a row is
+// computed, and the first rows are requested before the conversion of X, so HBM latency
+// overlaps it.
 //
 // Arithmetic (every product exact, sums in fp32, Y rounded once to bf16):
 //   * (q - z) is formed exactly in fp16: the nibble OR-ed into the mantissa of 1024.0, minus
 //     1024 + z (nibbles in bits 4..7 give 16 (q - z));
-//   * x is converted to fp16 exactly after scaling each (row of X, 128-weight block) by a
-//     power of two 2^e that puts its largest |x| in [2^14, 2^15); the positions that meet a
+//   * x is converted to fp16 exactly after scaling each (row of X, 32-weight chunk) by a power
+//     of two 2^e that puts its largest |x| in [2^14, 2^15); the positions that meet a
 //     16 (q - z) weight carry 2^(e - 4);
-//   * g a multiple of 128: one v_mfma_f32_16x16x32_f16 per dword of codes, with each lane's A
-//     operand the x of its own weights: the diagonal D[n][n] sums the exact products of the
-//     four lanes of a 128-weight block (one group), and the other entries are not used; the
-//     block's sum is multiplied by its scale and 2^-e and accumulated in fp32;
-//   * other g (32, 64, 96): v_dot2_f32_f16 of the same exact operands per 32-weight chunk;
+//   * the products and their sums run on the matrix cores, whose pipe is separate from the
+//     vector ALU that forms (q - z): one v_mfma_f32_4x4x4_16b_f16 per four weights, each lane
+//     supplying its own x and (q - z), so that one diagonal entry of its result is its own
+//     four-term dot product in fp32 (the matrix cores flush fp16 subnormals, so the staging
+//     keeps every nonzero operand normal); each 32-weight chunk's sum is multiplied by its
+//     scale and 2^-e and accumulated in fp32;
 //   * X whose fp16 conversion would lose a bit (a nonzero |x| 2^(e-4) below 2^-14, fp16's
-//     smallest normal: a dynamic range above about 2^24 inside one 128-weight block) takes an
+//     smallest normal: a dynamic range above about 2^24 inside one 32-weight chunk) takes an
 //     exact fp32 path instead: (q - z) and x converted to fp32, one fma per weight.  The
 //     choice is one flag for the whole launch (every block stages the same X).
 #include "q4_device.h"
@@ -40,6 +40,8 @@ namespace q4 {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Sum over the 64 lanes of a wave, returned uniformly.
 __device__ __forceinline__ float dpp_row_sum(float v) {
@@ -56,16 +58,6 @@ __device__ __forceinline__ float wave_total(float v) {
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (a + b) + (c + d);
-}
-
-// Max (or min) over each aligned quad of lanes, returned to every lane of the quad.
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float quad_min(float v) {
-  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  return fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
 }
 
 // Four fp16 pairs (q - z) of one dword of codes (8 nibbles): nibble OR-ed into 1024.0 minus
@@ -94,8 +86,7 @@ struct RowBuf {
   uint32_t z[SHARE ? 1 : J];      // zero-point
 };
 
-// DIAG: g is a multiple of 128 (the matrix-core diagonal form); else v_dot2 per chunk.
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING, bool DIAG>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
 __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -105,7 +96,6 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   const int G = K / g;
   const int cpg = g >> 5;                     // chunks per group
   const int lane = threadIdx.x & (kWave - 1);
-  const int pi = 4 * (lane & 15) + (lane >> 4);   // this lane's chunk inside each 1 KiB
   const int64_t wpb = BLOCK / kWave;
   const int64_t nw = (int64_t)gridDim.x * wpb;
   const int64_t n0 = (int64_t)blockIdx.x * wpb +
@@ -115,16 +105,24 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   bool cval[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int c = pi + kWave * j;
+    const int c = lane + kWave * j;
     cval[j] = FULL || c < C;
     goff[j] = (cval[j] ? c : C - 1) / cpg;
+  }
+  // SHARE with at most four chunks per lane: the exchange addresses 4 goff[j] (below 256, as a
+  // row has at most 64 groups) packed one per byte, a register instead of J
+  constexpr bool PACK = SHARE && J <= 4;
+  uint32_t gpack = 0;
+  if constexpr (PACK) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) gpack |= (uint32_t)(4 * goff[j]) << (8 * j);
   }
 
   // Loads are unconditional.  A row past the end gets an empty buffer resource, so its loads
   // read no memory and return 0; chunks past the row end lie past the resource's end (read 0
   // and meet x = 0), and rows past N are not stored.
   const int gown = min(lane, G - 1);           // SHARE: the group this lane loads
-  auto load = [&](RowBuf<J, SHARE>& b, int64_t row) {
+  auto load = [&](RowBuf<J, SHARE>& b, int64_t row) __attribute__((always_inline)) {
     const bool live = row < N;                  // wave-uniform
     const size_t r = live ? (size_t)row : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + r * C, live ? (uint32_t)C * 16u : 0u);
@@ -132,7 +130,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const __amdgpu_buffer_rsrc_t rz = buffer_over(zeros + r * G, live ? (uint32_t)G : 0u);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = pi + kWave * j;
+      const int c = lane + kWave * j;
       b.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * c, 0, kBufferNT));
       if (!SHARE) {
         b.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * goff[j], 0, 0);
@@ -146,60 +144,58 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   };
 
   static_assert(RING == 2 || RING == 3, "two or three rows in flight");
+  // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, chunk), four planes ----
+  // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t; fs
+  // holds 2^-e.  One thread per chunk (M C <= BLOCK, checked at launch).  X is requested
+  // before the first rows of W, so that it arrives first and the rows compute as they land.
+  // The range of |x| is taken on the bf16 bit patterns (their order as unsigned 16-bit integers
+  // is the order of the values), two at a time; the smallest nonzero one as the smallest of
+  // bits - 1 (zero wraps to the largest).
+  const int idx = threadIdx.x;
+  const bool stager = idx < M * C;
+  const int m_x = stager ? idx / C : 0;
+  const int c_x = stager ? idx - m_x * C : 0;
+  u32x4 v[4];
+  if (stager) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o) v[o] = reinterpret_cast<const u32x4*>(X + (size_t)m_x * K + (size_t)c_x * 32)[o];
+  }
+
   RowBuf<J, SHARE> b0, b1, b2;
   load(b0, n0);
   load(b1, n0 + nw);
   if constexpr (RING == 3) load(b2, n0 + 2 * nw);
 
-  // ---- X -> LDS: fp16 pairs scaled by 2^e per (m, 128-weight block), four planes ----
-  // plane t of chunk c of row m holds (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16 of octet t; fs
-  // holds 2^-e per chunk (the same for the four chunks of a block).  One thread per chunk; the
-  // four chunks of a block are an aligned quad of lanes (C is a multiple of 4 or the block is
-  // the row's last), so the block's range is a quad reduction.
   u32x4* xs = lds4;                                                 // [M][4][C]
   float* fs = reinterpret_cast<float*>(lds4 + (size_t)M * 4 * C);   // [M][C]
   int lossy = 0;
-  const int total = M * C;
-  const int trips = (total + BLOCK - 1) / BLOCK;
-  for (int it = 0; it < trips; ++it) {          // all lanes take part in every quad reduction
-    const int idx = it * BLOCK + (int)threadIdx.x;
-    const bool act = idx < total;
-    const int m = act ? idx / C : 0;
-    const int c = act ? idx - m * C : 0;
-    u32x4 v[4];
-#pragma unroll
-    for (int o = 0; o < 4; ++o) v[o] = act ? reinterpret_cast<const u32x4*>(X + (size_t)m * K + (size_t)c * 32)[o]
-                                           : u32x4{0u, 0u, 0u, 0u};
-    float amax = 0.0f, amin = __builtin_inff();
+  if (stager) {
+    const int m = m_x, c = c_x;
+    u16x2 hi = {0, 0}, lo = {0xffff, 0xffff};
 #pragma unroll
     for (int o = 0; o < 4; ++o)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a = fabsf(bf16_lo(v[o][i])), bb = fabsf(bf16_hi(v[o][i]));
-        amax = fmaxf(amax, fmaxf(a, bb));
-        amin = fminf(amin, fminf(a > 0.0f ? a : __builtin_inff(), bb > 0.0f ? bb : __builtin_inff()));
+        const u16x2 a = __builtin_bit_cast(u16x2, v[o][i] & 0x7fff7fffu);
+        hi = __builtin_elementwise_max(hi, a);
+        lo = __builtin_elementwise_min(lo, a - u16x2{1, 1});
       }
-    // the block of chunk c is chunks 4 (c / 4) .. + 3 of the same row m: lanes 4 (idx / 4) .. + 3
-    // when C is a multiple of 4 (the rows then start on quad boundaries); otherwise per chunk
-    if ((C & 3) == 0) {
-      amax = quad_max(amax);
-      amin = quad_min(amin);
-    }
+    const uint32_t amax_b = hi[0] > hi[1] ? hi[0] : hi[1];
+    const uint32_t amin_b1 = lo[0] < lo[1] ? lo[0] : lo[1];          // 0xffff: no nonzero x
+    const float amax = __uint_as_float(amax_b << 16);
     int e = 0;
     if (amax > 0.0f) e = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);   // amax 2^e in [2^14, 2^15)
-    lossy |= (int)(act && amin < __builtin_inff() && __builtin_ldexpf(amin, e) < 0x1p-10f);
-    if (act) {
+    lossy |= (int)(amin_b1 != 0xffffu && __builtin_ldexpf(__uint_as_float((amin_b1 + 1u) << 16), e) < 0x1p-10f);
 #pragma unroll
-      for (int o = 0; o < 4; ++o) {
-        const u32x4 q = v[o];
-        const f16x2 p0 = {(_Float16)__builtin_ldexpf(bf16_lo(q[0]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[2]), e)};
-        const f16x2 p1 = {(_Float16)__builtin_ldexpf(bf16_hi(q[0]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[2]), e - 4)};
-        const f16x2 p2 = {(_Float16)__builtin_ldexpf(bf16_lo(q[1]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[3]), e)};
-        const f16x2 p3 = {(_Float16)__builtin_ldexpf(bf16_hi(q[1]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[3]), e - 4)};
-        xs[((size_t)m * 4 + o) * C + c] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
-      }
-      fs[idx] = __builtin_ldexpf(1.0f, -e);
+    for (int o = 0; o < 4; ++o) {
+      const u32x4 q = v[o];
+      const f16x2 p0 = {(_Float16)__builtin_ldexpf(bf16_lo(q[0]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[2]), e)};
+      const f16x2 p1 = {(_Float16)__builtin_ldexpf(bf16_hi(q[0]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[2]), e - 4)};
+      const f16x2 p2 = {(_Float16)__builtin_ldexpf(bf16_lo(q[1]), e), (_Float16)__builtin_ldexpf(bf16_lo(q[3]), e)};
+      const f16x2 p3 = {(_Float16)__builtin_ldexpf(bf16_hi(q[1]), e - 4), (_Float16)__builtin_ldexpf(bf16_hi(q[3]), e - 4)};
+      xs[((size_t)m * 4 + o) * C + c] = u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
     }
+    fs[idx] = __builtin_ldexpf(1.0f, -e);
   }
   // one flag for the launch: every block stages the same X
   const bool exact = __syncthreads_or(lossy) != 0;
@@ -208,29 +204,30 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   // them, with their factors, from LDS into registers once and reads no LDS per row.  Chunks
   // past the row end are 0.
   constexpr bool XREG = MT == 1 && (J <= 2 || (J == 4 && (BLOCK <= 768 || RING <= 2)));   // register budget
+  static_assert(!XREG || J <= 4, "one byte of xe per chunk");
   u32x4 xr[XREG ? J : 1][4];
-  float xf[XREG ? J : 1];
-  if constexpr (XREG) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
-#pragma unroll
-      for (int o = 0; o < 4; ++o) xr[j][o] = cval[j] ? xs[(size_t)o * C + c] : u32x4{0u, 0u, 0u, 0u};
-      xf[j] = fs[c];
-    }
-  }
+  // the chunks' factors 2^-e, as the exponents -e packed one per byte (J <= 4): one register
+  uint32_t xe = 0;
   uint32_t bias = 0x64006400u;
   asm volatile("" : "+v"(bias));   // keep in a VGPR: (x & mask) | bias -> one v_and_or_b32
-  // the lanes whose D fragment holds a diagonal entry D[n][n]: rows 4 (l / 16) .. + 3 of column
-  // l % 16 contain n when l / 16 == (l % 16) / 4; the entry is element (l % 16) % 4
-  const bool diag_lane = (lane >> 4) == ((lane & 15) >> 2);
+  // Y[m, row] from lane m, through a resource based at the element (its address is
+  // wave-uniform, so it takes no vector registers)
+  auto store_y = [&](int m, int64_t row, float v) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = buffer_over(Y + (size_t)m * (size_t)N + (size_t)row, 2u);
+    if (lane == m) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, 0, 0, 0);
+  };
 
-  auto group_sz = [&](const RowBuf<J, SHARE>& b, uint32_t (&sb)[J], uint32_t (&zb)[J]) {
+  auto group_sz = [&](const RowBuf<J, SHARE>& b, uint32_t (&sb)[J], uint32_t (&zb)[J]) __attribute__((always_inline)) {
     if (SHARE) {
       const uint32_t sz = SYM ? b.s[0] : (b.s[0] | (b.z[0] << 16));   // one word per group
+      // opaque to the compiler, so that the bytes are taken apart here rather than once into J
+      // registers
+      uint32_t gp = gpack;
+      asm volatile("" : "+v"(gp));
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * goff[j], (int)sz);
+        const int addr = PACK ? (int)((gp >> (8 * j)) & 0xffu) : 4 * goff[j];
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)sz);
         sb[j] = w & 0xffffu;
         zb[j] = SYM ? 8u : w >> 16;
       }
@@ -243,88 +240,62 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     }
   };
 
-  auto process_fast = [&](const RowBuf<J, SHARE>& b, int64_t row) {
+  // One 4x4x4 matrix-core product per half dword of codes: lane l supplies row l % 4 of A (its
+  // own four x) and column l % 4 of B (its own four (q - z)) of block l / 4, so the diagonal
+  // entry D[l % 4][l % 4], element l % 4 of lane l's result, is the lane's own exact four-term
+  // dot product summed in fp32; the other entries are not used.
+  auto process_fast = [&](const RowBuf<J, SHARE>& b, int64_t row) __attribute__((always_inline)) {
     uint32_t sb[J], zb[J];
     group_sz(b, sb, zb);
-    float tot[MT];
-    if constexpr (DIAG) {
-      f32x4 acc[MT];
+    // opaque to the compiler, so that the bytes are taken apart here rather than once into J
+    // registers
+    uint32_t xep = xe;
+    asm volatile("" : "+v"(xep));
+    auto xexp = [&](int j) { return (int)(int8_t)(uint8_t)(xep >> (8 * j)); };
+    f32x4 acc4[MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MT; ++m) acc4[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
-        const f16x2 b1 = as_f16x2((0x6400u + zb[j]) * 0x00010001u);
-        const f16x2 b16 = as_f16x2((0x6400u + 16u * zb[j]) * 0x00010001u);
-        f32x4 pacc[MT];
+    for (int j = 0; j < J; ++j) {
+      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+      const f16x2 b1 = as_f16x2((0x6400u + zb[j]) * 0x00010001u);
+      const f16x2 b16 = as_f16x2((0x6400u + 16u * zb[j]) * 0x00010001u);
+      f32x4 pacc[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < MT; ++m) pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int o = 0; o < 4; ++o) {
-          const f16x8 bw = dequant<SYM>(b.w[j][o], bias, b1, b16);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = XREG ? xr[XREG ? j : 0][o]
-                                  : (cval[j] ? xs[((size_t)m * 4 + o) * C + c] : u32x4{0u, 0u, 0u, 0u});
-            pacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, xv), bw, pacc[m], 0, 0, 0);
-          }
-        }
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
+      for (int o = 0; o < 4; ++o) {
+        const f16x8 bw = dequant<SYM>(b.w[j][o], bias, b1, b16);
+        const f16x4 blo = {bw[0], bw[1], bw[2], bw[3]}, bhi = {bw[4], bw[5], bw[6], bw[7]};
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const float f = s * (XREG ? xf[XREG ? j : 0] : fs[m * C + c]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[m][r] = __builtin_fmaf(pacc[m][r], f, acc[m][r]);
+          const u32x4 xv = XREG ? xr[XREG ? j : 0][o]
+                                : (cval[j] ? xs[((size_t)m * 4 + o) * C + c] : u32x4{0u, 0u, 0u, 0u});
+          const f16x8 xa = __builtin_bit_cast(f16x8, xv);
+          pacc[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(f16x4{xa[0], xa[1], xa[2], xa[3]}, blo, pacc[m], 0, 0, 0);
+          pacc[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(f16x4{xa[4], xa[5], xa[6], xa[7]}, bhi, pacc[m], 0, 0, 0);
         }
       }
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const int el = lane & 3;
-        const float dv = el == 0 ? acc[m][0] : (el == 1 ? acc[m][1] : (el == 2 ? acc[m][2] : acc[m][3]));
-        tot[m] = wave_total(diag_lane ? dv : 0.0f);
+        const float f = XREG ? __builtin_ldexpf(s, xexp(j)) : s * fs[m * C + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc4[m][r] = __builtin_fmaf(pacc[m][r], f, acc4[m][r]);
       }
-    } else {
-      float acc[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int c = FULL ? pi + kWave * j : min(pi + kWave * j, C - 1);
-        const f16x2 b1 = as_f16x2((0x6400u + zb[j]) * 0x00010001u);
-        const f16x2 b16 = as_f16x2((0x6400u + 16u * zb[j]) * 0x00010001u);
-        // four independent partial sums per row of X (one per dword) keep the dot2 chains short
-        float d[MT][4];
-#pragma unroll
-        for (int o = 0; o < 4; ++o) {
-          const f16x8 bw = dequant<SYM>(b.w[j][o], bias, b1, b16);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = XREG ? xr[XREG ? j : 0][o]
-                                  : (cval[j] ? xs[((size_t)m * 4 + o) * C + c] : u32x4{0u, 0u, 0u, 0u});
-            float t = __builtin_amdgcn_fdot2(f16x2{bw[0], bw[1]}, as_f16x2(xv[0]), 0.0f, false);
-            t = __builtin_amdgcn_fdot2(f16x2{bw[2], bw[3]}, as_f16x2(xv[1]), t, false);
-            t = __builtin_amdgcn_fdot2(f16x2{bw[4], bw[5]}, as_f16x2(xv[2]), t, false);
-            d[m][o] = __builtin_amdgcn_fdot2(f16x2{bw[6], bw[7]}, as_f16x2(xv[3]), t, false);
-          }
-        }
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const float f = s * (XREG ? xf[XREG ? j : 0] : fs[m * C + c]);
-          acc[m] = __builtin_fmaf((d[m][0] + d[m][1]) + (d[m][2] + d[m][3]), f, acc[m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) tot[m] = wave_total(acc[m]);
     }
+    const int el = lane & 3;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (lane == m && m < M) Y[(size_t)m * N + row] = f32_to_bf16_bits(tot[m]);
+    for (int m = 0; m < MT; ++m) {
+      const float dv = el == 0 ? acc4[m][0] : (el == 1 ? acc4[m][1] : (el == 2 ? acc4[m][2] : acc4[m][3]));
+      const float tot = wave_total(dv);
+      if (m < M) store_y(m, row, tot);
+    }
   };
 
   // Exact path: (q - z) and x in fp32, one fma per weight (exact products), x read from X.
   const __amdgpu_buffer_rsrc_t rx = buffer_over(X, (uint32_t)M * (uint32_t)K * 2u);
-  auto process_exact = [&](const RowBuf<J, SHARE>& b, int64_t row) {
+  auto process_exact = [&](const RowBuf<J, SHARE>& b, int64_t row) __attribute__((always_inline)) {
     uint32_t sb[J], zb[J];
     group_sz(b, sb, zb);
     float acc[MT];
@@ -332,7 +303,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int c = pi + kWave * j;
+      const int c = lane + kWave * j;
       const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[j]);
       const float zf = (float)zb[j];
 #pragma unroll
@@ -359,35 +330,54 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const float tot = wave_total(acc[m]);
-      if (lane == m && m < M) Y[(size_t)m * N + row] = f32_to_bf16_bits(tot);
+      if (m < M) store_y(m, row, tot);
     }
-  };
-
-  auto process = [&](const RowBuf<J, SHARE>& b, int64_t row) {
-    if (exact) process_exact(b, row);           // block-uniform
-    else process_fast(b, row);
   };
 
   // sched_barrier keeps the compiler from hoisting one row's work into another's, which would
   // keep more than RING rows of registers live.  The slots are named, not an array: indexed
-  // slots made the compiler wait for a later row's loads before computing an earlier one.
-  const int64_t step = RING * nw;
-  for (int64_t n = n0; n < N; n += step) {
-    process(b0, n);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b0, n + step);
-    __builtin_amdgcn_sched_barrier(0);
-    if (n + nw < N) process(b1, n + nw);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b1, n + nw + step);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (RING == 3) {
-      if (n + 2 * nw < N) process(b2, n + 2 * nw);
+  // slots made the compiler wait for a later row's loads before computing an earlier one.  The
+  // exact form has a loop of its own (one row at a time), so that the pipelined loop holds no
+  // load but its rows' (a load under a branch makes the compiler wait for every load in flight).
+  auto run = [&](auto process) __attribute__((always_inline)) {
+    const int64_t step = RING * nw;
+    for (int64_t n = n0; n < N; n += step) {
+      process(b0, n);
       __builtin_amdgcn_sched_barrier(0);
-      load(b2, n + 2 * nw + step);
+      load(b0, n + step);
       __builtin_amdgcn_sched_barrier(0);
+      if (n + nw < N) process(b1, n + nw);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b1, n + nw + step);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (RING == 3) {
+        if (n + 2 * nw < N) process(b2, n + 2 * nw);
+        __builtin_amdgcn_sched_barrier(0);
+        load(b2, n + 2 * nw + step);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (exact) {                                 // block-uniform; rows one at a time
+    for (int64_t n = n0; n < N; n += nw) {
+      // X is read again for every row (a compiler barrier keeps its loads in the loop rather
+      // than hoisted into registers for all rows)
+      asm volatile("" ::: "memory");
+      load(b0, n);
+      process_exact(b0, n);
+    }
+    return;
+  }
+  if constexpr (XREG) {   // after the exact loop: its registers are free there
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = FULL ? lane + kWave * j : min(lane + kWave * j, C - 1);
+#pragma unroll
+      for (int o = 0; o < 4; ++o) xr[j][o] = cval[j] ? xs[(size_t)o * C + c] : u32x4{0u, 0u, 0u, 0u};
+      xe |= (uint32_t)((__builtin_amdgcn_frexp_expf(fs[c]) - 1) & 0xff) << (8 * j);   // fs = 2^(exp - 1)
     }
   }
+  run(process_fast);
 }
 
 // Blocks of one kernel that fit on a compute unit at once (from its register and LDS use),
@@ -406,13 +396,14 @@ int64_t resident_blocks(Kernel kernel, int block, size_t lds, std::atomic<uint64
   return nb;
 }
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING, bool DIAG>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
 hipError_t launch_one(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus,
                       hipStream_t stream) {
   static std::atomic<uint64_t> memo{0};
-  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING, DIAG>;
+  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING>;
   const int64_t C = K >> 5;
+  if ((int64_t)M * C > BLOCK) return hipErrorInvalidValue;   // one staging thread per chunk of X
   const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 4;
   const int64_t wpb = BLOCK / kWave;
   int64_t blocks = (N + wpb - 1) / wpb;
@@ -430,13 +421,9 @@ hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sy
                       int num_cus, hipStream_t stream) {
   const bool full = (K >> 5) == kWave * J;
   const bool share = K / g <= kWave;
-  const bool diag = g % 128 == 0;
-#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                            \
-  if (diag) return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING, true>(X, M, N, K, g, packed, \
-                                                                            scales, zeros, Y,       \
-                                                                            num_cus, stream);       \
-  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING, false>(X, M, N, K, g, packed, scales,  \
-                                                                    zeros, Y, num_cus, stream)
+#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                        \
+  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING>(X, M, N, K, g, packed, scales, zeros, \
+                                                             Y, num_cus, stream)
 #define Q4_GEMV_SHARE(SYMV, FULLV)                                                           \
   if (share) { Q4_GEMV_ONE(SYMV, FULLV, true); } else { Q4_GEMV_ONE(SYMV, FULLV, false); }
   if (sym) {
