@@ -93,7 +93,8 @@ enum {
     Q4_ERR_ALIAS = -7,     /* an output buffer overlaps an input or another output          */
     Q4_ERR_UNSUPPORTED = -8, /* explicit kernel choice cannot run this shape (e.g. GEMV, M > 2) */
     Q4_ERR_WORKSPACE = -9, /* workspace smaller than the matching *_workspace_bytes() requires */
-    Q4_ERR_VALUE = -10     /* a numeric parameter out of range (GPTQ damping)                 */
+    Q4_ERR_VALUE = -10,    /* a numeric parameter out of range (GPTQ damping)                 */
+    Q4_ERR_SCRATCH = -11   /* sizes need more scratch than the library's static buffer holds */
 };
 
 /*
@@ -215,6 +216,19 @@ int q4_awq_search(const void* X, int64_t M, const void* Yref, const void* W, int
                   int32_t g, int32_t mode, int32_t n_alpha, void* workspace, int64_t workspace_bytes,
                   void* s_out, void* packed, void* scales, void* zeros, void* errors, void* best,
                   void* stream);
+
+/* For callers that cannot allocate device memory (code under stream capture, serving loops
+ * that forbid hipMalloc): q4_awq_search with its scratch in a static device buffer of
+ * q4_awq_static_scratch_bytes() bytes (64 MiB) that the library holds on each GPU it runs on
+ * until the process ends, instead of a caller's workspace.  Arguments, outputs and errors as
+ * for q4_awq_search without workspace and workspace_bytes, plus Q4_ERR_SCRATCH (returned before
+ * any HIP call) when q4_awq_workspace_bytes(M, N, K, g, n_alpha) exceeds the buffer.  No call
+ * allocates.  Calls on one GPU share its buffer: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued; calls in one stream are ordered. */
+int64_t q4_awq_static_scratch_bytes(void);
+int q4_awq_search_static(const void* X, int64_t M, const void* Yref, const void* W, int64_t N, int64_t K,
+                         int32_t g, int32_t mode, int32_t n_alpha, void* s_out, void* packed, void* scales,
+                         void* zeros, void* errors, void* best, void* stream);
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
  * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,

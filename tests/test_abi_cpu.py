@@ -30,7 +30,8 @@ def test_library_exports_all_declared_symbols():
                             "q4_select_kernel", "q4_status_string", "q4_version",
                             "q4_quantize_rtn_scaled", "q4_scale_columns", "q4_awq_workspace_bytes",
                             "q4_awq_search", "q4_quantize_rtn8", "q4_matmul_w8", "q4_select_kernel_w8",
-                            "q4_gptq_workspace_bytes", "q4_gptq"])
+                            "q4_gptq_workspace_bytes", "q4_gptq", "q4_awq_static_scratch_bytes",
+                            "q4_awq_search_static"])
     for name in names:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -394,3 +395,22 @@ def test_binding_rejects_host_tensors_of_the_right_form():
         q4.quantize_rtn_into(W, g, "asym", p, s, z)
     with pytest.raises(ValueError, match="GPU"):
         q4.matmul_into(_t((2, K), torch.bfloat16), p, s, z, g, "asym", _t((2, N), torch.bfloat16))
+
+
+def test_awq_search_static_rejects_sizes_beyond_its_scratch_before_any_hip_call():
+    """The no-allocation search checks its sizes on the host first: a layer whose workspace
+    exceeds the static scratch returns Q4_ERR_SCRATCH (no GPU needed), and shape errors come
+    through as for q4_awq_search."""
+    lib = q4.library()
+    cap = q4.awq_static_scratch_bytes()
+    assert cap == 64 << 20
+    M, N, K, g, n_alpha = 256, 16384, 16384, 128, 11
+    assert q4.awq_workspace_bytes(M, N, K, g, n_alpha) > cap
+    st = lib.q4_awq_search_static(None, M, None, None, N, K, g, 0, n_alpha, None, None, None, None,
+                                  None, None, None)
+    assert st == -11
+    assert "static buffer" in q4.status_string(st)
+    assert lib.q4_awq_search_static(None, 0, None, None, N, K, g, 0, n_alpha, None, None, None, None,
+                                    None, None, None) == -2                     # M < 1
+    assert lib.q4_awq_search_static(None, 4, None, None, 64, 100, 128, 0, n_alpha, None, None, None,
+                                    None, None, None, None) == -3               # K % g != 0

@@ -16,7 +16,7 @@ __all__ = [
     "matmul_into", "dequantize", "dequantize_into", "quantize_rtn_scaled", "quantize_rtn_scaled_into",
     "scale_columns", "scale_columns_into", "awq_workspace_bytes", "awq_search", "awq_search_into",
     "quantize_rtn8", "quantize_rtn8_into", "matmul_w8", "matmul_w8_into", "select_kernel_w8",
-    "gptq_workspace_bytes", "gptq", "gptq_into",
+    "gptq_workspace_bytes", "gptq", "gptq_into", "awq_search_static_into", "awq_static_scratch_bytes",
     "select_kernel", "status_string", "version", "MODES", "KERNELS", "SCALE_OPS",
 ]
 
@@ -65,6 +65,11 @@ def library() -> ctypes.CDLL:
             lib.q4_awq_search.argtypes = [vp, i64, vp, vp, i64, i64, i32, i32, i32, vp, i64, vp, vp, vp,
                                           vp, vp, vp, vp]
             lib.q4_awq_search.restype = ctypes.c_int
+            lib.q4_awq_static_scratch_bytes.argtypes = []
+            lib.q4_awq_static_scratch_bytes.restype = ctypes.c_int64
+            lib.q4_awq_search_static.argtypes = [vp, i64, vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                 vp, vp]
+            lib.q4_awq_search_static.restype = ctypes.c_int
             lib.q4_select_kernel.argtypes = [i64, i64, i64, i32]
             lib.q4_select_kernel.restype = ctypes.c_int
             lib.q4_quantize_rtn8.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
@@ -347,6 +352,40 @@ def awq_search_into(X, Yref, W, g: int, mode: str, n_alpha: int, workspace, s_ou
                s_out.data_ptr(), packed.data_ptr(), _ptr(scales), _ptr(zeros), _ptr(errors), best.data_ptr())
     if st != 0:
         raise Q4Error(st, "q4_awq_search")
+
+
+def awq_search_static_into(X, Yref, W, g: int, mode: str, n_alpha: int, s_out, packed, scales, zeros,
+                           errors, best) -> None:
+    """q4_awq_search_static: the search with the library's static device scratch (no workspace,
+    no allocation by the library); caller-provided outputs."""
+    import torch
+    if X is None or X.dim() != 2 or W is None or W.dim() != 2:
+        raise ValueError("X and W must be 2-D bfloat16 tensors")
+    M, K = X.shape
+    N = W.shape[0]
+    _need(X, torch.bfloat16, (M, K), "awq_search_static: X")
+    _need(W, torch.bfloat16, (N, K), "awq_search_static: W")
+    _need(Yref, torch.bfloat16, (M, N), "awq_search_static: Yref")
+    _need(s_out, torch.float32, (K,), "awq_search_static: s_out")
+    _need(packed, torch.uint8, (N, K // 2), "awq_search_static: packed")
+    G = _groups(K, g)
+    if G is not None:
+        _need(scales, torch.float16, (N, G), "awq_search_static: scales")
+        _need(zeros, torch.uint8, (N, G), "awq_search_static: zeros")
+    if n_alpha >= 1:
+        _need(errors, torch.float64, (n_alpha,), "awq_search_static: errors")
+    _need(best, torch.int32, (1,), "awq_search_static: best")
+    _on_gpu("awq_search_static", X, Yref, W, s_out, packed, scales, zeros, errors, best)
+    st = _call(W, library().q4_awq_search_static, X.data_ptr(), M, Yref.data_ptr(), W.data_ptr(), N, K, g,
+               _mode(mode), n_alpha, s_out.data_ptr(), packed.data_ptr(), _ptr(scales), _ptr(zeros),
+               _ptr(errors), best.data_ptr())
+    if st != 0:
+        raise Q4Error(st, "q4_awq_search_static")
+
+
+def awq_static_scratch_bytes() -> int:
+    """Bytes of the static device scratch q4_awq_search_static works in (per GPU)."""
+    return int(library().q4_awq_static_scratch_bytes())
 
 
 def awq_search(X, Yref, W, g: int = 128, mode: str = "asym", n_alpha: int = 11):

@@ -39,6 +39,7 @@ SOURCES = {
     "gptq.hip": ["-fno-fast-math"],
     # the activation scaling's IEEE division and product must not be contracted or re-associated
     "awq.hip": ["-ffp-contract=off", "-fno-fast-math"],
+    "awq_static.hip": [],
     "q4_abi.cpp": [],
 }
 

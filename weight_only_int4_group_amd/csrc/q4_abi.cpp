@@ -133,6 +133,7 @@ const char* q4_status_string(int status) {
     case Q4_ERR_UNSUPPORTED: return "the chosen kernel does not support this shape";
     case Q4_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() requires";
     case Q4_ERR_VALUE: return "a numeric parameter is out of range (e.g. GPTQ damping not finite and >= 0)";
+    case Q4_ERR_SCRATCH: return "the sizes need more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
