@@ -235,9 +235,10 @@ int q4_awq_search_static(const void* X, int64_t M, const void* Yref, const void*
  * g in {32, 64, 128}, N * K / 2 < 2^32, and K split into at most 8 equal ranges of KR
  * weights: KR = 32 P S with P = 4, 2 or 1 parts for M <= 4, <= 8 or <= 16, S = 16 slices (8
  * for g = 32 at M <= 8 and for g = 64 at M <= 4), S halved (down to P S = 16) while K is
- * not a multiple of KR or holds fewer than 4 ranges; K % KR == 0, KR >= 512, and two stages
- * of 16 rows x KR weights per range fitting 160 KiB of LDS.  So K must be a multiple of 512,
- * at most 4096 for M > 8 (and for g = 32 at M > 4) and at most 8192 otherwise.  Other shapes
+ * not a multiple of KR or holds fewer than 4 ranges, and S = 32 for P = 1, g >= 64 and K a
+ * multiple of 1024 above 4096; K % KR == 0, KR >= 512, and two stages of 16 rows x KR weights
+ * per range fitting 160 KiB of LDS.  So K must be a multiple of 512, at most 4096 for g = 32
+ * at M > 4, and at most 8192 otherwise (a multiple of 1024 above 4096 at M > 8).  Other shapes
  * return Q4_ERR_UNSUPPORTED.  Every kernel satisfies the same accuracy bound; callers use
  * this to pin a kernel. */
 int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, int32_t mode,

@@ -78,7 +78,7 @@ def test_quantize_validation(kw, status):
     (dict(M=2, K=8192, g=128, kernel=1), -8), (dict(M=3, kernel=1), -8),
     (dict(M=1, K=32768, g=128, kernel=1), -8),
     (dict(M=17, K=128, g=32, kernel=3), -8), (dict(M=4, K=96, g=96, kernel=3), -8),
-    (dict(M=4, K=480, g=160, kernel=3), -8), (dict(M=16, K=8192, g=128, kernel=3), -8),
+    (dict(M=4, K=480, g=160, kernel=3), -8), (dict(M=16, K=4608, g=128, kernel=3), -8),
     (dict(M=16, K=8192, g=32, kernel=3), -8),
     (dict(kernel=4), -4), (dict(kernel=-1), -4),
 ])
@@ -126,7 +126,10 @@ def test_select_kernel():
         assert q4.select_kernel(M, 28672, 8192, 128) == "decode"
     assert q4.select_kernel(4, 11008, 4096, 128) == "decode"
     assert q4.select_kernel(16, 4096, 4096, 128) == "decode"
-    assert q4.select_kernel(16, 8192, 8192, 128) == "gemm"      # 16 ranges of 512
+    assert q4.select_kernel(16, 8192, 8192, 128) == "decode"    # 8 ranges of 1024 (32 slices)
+    assert q4.select_kernel(16, 8192, 8192, 32) == "gemm"       # g = 32: 16 ranges of 512
+    assert q4.select_kernel(12, 28672, 8192, 64) == "decode"
+    assert q4.select_kernel(16, 4096, 16384, 128) == "gemm"     # 16 ranges of 1024
     assert q4.select_kernel(8, 4096, 4096, 32) == "decode"
     assert q4.select_kernel(8, 4096, 8192, 32) == "gemm"        # g = 32 takes ranges of 512 at M > 4
     assert q4.select_kernel(3, 4096, 1536, 64) == "decode"      # K = 3 x 512

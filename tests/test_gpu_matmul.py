@@ -27,6 +27,8 @@ def decode_fits(M, N, K, g, mode="asym"):
     S = 8 if (g == 32 and P >= 2) or (g == 64 and P == 4) else 16
     while S > 4 and P * (S // 2) >= 16 and (K % (32 * P * S) != 0 or K // (32 * P * S) < 4):
         S //= 2
+    if P == 1 and g >= 64 and K // 512 > 8 and K % 1024 == 0:
+        S = 32
     KR = 32 * P * S
     if K % KR != 0 or KR < 512 or KR // g < 4 or K // KR > 8:
         return False
@@ -113,6 +115,19 @@ def test_70b_mlp_decode(layer70b, M):
         _check_every_element(Y, X_bits[:M], qw, cfg.g, cfg.mode, cfg.name, kernel)
 
 
+def test_70b_mlp_decode_m16(layer70b):
+    """The 70B-shaped layer at M = 16 (X drawn by the same recipe with 16 rows): every element
+    of Y, for every kernel that runs it (the 32-slice decode among them)."""
+    import dataclasses
+    cfg, _, qw = layer70b
+    _, X16 = make_layer(dataclasses.replace(cfg, M_max=16))
+    ks = kernels_for(16, cfg.N, cfg.K, cfg.g)
+    assert "decode" in ks
+    for kernel in ks:
+        Y = _gpu_matmul(X16, _upload(*qw), cfg.g, cfg.mode, kernel)
+        _check_every_element(Y, X16, qw, cfg.g, cfg.mode, cfg.name + " M=16", kernel)
+
+
 @pytest.fixture(scope="module")
 def prefill_runs():
     """The prefill workload's Y (bench launch configuration: auto kernel) for g = 128 and 32."""
@@ -163,7 +178,7 @@ def test_adversarial_dynamic_range(log2_ratio, N, K, g):
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K,g", [(100, 1536, 64), (300, 2048, 128), (33, 4096, 32), (129, 8192, 64),
-                                   (50, 3072, 128), (17, 512, 32), (257, 4096, 128)])
+                                   (50, 3072, 128), (17, 512, 32), (257, 4096, 128), (70, 6144, 128)])
 def test_decode_shapes(M, N, K, g):
     """Shapes the matrix-core decode kernel takes (K a multiple of 512, ragged N), every kernel."""
     rng = np.random.default_rng(M * 17 + N + K + g)

@@ -11,9 +11,10 @@
 // quarter kq = l / 16, and D rows 4 (l / 16) .. + 3 of column n.
 //
 // Work split.  A workgroup (one per compute unit, persistent) walks 16-row blocks of W.  Its WS
-// waves split K: wave w owns the K range [w KR, (w + 1) KR).  A wave keeps its X range in
-// registers for the whole kernel (the A operand of every row block) and streams its W range of
-// each row block through LDS; the WS partial sums of a row block meet in LDS in wave order.
+// waves split K: wave w owns the K range [v KR, (v + 1) KR), v = (w + workgroup) mod WS.  A
+// wave keeps its X range in registers for the whole kernel (the A operand of every row block)
+// and streams its W range of each row block through LDS; the WS partial sums of a row block
+// meet in LDS in wave order.
 // With M <= 8 (or <= 4) tokens, the 16 token slots carry P = 2 (or 4) parts of the wave's
 // K range: slot m holds token m % (16 / P) of part m / (16 / P), and part p's weights go to
 // their own accumulator, whose rows of part p are the only ones kept.  So the same registers
@@ -161,7 +162,9 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   const int m = lane & 15, kq = lane >> 4;           // A row / B column, k quarter
   const int G = K / TK;                              // groups per row (g = TK)
   const int NB = (N + 15) >> 4;
-  const int K0 = w * KR;
+  // the waves' K ranges rotate with the workgroup, so that the workgroups starting together on
+  // one chip region request different parts of X first
+  const int K0 = ((w + (int)blockIdx.x) % WS) * KR;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const uint32_t my_stages = lds0 + (uint32_t)(w * S) * Gm::STAGE;
   const uint32_t red0 = lds0 + (uint32_t)(WS * S) * Gm::STAGE;
@@ -177,6 +180,51 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
     xr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                           rx, 2u * ((uint32_t)tok * (uint32_t)K + (uint32_t)k), 0, 0));
   }
+  // ---- stage copies ----
+  // Each row block's copies go through resources based at its first row and this wave's K
+  // range, holding the bytes up to the end of the matrix: rows past N then lie past the
+  // resource's end and read as 0.  The range check covers the vector offset only, so every
+  // row offset goes there; the scalar offset carries the 256-byte segment inside the row.
+  // Codes: copy i covers rows 4 (i % 4) + lane / 16 and the 256-byte segment i / 4; lane l
+  // reads chunk (l % 16) ^ row of it, i.e. the chunk bits XOR 64 (i % 4) bytes (rows are a
+  // multiple of 256 bytes long).
+  const uint32_t rowbytes = (uint32_t)K / 2u;
+  const uint32_t code_lane = (uint32_t)(lane >> 4) * rowbytes + 16u * (uint32_t)((lane & 15) ^ (lane >> 4));
+  uint32_t cv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cv[q] = (code_lane ^ (64u * (uint32_t)q)) + 4u * (uint32_t)q * rowbytes;
+  // scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2); zeros:
+  // dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
+  // stage's 16 rows in LDS)
+  uint32_t sv[Gm::NSI], zv[Gm::NZI > 0 ? Gm::NZI : 1];
+#pragma unroll
+  for (int q = 0; q < Gm::NSI; ++q)
+    sv[q] = (uint32_t)(q * (128 / NG) + lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
+#pragma unroll
+  for (int q = 0; q < Gm::NZI; ++q)
+    zv[q] = (uint32_t)(q * (256 / NG) + lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
+  auto issue = [&](int slot, int rb) {
+    const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
+    const uint32_t n0 = (uint32_t)rb * 16u;                          // rb < NB
+    const uint32_t g0 = n0 * (uint32_t)G + (uint32_t)(K0 / TK);      // first group of the range
+    const u32x4 rw = buffer_words(packed + (size_t)n0 * rowbytes + (size_t)(K0 / 2),
+                                  ((uint32_t)N - n0) * rowbytes - (uint32_t)(K0 / 2));
+    const u32x4 rs = buffer_words(scales + g0, ((uint32_t)N * (uint32_t)G - g0) * 2u);
+    const u32x4 rz = buffer_words(zeros + g0, SYM ? 0u : (uint32_t)N * (uint32_t)G - g0);
+#pragma unroll
+    for (int i = 0; i < Gm::NCI; ++i) dma16(rw, cv[i & 3], 256u * (uint32_t)(i >> 2), st + 1024u * (uint32_t)i);
+#pragma unroll
+    for (int q = 0; q < Gm::NSI; ++q) dma4(rs, sv[q], 0u, st + Gm::SOFF + 256u * (uint32_t)q);
+#pragma unroll
+    for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
+  };
+
+  // the first stages are requested right behind X, so that their latency overlaps X's (the
+  // conversion of X below waits for them too: loads complete in order)
+  const int stride = gridDim.x;
+  for (int s = 0; s < S; ++s)
+    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+
   float amax = 0.0f, amin = __builtin_inff();
 #pragma unroll
   for (int s = 0; s < NSL; ++s)
@@ -222,49 +270,6 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
     }
     xr[s] = u32x4{o[0], o[1], o[2], o[3]};
   }
-
-  // ---- stage copies ----
-  // Each row block's copies go through resources based at its first row and this wave's K
-  // range, holding the bytes up to the end of the matrix: rows past N then lie past the
-  // resource's end and read as 0.  The range check covers the vector offset only, so every
-  // row offset goes there; the scalar offset carries the 256-byte segment inside the row.
-  // Codes: copy i covers rows 4 (i % 4) + lane / 16 and the 256-byte segment i / 4; lane l
-  // reads chunk (l % 16) ^ row of it, i.e. the chunk bits XOR 64 (i % 4) bytes (rows are a
-  // multiple of 256 bytes long).
-  const uint32_t rowbytes = (uint32_t)K / 2u;
-  const uint32_t code_lane = (uint32_t)(lane >> 4) * rowbytes + 16u * (uint32_t)((lane & 15) ^ (lane >> 4));
-  uint32_t cv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) cv[q] = (code_lane ^ (64u * (uint32_t)q)) + 4u * (uint32_t)q * rowbytes;
-  // scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2); zeros:
-  // dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
-  // stage's 16 rows in LDS)
-  uint32_t sv[Gm::NSI], zv[Gm::NZI > 0 ? Gm::NZI : 1];
-#pragma unroll
-  for (int q = 0; q < Gm::NSI; ++q)
-    sv[q] = (uint32_t)(q * (128 / NG) + lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
-#pragma unroll
-  for (int q = 0; q < Gm::NZI; ++q)
-    zv[q] = (uint32_t)(q * (256 / NG) + lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
-  auto issue = [&](int slot, int rb) {
-    const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
-    const uint32_t n0 = (uint32_t)rb * 16u;                          // rb < NB
-    const uint32_t g0 = n0 * (uint32_t)G + (uint32_t)(K0 / TK);      // first group of the range
-    const u32x4 rw = buffer_words(packed + (size_t)n0 * rowbytes + (size_t)(K0 / 2),
-                                  ((uint32_t)N - n0) * rowbytes - (uint32_t)(K0 / 2));
-    const u32x4 rs = buffer_words(scales + g0, ((uint32_t)N * (uint32_t)G - g0) * 2u);
-    const u32x4 rz = buffer_words(zeros + g0, SYM ? 0u : (uint32_t)N * (uint32_t)G - g0);
-#pragma unroll
-    for (int i = 0; i < Gm::NCI; ++i) dma16(rw, cv[i & 3], 256u * (uint32_t)(i >> 2), st + 1024u * (uint32_t)i);
-#pragma unroll
-    for (int q = 0; q < Gm::NSI; ++q) dma4(rs, sv[q], 0u, st + Gm::SOFF + 256u * (uint32_t)q);
-#pragma unroll
-    for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
-  };
-
-  const int stride = gridDim.x;
-  for (int s = 0; s < S; ++s)
-    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
 
   // fragment reads: B column n = m (row of the block), quarter kq
   const int n = m;
@@ -384,6 +389,9 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym) {
   int NSL = 16;
   if ((g == 32 && P >= 2) || (g == 64 && P == 4)) NSL = 8;
   while (NSL > 4 && P * (NSL / 2) >= 16 && (K % (P * NSL * 32) != 0 || K / (P * NSL * 32) < 4)) NSL /= 2;
+  // one part (M > 8) and more than 8 ranges of 512: 32 slices (a 1024 range per wave, 128
+  // registers of X) for g = 64 and 128
+  if (P == 1 && g >= 64 && K / 512 > kMaxWaves && K % 1024 == 0) NSL = 32;
   const int64_t KR = (int64_t)P * NSL * 32;
   if (K % KR != 0 || KR < 512 || KR / g < 4) return pl;
   const int64_t WS = K / KR;
@@ -415,11 +423,12 @@ hipError_t launch_one(const Plan& pl, const void* X, int M, int64_t N, int64_t K
   return hipGetLastError();
 }
 
-// (plan_for never picks 16 slices for g = 32 at two or four parts, or for g = 64 at four parts)
+// (plan_for never picks 16 slices for g = 32 at two or four parts, or for g = 64 at four parts,
+// nor 32 slices for g = 32)
 template <int P, int NSL, bool SYM>
 hipError_t launch_tk(const Plan& pl, int g, const void* X, int M, int64_t N, int64_t K, const void* packed,
                      const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
-  if constexpr (!(NSL == 16 && P >= 2))
+  if constexpr (!(NSL == 16 && P >= 2) && NSL != 32)
     if (g == 32) return launch_one<P, NSL, 32, SYM>(pl, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
   if constexpr (!(NSL == 16 && P == 4))
     if (g == 64) return launch_one<P, NSL, 64, SYM>(pl, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
@@ -434,6 +443,7 @@ hipError_t launch_mode(const Plan& pl, int g, const void* X, int M, int64_t N, i
   if (pl.P == PV && pl.NSL == NV)                                                                            \
     return launch_tk<PV, NV, SYM>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
   Q4_DECODE(1, 16)
+  Q4_DECODE(1, 32)
   Q4_DECODE(2, 16)
   Q4_DECODE(2, 8)
   Q4_DECODE(4, 16)
