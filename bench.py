@@ -377,6 +377,62 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measure_decode_range(torch, q4, reps=300, min_bytes=700e6):
+    """The M <= 16 decode workloads, each on its seeded synthetic inputs (synth recipe): config 1
+    (tiny 128 x 256, M=1, a launch-latency case: time reported), config 3 (batched decode
+    4096 x 4096, M=16, sym), config 4 at M = 4 and 8 (70B-shaped MLP) and the 70B shape at M=16.
+    Each rotates over enough distinct quantized weight copies that the Infinity Cache cannot
+    serve them; the kernel q4_matmul picks (Q4_KERNEL_AUTO) is launched `reps` times back to back
+    through the C-ABI with its arguments marshalled once, between HIP events on the launch
+    stream.  Algorithmic bytes per launch = packed codes + fp16 scales + uint8 zeros (asym) + X
+    + Y; the roofline is HBM."""
+    from synth import CONFIGS, make_layer
+    import numpy as np
+    dev = torch.device("cuda:0")
+    lib = q4.library()
+    st = torch.cuda.current_stream().cuda_stream
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    import dataclasses
+    c4 = CONFIGS[3]
+    c4_16 = dataclasses.replace(c4, M_max=16)     # the config-4 recipe drawn with 16 rows of X
+    cases = [("config1", CONFIGS[0], 1), ("config3", CONFIGS[2], 16), ("config4_m4", c4, 4),
+             ("config4_m8", c4, 8), ("70b_m16", c4_16, 16)]
+    out = {}
+    drawn = {}
+    for key, c, M in cases:
+        if c not in drawn:                          # one draw per recipe; M = 4 nests in M = 8
+            drawn[c] = make_layer(c)
+        W_bits, X_bits = drawn[c]
+        W, X = up(W_bits), up(X_bits[:M])
+        by = matmul_bytes(M, c.N, c.K, c.g, c.mode)
+        copies = max(1, int(min_bytes // weight_bytes(c.N, c.K, c.g, c.mode)) + 1)
+        copies = min(copies, 400)
+        sets = [q4.quantize_rtn(W, c.g, c.mode) for _ in range(copies)]
+        del W
+        Y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
+        args = [(X.data_ptr(), M, c.N, c.K, c.g, q4.MODES[c.mode], p.data_ptr(), s.data_ptr(), z.data_ptr(),
+                 Y.data_ptr(), st) for (p, s, z) in sets]
+        for a in args:
+            assert lib.q4_matmul(*a) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            lib.q4_matmul(*args[r % copies])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = by / (ms * 1e-3) / 1e9
+        out[key] = {"workload": f"{c.name}" + (f" at M={M}" if M != c.M_max else "") + f", {copies} weight copies",
+                    "M": M, "N": c.N, "K": c.K, "g": c.g, "mode": c.mode,
+                    "kernel": q4.select_kernel(M, c.N, c.K, c.g), "ms": round(ms, 5), "bytes_per_launch": by,
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        del sets, args
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_gptq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, reps=3, with_oracle=True,
                  oracle_rows=32):
     """GPTQ of the prefill layer W[8192, 8192] (asym, g=128) on `calib` calibration rows of its
@@ -528,7 +584,7 @@ def summarize_counters(fetch_dir, write_dir):
     copy_bytes = 512 * 2 ** 20
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
-    is_gemv = lambda k: "gemv_kernel" in k
+    is_gemv = lambda k: "gemv_kernel<1, 4," in k          # the 70B-shaped M = 1 instance
     is_copy = lambda k: "copyBuffer" in k
     gf, gw = mean_of(fetch, is_gemv), mean_of(write, is_gemv)
     cw_all = [x for k, v in write.items() if is_copy(k) for x in v]
@@ -553,6 +609,12 @@ def summarize_counters(fetch_dir, write_dir):
         res["copy_factor_fetch"] = ff
         res["copy_factor_write"] = fw
         res["traffic_bytes_per_launch"] = gf[0] * 1024 * ff + gw[0] * 1024 * fw
+        # every kernel of the run, scaled the same way (MB per dispatch)
+        res["per_kernel_MB"] = {
+            k: {"fetch": round(sum(v) / len(v) * 1024 * ff / 1e6, 3),
+                "write": round(sum(write.get(k, [0.0])) / max(1, len(write.get(k, []))) * 1024 * fw / 1e6, 3),
+                "dispatches": len(v)}
+            for k, v in sorted(fetch.items())}
     else:
         res["traffic_bytes_per_launch"] = None
     return res
@@ -864,6 +926,8 @@ def main(argv=None):
     note("standalone dequantize measured")
     out["gemv_llama7b_up"] = measure_gemv_7b(torch, q4)
     note("Llama-7B-shaped decode measured")
+    out["decode_m_le_16"] = measure_decode_range(torch, q4)
+    note("M <= 16 decode workloads measured")
     if not args.no_w8:
         out["w8a16"] = measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5,
                                   with_oracle=not args.no_cpu_baseline)
