@@ -493,14 +493,16 @@ def gptq_hessian_ref(X_bits, damp: float = 0.01) -> np.ndarray:
     return H + damp * m * np.eye(H.shape[0])
 
 
-def gptq_ref(W_bits, X_bits, g: int = 128, mode: str = "asym", damp: float = 0.01):
+def gptq_ref(W_bits, X_bits, g: int = 128, mode: str = "asym", damp: float = 0.01,
+             return_quotients: bool = False):
     """GPTQ of a bf16 weight W[N, K] on bf16 calibration rows X[M, K], in the library's INT4
     group format (R11): (packed uint8[N, K/2], scales fp16[N, K/g], zeros uint8[N, K/g]).
 
     The scales and zero-points are RTN's on the original weights (fixed up front).  The sweep
     runs in fp64 over all rows at once, column by column, with U the upper Cholesky factor of
     H^-1: code of the compensated column (fp32 decision, as RTN), err = (w_i - x_hat_i) / U_ii,
-    w[:, i+1:] -= err U[i, i+1:].
+    w[:, i+1:] -= err U[i, i+1:].  With return_quotients the fp32 quotients fl32(w') / scale the
+    codes were rounded from are returned as a fourth value (float32 [N, K]).
     """
     W_bits = np.asarray(W_bits, dtype=np.uint16)
     N, K = W_bits.shape
@@ -516,14 +518,19 @@ def gptq_ref(W_bits, X_bits, g: int = 128, mode: str = "asym", damp: float = 0.0
     U = np.linalg.cholesky(np.linalg.inv(H)).T               # upper, U^T U = H^-1
     w = W32.astype(np.float64)
     q = np.empty((N, K), dtype=np.int64)
+    quots = np.empty((N, K), dtype=np.float32) if return_quotients else None
     for i in range(K):
         G = i // g
         quot = w[:, i].astype(np.float32) / s32[:, G]         # fl32(fl32(w') / scale)
+        if return_quotients:
+            quots[:, i] = quot
         r = np.clip(np.rint(quot), np.float32(-2.0 ** 40), np.float32(2.0 ** 40)).astype(np.int64)
         q[:, i] = np.clip(r + z[:, G], q_min, q_max)
         what = s64[:, G] * (q[:, i] - z[:, G])
         err = (w[:, i] - what) / U[i, i]
         w[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    if return_quotients:
+        return pack_codes_ref(q), s16.astype(np.float16), z.astype(np.uint8), quots
     return pack_codes_ref(q), s16.astype(np.float16), z.astype(np.uint8)
 
 

@@ -3,8 +3,10 @@
 The scales and zero-points are RTN's and must be bit-exact.  The codes come from a sequential
 compensation that the GPU runs in fp32 and the oracle in fp64, so a code whose compensated
 weight lies near a rounding boundary may differ (and steer later columns of its row slightly
-differently); the comparison is therefore: at least 97 % identical codes, and a calibration
-output error ||X W^T - X W_hat^T|| within 2 % of the oracle's and below RTN's.  Cases without
+differently); the comparison is therefore: every row's codes identical up to its first
+difference, and there the oracle's fp32 quotient within BOUNDARY of a rounding boundary; at
+least 99 % identical codes; and a calibration output error ||X W^T - X W_hat^T|| within 2 %
+of the oracle's and below RTN's.  Cases without
 any compensation (a diagonal Hessian, an all-zero calibration set) must equal RTN bit for bit,
 and two runs must give identical outputs.
 """
@@ -16,8 +18,12 @@ from synth import CONFIGS, bf16_bits_to_f32, f64_to_bf16_bits, make_layer
 
 pytestmark = pytest.mark.gpu
 
-MIN_SAME = 0.97
+MIN_SAME = 0.99          # observed 0.992-1.0 on every case below
 ERR_RATIO = 1.02
+# Distance (in code steps) from a half-integer of the oracle's quotient where a row's first code
+# differs: the fp32 sweep drifts from the fp64 one by about 2^-24 |quotient| per column update,
+# under 1e-3 for K <= 8192 and |quotient| <= 8; observed at most 1e-5.
+BOUNDARY = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -55,17 +61,38 @@ def _out_err(X_bits, W_bits, quant, g, mode, rows=None):
     return np.linalg.norm(X @ W.T - X @ What.T)
 
 
+def _first_differences(codes_gpu, codes_ref, quots):
+    """Distance from the nearest rounding boundary (a half-integer) of the oracle's fp32 quotient
+    at each row's first differing code, and the number of rows that differ at all."""
+    dists = []
+    for r in range(codes_gpu.shape[0]):
+        d = np.nonzero(codes_gpu[r] != codes_ref[r])[0]
+        if d.size:
+            qv = float(quots[r, d[0]])
+            dists.append(abs(qv - np.floor(qv) - 0.5))
+    return dists
+
+
 def _compare(W_bits, X_bits, g, mode, label, rows=None):
     from tests.gpu_util import log
     p, s, z, info = _run(W_bits, X_bits, g, mode)
     assert info == 0, f"{label}: Cholesky pivot failure at {info - 1}"
     Wr = W_bits if rows is None else W_bits[rows]
-    rp, rs, rz = orc.gptq_ref(Wr, X_bits, g, mode)
+    rp, rs, rz, quots = orc.gptq_ref(Wr, X_bits, g, mode, return_quotients=True)
     if rows is not None:
         p, s, z = p[rows], s[rows], z[rows]
     assert np.array_equal(s, rs.view(np.uint16)), f"{label}: scales differ"
     assert np.array_equal(z, rz), f"{label}: zeros differ"
-    same = (orc.unpack_codes_ref(p, mode) == orc.unpack_codes_ref(rp, mode)).mean()
+    cg, cr = orc.unpack_codes_ref(p, mode), orc.unpack_codes_ref(rp, mode)
+    # Up to a row's first difference the two sweeps saw the same codes, so they compensated the
+    # same way up to rounding; a code can then only flip where the oracle's quotient lies
+    # within BOUNDARY of a rounding boundary (the fp32 sweep's drift is far smaller).
+    dists = _first_differences(cg, cr, quots)
+    worst = max(dists) if dists else 0.0
+    log(f"gptq {label}: {len(dists)} of {cg.shape[0]} rows differ; at their first differing code the "
+        f"oracle's quotient is at most {worst:.2e} from a rounding boundary")
+    assert worst <= BOUNDARY, f"{label}: a code differs {worst} away from any rounding boundary"
+    same = (cg == cr).mean()
     e_gpu = _out_err(X_bits, Wr, (p, s.view(np.float16), z), g, mode)
     e_ref = _out_err(X_bits, Wr, (rp, rs, rz), g, mode)
     e_rtn = _out_err(X_bits, Wr, orc.quantize_rtn_ref(Wr, g, mode), g, mode)
