@@ -170,10 +170,12 @@ __device__ __forceinline__ u32x2 pack8_bytes(const float x[8], const GroupParams
 // Store the codes of chunk c (8 weights): a dword of nibbles (B = 4) or two dwords of bytes.
 template <bool SYM, int B>
 __device__ __forceinline__ void store_codes(void* codes, int64_t c, const float x[8], const GroupParams& p) {
+  // The codes are written once and not read back by this kernel: streaming stores keep them
+  // from displacing the weight stream in the caches.
   if constexpr (B == 8) {
-    reinterpret_cast<u32x2*>(codes)[c] = pack8_bytes<SYM>(x, p);
+    __builtin_nontemporal_store(pack8_bytes<SYM>(x, p), reinterpret_cast<u32x2*>(codes) + c);
   } else {
-    reinterpret_cast<uint32_t*>(codes)[c] = pack8<SYM>(x, p);
+    __builtin_nontemporal_store(pack8<SYM>(x, p), reinterpret_cast<uint32_t*>(codes) + c);
   }
 }
 
@@ -300,7 +302,9 @@ hipError_t launch_lanes(const void* W, int64_t nchunks, void* packed, void* scal
   const int64_t steps = (nchunks + kWave * U - 1) / (kWave * U);   // wave-steps needed
   const int64_t waves_wanted = steps;
   int64_t blocks = (waves_wanted + 3) / 4;
-  const int64_t cap = (int64_t)num_cus * 8;
+  // Up to 64 blocks per CU: enough waves in flight to keep HBM busy while each wave waits on
+  // its loads (8 per CU left the stream at about 55 % of peak).
+  const int64_t cap = (int64_t)num_cus * 64;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   auto go = [&](auto kernel) {
