@@ -3,9 +3,10 @@
 
 One step is one pass of the whole path over synthetic inputs resident in HBM:
   1. quantize  -- group-wise INT4 RTN of the 70B-shaped MLP weight W[28672, 8192] (asym, g=128)
-  2. decode    -- W4A16 GEMV, M = 1, through L layers of that shape (L distinct quantized weight
-                  copies, 6 by default, 740 MB in total, so the 256 MB Infinity Cache cannot
-                  serve the weights); the copy quantized in step 1 is read last
+  2. decode    -- W4A16 GEMV, M = 1, through L layers of that shape, each with its own quantized
+                  weight copy: 80 by default, the layer count of a 70B Llama decoder, so one
+                  step is one token's pass through every layer's MLP up-projection (9.9 GB of
+                  weights; the 256 MB Infinity Cache cannot serve them)
   3. prefill   -- W4A16 GEMM, M = 2048, W[8192, 8192] (asym, g=128 and g=32)
 The headline value is the decode GEMV's HBM throughput: algorithmic bytes (packed codes +
 fp16 scales + uint8 zeros + X + Y) per launch / measured launch time, HIP events on the
@@ -87,7 +88,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--layers", type=int, default=6, help="distinct decode weight copies per step")
+    p.add_argument("--layers", type=int, default=80,
+                   help="decoder layers per step, each with its own quantized weight copy")
     p.add_argument("--no-check", action="store_true",
                    help="skip the parity assertion of the CPU-baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -348,7 +350,9 @@ def measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5, copies=3, reps=30, w
 def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
     """The Llama-7B MLP up-projection decode, W[11008, 4096] asym g=128, M=1, seeded synthetic
     inputs of that workload: W4A16 GEMV over enough distinct quantized copies that the
-    Infinity Cache cannot serve them, HIP events around `reps` back-to-back launches."""
+    Infinity Cache cannot serve them, HIP events around `reps` back-to-back launches through
+    the C-ABI with their arguments marshalled once (at under 10 us per launch, the Python
+    binding's per-call cost would otherwise set the pace)."""
     from synth import CONFIGS, make_layer
     import numpy as np
     c = CONFIGS[1]
@@ -360,13 +364,17 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
     copies = int(min_bytes // weight_bytes(c.N, c.K, c.g, c.mode)) + 1
     sets = [q4.quantize_rtn(W, c.g, c.mode) for _ in range(copies)]
     Y = torch.empty((1, c.N), dtype=torch.bfloat16, device=dev)
-    for i in range(copies):
-        q4.matmul_into(X, *sets[i], c.g, c.mode, Y)
+    lib = q4.library()
+    st = torch.cuda.current_stream().cuda_stream
+    args = [(X.data_ptr(), 1, c.N, c.K, c.g, q4.MODES[c.mode], p.data_ptr(), s.data_ptr(), z.data_ptr(),
+             Y.data_ptr(), st) for (p, s, z) in sets]
+    for a in args:
+        assert lib.q4_matmul(*a) == 0
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for r in range(reps):
-        q4.matmul_into(X, *sets[r % copies], c.g, c.mode, Y)
+        lib.q4_matmul(*args[r % copies])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -481,7 +489,7 @@ def measure_gptq(torch, q4, W5, X5, W5_bits, X5_bits, calib=512, g=128, reps=3, 
 
 def measure_dequant(torch, q4, sets, W4_bits, g=128, reps=30, with_oracle=True, oracle_rows=1024):
     """q4_dequantize of the 70B-shaped weight W[28672, 8192] (asym, g=128) to bf16, rotating over
-    the benchmark's six quantized copies; algorithmic bytes = codes + scales + zeros read + the
+    the benchmark's per-layer quantized copies; algorithmic bytes = codes + scales + zeros read + the
     bf16 output written.  In the CPU-baseline leg the oracle quantizes the first `oracle_rows`
     rows, the library dequantizes those codes and must match the oracle's dequantization bit
     for bit, and the oracle's dequantization is timed."""
@@ -892,7 +900,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": (f"70B-shaped MLP decode: W4A16 GEMV M=1, W[{N4},{K4}] asym g={g4}, "
-                         f"{L} weight copies per step; plus RTN quantize of that W and prefill "
+                         f"{L} layers per step, each with its own weight copy; plus RTN quantize "
+                         f"of that W and prefill "
                          f"GEMM M={X5.shape[0]} W[{c5.N},{c5.K}] g=128 and g=32"),
             "M": 1, "N": N4, "K": K4, "g": g4, "mode": "asym", "layers_per_step": L,
         },
