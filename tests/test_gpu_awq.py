@@ -59,7 +59,8 @@ def _same_quant(gpu, ref, label):
             raise AssertionError(f"{label}: {name} differs at {bad.tolist()}")
 
 
-@pytest.mark.parametrize("N,K,g", [(64, 256, 32), (33, 1024, 128), (17, 480, 96), (8, 8192, 8192), (129, 2048, 64)])
+@pytest.mark.parametrize("N,K,g", [(64, 256, 32), (33, 1024, 128), (17, 480, 96), (8, 8192, 8192), (129, 2048, 64),
+                                    (40, 4096, 32), (9, 1536, 512), (1030, 512, 256)])
 @pytest.mark.parametrize("mode", ["asym", "sym"])
 def test_quantize_scaled_bitexact(N, K, g, mode):
     import torch
