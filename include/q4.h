@@ -234,7 +234,8 @@ int q4_awq_search_static(const void* X, int64_t M, const void* Yref, const void*
  * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,
  * g in {32, 64, 128}, N * K / 2 < 2^32, and K split into at most 8 equal ranges of KR
  * weights: KR = 32 P S with P = 4, 2 or 1 parts for M <= 4, <= 8 or <= 16, S = 16 slices (8
- * for g = 32 at M <= 8 and for g = 64 at M <= 4), S halved (down to P S = 16) while K is
+ * for g = 32 at M <= 8, and at M <= 4 for g = 64 or K a multiple of 1024 up to 8192), S
+ * halved (down to P S = 16) while K is
  * not a multiple of KR or holds fewer than 4 ranges, and S = 32 for P = 1, g >= 64 and K a
  * multiple of 1024 above 4096; K % KR == 0, KR >= 512, and two stages of 16 rows x KR weights
  * per range fitting 160 KiB of LDS.  So K must be a multiple of 512, at most 4096 for g = 32

@@ -25,6 +25,8 @@ def decode_fits(M, N, K, g, mode="asym"):
         return False
     P = 4 if M <= 4 else (2 if M <= 8 else 1)
     S = 8 if (g == 32 and P >= 2) or (g == 64 and P == 4) else 16
+    if P == 4 and K % 1024 == 0 and K // 1024 <= 8:
+        S = 8
     while S > 4 and P * (S // 2) >= 16 and (K % (32 * P * S) != 0 or K // (32 * P * S) < 4):
         S //= 2
     if P == 1 and g >= 64 and K // 512 > 8 and K % 1024 == 0:

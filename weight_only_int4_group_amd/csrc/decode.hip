@@ -388,6 +388,9 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym) {
   // a workgroup has four waves where K allows
   int NSL = 16;
   if ((g == 32 && P >= 2) || (g == 64 && P == 4)) NSL = 8;
+  // four parts: 8 slices wherever that gives at most 8 ranges of 1024, i.e. two waves per SIMD
+  // (the 70B-shaped layer at M = 4: 31.1 -> 29.2 us)
+  if (P == 4 && K % 1024 == 0 && K / 1024 <= kMaxWaves) NSL = 8;
   while (NSL > 4 && P * (NSL / 2) >= 16 && (K % (P * NSL * 32) != 0 || K / (P * NSL * 32) < 4)) NSL /= 2;
   // one part (M > 8) and more than 8 ranges of 512: 32 slices (a 1024 range per wave, 128
   // registers of X) for g = 64 and 128
