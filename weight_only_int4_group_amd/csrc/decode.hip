@@ -219,10 +219,14 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
     for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
   };
 
-  // the first stages are requested right behind X, so that their latency overlaps X's (the
-  // conversion of X below waits for them too: loads complete in order)
+  // With two or four parts the first stage is requested right behind X (the conversion of X
+  // below waits for it too: loads complete in order); the other stages, and with one part
+  // (M > 8, whose X range is 32 or 64 KB per wave) every stage, only after the conversion, so
+  // that X does not queue behind them (70B-shaped layer, M = 4 / 8 / 16: 29.0 / 31.9 / 42.5 ->
+  // 28.3 / 30.0 / 37.8-39.1 us, config 3 9.9 -> 9.2 us)
   const int stride = gridDim.x;
-  for (int s = 0; s < S; ++s)
+  constexpr int EARLY = P == 1 ? 0 : 1;
+  for (int s = 0; s < min(S, EARLY); ++s)
     if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
 
   float amax = 0.0f, amin = __builtin_inff();
@@ -270,6 +274,9 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
     }
     xr[s] = u32x4{o[0], o[1], o[2], o[3]};
   }
+
+  for (int s = EARLY; s < S; ++s)
+    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
 
   // fragment reads: B column n = m (row of the block), quarter kq
   const int n = m;
