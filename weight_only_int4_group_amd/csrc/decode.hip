@@ -50,6 +50,7 @@ namespace q4 {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 8;
 constexpr size_t kLdsMax = 160 * 1024;
@@ -229,24 +230,30 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   for (int s = 0; s < min(S, EARLY); ++s)
     if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
 
-  float amax = 0.0f, amin = __builtin_inff();
+  // The range of |x| is taken on the bf16 bit patterns (their order as unsigned 16-bit integers
+  // is the order of the values), two at a time; the smallest nonzero one as the smallest of
+  // bits - 1 (zero wraps to the largest).
+  u16x2 hi = {0, 0}, lo = {0xffff, 0xffff};
 #pragma unroll
   for (int s = 0; s < NSL; ++s)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float a = fabsf(bf16_lo(xr[s][c])), b = fabsf(bf16_hi(xr[s][c]));
-      amax = fmaxf(amax, fmaxf(a, b));
-      amin = fminf(amin, fminf(a > 0.0f ? a : __builtin_inff(), b > 0.0f ? b : __builtin_inff()));
+      const u16x2 a = __builtin_bit_cast(u16x2, xr[s][c] & 0x7fff7fffu);
+      hi = __builtin_elementwise_max(hi, a);
+      lo = __builtin_elementwise_min(lo, a - u16x2{1, 1});
     }
+  int amax_b = hi[0] > hi[1] ? hi[0] : hi[1];
+  int amin_b1 = lo[0] < lo[1] ? lo[0] : lo[1];                     // 0xffff: no nonzero x
   // the part of one token is spread over the four quarters kq: lanes m, m + 16, m + 32, m + 48
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  amin = fminf(amin, __shfl_xor(amin, 16));
-  amin = fminf(amin, __shfl_xor(amin, 32));
+  amax_b = max(amax_b, __shfl_xor(amax_b, 16));
+  amax_b = max(amax_b, __shfl_xor(amax_b, 32));
+  amin_b1 = min(amin_b1, __shfl_xor(amin_b1, 16));
+  amin_b1 = min(amin_b1, __shfl_xor(amin_b1, 32));
+  const float amax = __uint_as_float((uint32_t)amax_b << 16);
   int e = 0;
   if (amax > 0.0f) e = min(15 - __builtin_amdgcn_frexp_expf(amax), 126);   // amax 2^e in [2^14, 2^15)
   // exact in fp16 (normal, as the matrix cores need) iff every nonzero |x| 2^(e-4) >= 2^-14
-  const bool lossy = amin < __builtin_inff() && __builtin_ldexpf(amin, e) < 0x1p-10f;
+  const bool lossy = amin_b1 != 0xffff && __builtin_ldexpf(__uint_as_float((uint32_t)(amin_b1 + 1) << 16), e) < 0x1p-10f;
   const bool exact = __builtin_amdgcn_ballot_w64(lossy) != 0;              // wave-uniform
   const float my_fac = exact ? 1.0f : __builtin_ldexpf(1.0f, -e);
 #pragma unroll
