@@ -221,10 +221,10 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   };
 
   // With two or four parts the first stage is requested right behind X (the conversion of X
-  // below waits for it too: loads complete in order); the other stages, and with one part
-  // (M > 8, whose X range is 32 or 64 KB per wave) every stage, only after the conversion, so
-  // that X does not queue behind them (70B-shaped layer, M = 4 / 8 / 16: 29.0 / 31.9 / 42.5 ->
-  // 28.3 / 30.0 / 37.8-39.1 us, config 3 9.9 -> 9.2 us)
+  // below waits for it too: loads complete in order) and the others after the conversion;
+  // with one part (M > 8, whose X range is 32 or 64 KB per wave) every stage once X has
+  // arrived: X does not queue behind them (70B-shaped layer, M = 4 / 8 / 16: 29.0 / 31.9 /
+  // 42.5 -> 28.3 / 30.0 / 37.8-39.1 us, config 3 9.9 -> 9.2 us)
   const int stride = gridDim.x;
   constexpr int EARLY = P == 1 ? 0 : 1;
   for (int s = 0; s < min(S, EARLY); ++s)
@@ -256,6 +256,14 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   const bool lossy = amin_b1 != 0xffff && __builtin_ldexpf(__uint_as_float((uint32_t)(amin_b1 + 1) << 16), e) < 0x1p-10f;
   const bool exact = __builtin_amdgcn_ballot_w64(lossy) != 0;              // wave-uniform
   const float my_fac = exact ? 1.0f : __builtin_ldexpf(1.0f, -e);
+  // one part: the stages are requested now that X is here, so that the conversion below
+  // overlaps their latency (M = 16: 35.0 -> 33.9 us; config 3 8.8 -> 8.7 us)
+  if constexpr (P == 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < S; ++s)
+      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int s = 0; s < NSL; ++s) {
     const u32x4 v = xr[s];
@@ -282,8 +290,9 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
     xr[s] = u32x4{o[0], o[1], o[2], o[3]};
   }
 
-  for (int s = EARLY; s < S; ++s)
-    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+  if constexpr (P > 1)
+    for (int s = EARLY; s < S; ++s)
+      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
 
   // fragment reads: B column n = m (row of the block), quarter kq
   const int n = m;
