@@ -464,6 +464,17 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     // the groups in order, which is what makes the MFMA asm safe: an operand written in group
     // g is first read in group g + 1 or later, behind at least three MFMAs, and every
     // accumulator is rewritten only by its own MFMA, 16 groups later.
+    // LDS byte offsets of this lane's X fragment for (stage R, sub-step ks), kept in registers
+    // (opaque to the compiler) so that each read's remaining row-block offset, at most
+    // 15 x 4 KiB, is the instruction's immediate
+    uint32_t xoff[2][4];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        xoff[rr][kk] = (uint32_t)rr * kStageBytes + (rd_off ^ (16u * kk));
+        asm volatile("" : "+v"(xoff[rr][kk]));
+      }
     u32x4 a[2][NB];                          // operands of sub-step ks (slot ks & 1)
     float sc[2][NB], cc1[2][NB], cc64[2][NB];   // per step slot: scale, -s (1024 + z), -s (64 + z)
 
@@ -494,11 +505,10 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
 
     auto step_large = [&](auto S, int kt) {
       constexpr int R = decltype(S)::value;
-      const uint8_t* xs = xl + (uint32_t)R * kStageBytes;
       constexpr int NG = 4 * MB;          // groups per step
       constexpr int XA = 2;               // X fragments read this many groups ahead
       auto xfrag = [&](int g) {
-        return *reinterpret_cast<const bf16x8*>(xs + (g % MB) * 16 * kRowBytes + (rd_off ^ (16u * (g / MB))));
+        return *reinterpret_cast<const bf16x8*>(xl + xoff[R][g / MB] + (g % MB) * 16 * kRowBytes);
       };
       bf16x8 bx[XA + 1];
 #pragma unroll
@@ -523,14 +533,31 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
         if constexpr (g < kDmaOps) copy_x_piece(R ^ 1, kt + 1, g);
         if constexpr (g == kDmaOps) { if (!REGSZ) copy_sz(R ^ 1, kt + 1); }
         __builtin_amdgcn_sched_barrier(0);
-        // Slot 1: the biased fp16 pairs of a new code dword.
+        // Slot 1: half of the biased fp16 pairs of a new code dword (the other half one group
+        // later, which evens out the vector work between groups).
         mfma_acc(acc[1][mb], a[ks & 1][1], b);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (piece == 0) {
-          constexpr int kn = next ? 0 : ks + 1;                   // the sub-step dequantised
+        if constexpr (B == 8) {
+          if constexpr (piece == 0) {
+            constexpr int kn = next ? 0 : ks + 1;                   // the sub-step dequantised
+            const u32x4* wsrc = next ? wq[R ^ 1][nbw] : wq[R][nbw];
+            bq = deq_prep_b<SYM>(sub_d0(wsrc, kn), sub_d1(wsrc, kn));
+          }
+        } else if constexpr (piece <= 1) {
+          // the four biased pairs of the dword in two halves: (k0, k4), (k1, k5) for pieces 0 and
+          // 2 here, (k2, k6), (k3, k7) for pieces 1 and 3 one group later
+          constexpr int kn = next ? 0 : ks + 1;
           const u32x4* wsrc = next ? wq[R ^ 1][nbw] : wq[R][nbw];
-          if constexpr (B == 8) bq = deq_prep_b<SYM>(sub_d0(wsrc, kn), sub_d1(wsrc, kn));
-          else bq = deq_prep<SYM>(sub_d0(wsrc, kn));
+          uint32_t dw = sub_d0(wsrc, kn);
+          if (SYM) dw ^= 0x88888888u;
+          if constexpr (piece == 0) {
+            bq.q0 = as_f16x2(and_or(dw, 0x000F000Fu, 0x64006400u));
+            bq.q1 = as_f16x2(and_or(dw, 0x00F000F0u, 0x54005400u));
+          } else {
+            const uint32_t d8 = dw >> 8;
+            bq.q2 = as_f16x2(and_or(d8, 0x000F000Fu, 0x64006400u));
+            bq.q3 = as_f16x2(and_or(d8, 0x00F000F0u, 0x54005400u));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         // Slot 2: the two exact products of this group's pair.
