@@ -19,8 +19,8 @@ Plain numpy, written to be checked by eye against the pages:
   "DL S067" §2 "Per-tensor vs per-channel vs per-group": one scale (and zero) per group of
   g consecutive weights along the input dimension of each output row, g = 128 by default;
 * W4A16 -- "LLM Weight Quantization ...", "The vocabulary": 4-bit weights dequantised to
-  16-bit, the matmul in 16-bit.  The oracle computes the product exactly enough to judge
-  the GPU: fp64 dequantisation and fp64 accumulation.
+  16-bit, the matmul in 16-bit.  The oracle computes the product exactly enough to check
+  the GPU against: fp64 dequantisation and fp64 accumulation.
 
 Readings of points the pages leave open (each one is listed with its reason in the
 design notes of the repository):
