@@ -178,6 +178,32 @@ def test_adversarial_dynamic_range(log2_ratio, N, K, g):
             _check_full(X_bits, W_bits, g, mode, f"adversarial 2^{log2_ratio}", kernels_for(M, N, K, g))
 
 
+@pytest.mark.parametrize("M,N,K,g", [(1, 33000, 1024, 128), (2, 33001, 1024, 64), (1, 17003, 8192, 128),
+                                     (1, 17000, 6144, 128), (2, 33001, 4096, 128), (1, 33000, 1536, 512)])
+def test_gemv_many_rows_per_wave(M, N, K, g):
+    """GEMV shapes with at least four rows per wave on a 256-CU device, where each wave copies its
+    contiguous rows' scales and zero-points into LDS once (4 | K / g; K / g = 3 keeps the per-row
+    loads): every element of Y, ragged row counts, both modes."""
+    rng = np.random.default_rng(N + K + g + M)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        qw = orc.quantize_rtn_ref(W_bits, g, mode)
+        Y = _gpu_matmul(X_bits, _upload(*qw), g, mode, "gemv")
+        _check_every_element(Y, X_bits, qw, g, mode, "gemv-many-rows", "gemv")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_many_rows_per_wave_exact_path(M):
+    """X whose fp16 staging would lose bits (the exact fp32 path) on a many-rows-per-wave shape."""
+    N, K, g = 33000, 1024, 128
+    W_bits, X_bits = adversarial_layer(N, K, M, 36, seed=5 + M)
+    for mode in ("asym", "sym"):
+        qw = orc.quantize_rtn_ref(W_bits, g, mode)
+        Y = _gpu_matmul(X_bits, _upload(*qw), g, mode, "gemv")
+        _check_every_element(Y, X_bits, qw, g, mode, "gemv-many-rows-exact", "gemv")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K,g", [(100, 1536, 64), (300, 2048, 128), (33, 4096, 32), (129, 8192, 64),
                                    (50, 3072, 128), (17, 512, 32), (257, 4096, 128), (70, 6144, 128)])

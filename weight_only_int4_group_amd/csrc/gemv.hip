@@ -15,6 +15,13 @@
 // computed, and its first row is requested before the conversion of X, so HBM latency
 // overlaps it.
 //
+// Scales and zero-points.  A row has at most 64 groups in the common case, and then lane l
+// reads group l's scale and zero-point and the lanes exchange them.  Read per row, they are two
+// small requests beside the row's 4 KiB of codes (about 9 % of the time of a 28672 x 8192
+// layer).  When a wave owns at least four rows, it owns a contiguous range of them instead and
+// copies the range's scales and zero-points into its own LDS area once (global -> LDS copies,
+// 256 bytes per instruction); each row then reads its pair from LDS.
+//
 // Arithmetic (every product exact, sums in fp32, Y rounded once to bf16):
 //   * (q - z) is formed exactly in fp16: the nibble OR-ed into the mantissa of 1024.0, minus
 //     1024 + z (nibbles in bits 4..7 give 16 (q - z));
@@ -60,6 +67,27 @@ __device__ __forceinline__ float wave_total(float v) {
   return (a + b) + (c + d);
 }
 
+// Raw-buffer descriptor words, for inline asm (the format of buffer_over).
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), (uint32_t)kBufferFlags};
+}
+
+// Global -> LDS copy of 4 bytes per lane: lane i's dword at byte voff of the resource lands at
+// LDS byte lds + 4 i.  The asm is taken to touch the memory of dep (a pointer the later loads
+// read through), so that the compiler moves no such load across it: a counted wait for the
+// copy relies on which loads were issued after it.
+__device__ __forceinline__ void copy_dword_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds, const void* dep) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds), "s"(dep) : "memory");
+}
+
+// Bytes of one wave's LDS copy of the scales and zero-points of rows rows (G groups a row).
+__host__ __device__ inline uint32_t stage_bytes(uint32_t rows, uint32_t G, bool sym) {
+  return ((rows * G * 2u + 255u) & ~255u) + (sym ? 0u : ((rows * G + 255u) & ~255u));
+}
+
 // Four fp16 pairs (q - z) of one dword of codes (8 nibbles): nibble OR-ed into 1024.0 minus
 // 1024 + z (1024 + 16 z for the nibbles in bits 4..7).  Slot order (k0, k4, k1, k5, k2, k6,
 // k3, k7); the odd k carry 16 (q - z).
@@ -78,7 +106,8 @@ __device__ __forceinline__ f16x8 dequant(uint32_t dw, uint32_t bias, f16x2 b1, f
 // SHARE (a row has at most 64 groups): lane l loads the scale and zero of group l only, and a
 // lane reads the values of its chunks' groups from the owning lanes (ds_bpermute), i.e. two
 // coalesced loads per row instead of two per chunk.  The rows of a wave are processed with all
-// 64 lanes active, so every source lane of the exchange holds its value.
+// 64 lanes active, so every source lane of the exchange holds its value.  With the LDS copy
+// (STAGE), s and z are read from LDS instead of memory.
 template <int J, bool SHARE>
 struct RowBuf {
   u32x4 w[J];
@@ -86,7 +115,7 @@ struct RowBuf {
   uint32_t z[SHARE ? 1 : J];      // zero-point
 };
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, bool STAGE, int RING>
 __global__ __launch_bounds__(BLOCK) void gemv_kernel(
     const uint16_t* __restrict__ X, int M, int64_t N, int K, int g,
     const u32x4* __restrict__ packed, const uint16_t* __restrict__ scales,
@@ -98,8 +127,23 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wpb = BLOCK / kWave;
   const int64_t nw = (int64_t)gridDim.x * wpb;
-  const int64_t n0 = (int64_t)blockIdx.x * wpb +
-                    __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // wave-uniform
+  const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // wave in block
+  const int64_t n0 = (int64_t)blockIdx.x * wpb + wib;                            // wave-uniform
+  static_assert(!STAGE || SHARE, "the LDS copy holds one scale and zero-point per lane and row");
+
+  // The wave's rows: rbase, rbase + rstride, ... below rend.  STAGE: a contiguous range, the
+  // waves' counts differing by at most one (N < 2^31, checked at launch); otherwise every nw-th
+  // row from n0.
+  int64_t rbase = n0, rstride = nw, rend = N;
+  uint32_t rmax = 0;                           // STAGE: rows of the busiest wave
+  if constexpr (STAGE) {
+    const uint32_t q = (uint32_t)N / (uint32_t)nw, r = (uint32_t)N - q * (uint32_t)nw;
+    const uint32_t w = (uint32_t)n0;
+    rbase = (int64_t)(w * q + min(w, r));
+    rstride = 1;
+    rend = rbase + (int64_t)(q + (w < r ? 1u : 0u));
+    rmax = q + (r != 0u ? 1u : 0u);
+  }
 
   int goff[J];
   bool cval[J];
@@ -123,7 +167,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   // and meet x = 0), and rows past N are not stored.
   const int gown = min(lane, G - 1);           // SHARE: the group this lane loads
   auto load = [&](RowBuf<J, SHARE>& b, int64_t row) __attribute__((always_inline)) {
-    const bool live = row < N;                  // wave-uniform
+    const bool live = row < rend;               // wave-uniform
     const size_t r = live ? (size_t)row : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_over(packed + r * C, live ? (uint32_t)C * 16u : 0u);
     const __amdgpu_buffer_rsrc_t rs = buffer_over(scales + r * G, live ? (uint32_t)G * 2u : 0u);
@@ -137,9 +181,25 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
         if (!SYM) b.z[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, goff[j], 0, 0);
       }
     }
-    if (SHARE) {
+    if (SHARE && !STAGE) {
       b.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * gown, 0, 0);
       if (!SYM) b.z[0] = __builtin_amdgcn_raw_buffer_load_b8(rz, gown, 0, 0);
+    }
+  };
+
+  // STAGE: the wave's LDS area, after X's: its rows' scales (rmax G fp16) then zero-points
+  // (rmax G bytes), each padded to 256 bytes; ldsz reads local row k's pair for group gown
+  // (rows past the wave's end read row 0's, never used).
+  const uint32_t x_lds = ((uint32_t)(M * C * 68) + 15u) & ~15u;
+  const uint32_t s_bytes = ((rmax * (uint32_t)G * 2u + 255u) & ~255u);
+  const uint32_t sz_lds = x_lds + (uint32_t)wib * stage_bytes(rmax, (uint32_t)G, SYM);
+  const uint32_t nrows = (uint32_t)(rend - rbase);
+  auto ldsz = [&](RowBuf<J, SHARE>& b, int64_t k) __attribute__((always_inline)) {
+    if constexpr (STAGE) {
+      const uint8_t* a = reinterpret_cast<const uint8_t*>(lds4) + sz_lds;
+      const uint32_t kk = ((uint32_t)k < nrows ? (uint32_t)k : 0u) * (uint32_t)G + (uint32_t)gown;
+      b.s[0] = *reinterpret_cast<const uint16_t*>(a + 2u * kk);
+      if (!SYM) b.z[0] = a[s_bytes + kk];
     }
   };
 
@@ -165,7 +225,7 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   // then queue behind the whole first round of rows (the Llama-7B up-projection, whose first
   // round is the whole layer: 8.9 -> 7.5 us; the 70B-shaped layer unchanged within noise).
   RowBuf<J, SHARE> b0, b1, b2;
-  load(b0, n0);
+  load(b0, rbase);
 
   u32x4* xs = lds4;                                                 // [M][4][C]
   float* fs = reinterpret_cast<float*>(lds4 + (size_t)M * 4 * C);   // [M][C]
@@ -341,32 +401,54 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
   // exact form has a loop of its own (one row at a time), so that the pipelined loop holds no
   // load but its rows' (a load under a branch makes the compiler wait for every load in flight).
   auto run = [&](auto process) __attribute__((always_inline)) {
-    const int64_t step = RING * nw;
-    for (int64_t n = n0; n < N; n += step) {
+    const int64_t step = RING * rstride;
+    int64_t k = 0;                              // local index of row n
+    for (int64_t n = rbase; n < rend; n += step, k += RING) {
       process(b0, n);
       __builtin_amdgcn_sched_barrier(0);
       load(b0, n + step);
+      ldsz(b0, k + RING);
       __builtin_amdgcn_sched_barrier(0);
-      if (n + nw < N) process(b1, n + nw);
+      if (n + rstride < rend) process(b1, n + rstride);
       __builtin_amdgcn_sched_barrier(0);
-      load(b1, n + nw + step);
+      load(b1, n + rstride + step);
+      ldsz(b1, k + 1 + RING);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (RING == 3) {
-        if (n + 2 * nw < N) process(b2, n + 2 * nw);
+        if (n + 2 * rstride < rend) process(b2, n + 2 * rstride);
         __builtin_amdgcn_sched_barrier(0);
-        load(b2, n + 2 * nw + step);
+        load(b2, n + 2 * rstride + step);
+        ldsz(b2, k + 2 + RING);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  load(b1, n0 + nw);
-  if constexpr (RING == 3) load(b2, n0 + 2 * nw);
+  if constexpr (STAGE) {
+    // issued here, after X, like the rows' second round: requested before X, the copies
+    // delayed it
+    const uint32_t nb = nrows * (uint32_t)G;
+    const u32x4 rs = buffer_words(scales + (size_t)rbase * G, nb * 2u);
+    const u32x4 rz = buffer_words(zeros + (size_t)rbase * G, nb);
+    const uint32_t a = (uint32_t)(uintptr_t)lds4 + sz_lds;
+    for (uint32_t i = 0; i < s_bytes; i += 256u) copy_dword_to_lds(rs, i + 4u * lane, a + i, packed);
+    if (!SYM) {
+      const uint32_t z_bytes = (rmax * (uint32_t)G + 255u) & ~255u;
+      for (uint32_t i = 0; i < z_bytes; i += 256u) copy_dword_to_lds(rz, i + 4u * lane, a + s_bytes + i, packed);
+    }
+  }
+  load(b1, rbase + rstride);
+  if constexpr (RING == 3) load(b2, rbase + 2 * rstride);
+  // STAGE: exactly the (RING - 1) J loads of rows 1 and 2 were issued after the copies (the
+  // asm keeps loads through packed on their side of it)
+  if constexpr (STAGE) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RING - 1) * J), "s"(packed) : "memory");
   if (exact) {                                 // block-uniform; rows one at a time
-    for (int64_t n = n0; n < N; n += nw) {
+    int64_t k = 0;
+    for (int64_t n = rbase; n < rend; n += rstride, ++k) {
       // X is read again for every row (a compiler barrier keeps its loads in the loop rather
       // than hoisted into registers for all rows)
       asm volatile("" ::: "memory");
       load(b0, n);
+      ldsz(b0, k);
       process_exact(b0, n);
     }
     return;
@@ -380,6 +462,9 @@ __global__ __launch_bounds__(BLOCK) void gemv_kernel(
       xe |= (uint32_t)((__builtin_amdgcn_frexp_expf(fs[c]) - 1) & 0xff) << (8 * j);   // fs = 2^(exp - 1)
     }
   }
+  ldsz(b0, 0);
+  ldsz(b1, 1);
+  if constexpr (RING == 3) ldsz(b2, 2);
   run(process_fast);
 }
 
@@ -399,19 +484,39 @@ int64_t resident_blocks(Kernel kernel, int block, size_t lds, std::atomic<uint64
   return nb;
 }
 
-template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, int RING>
+// STAGE: hipErrorNotSupported (nothing launched) when a wave would own fewer than kStageRows
+// rows, its LDS copy does not fit or the copy's conditions fail; the caller then launches the
+// form without it.
+constexpr int64_t kStageRows = 4;
+
+template <int MT, int J, bool SYM, int BLOCK, bool FULL, bool SHARE, bool STAGE, int RING>
 hipError_t launch_one(const void* X, int M, int64_t N, int64_t K, int g, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus,
                       hipStream_t stream) {
   static std::atomic<uint64_t> memo{0};
-  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, RING>;
+  const auto kernel = gemv_kernel<MT, J, SYM, BLOCK, FULL, SHARE, STAGE, RING>;
   const int64_t C = K >> 5;
   if ((int64_t)M * C > BLOCK) return hipErrorInvalidValue;   // one staging thread per chunk of X
-  const size_t lds = (size_t)M * C * 64 + (size_t)M * C * 4;
+  const size_t x_lds = ((size_t)M * C * 68 + 15) & ~(size_t)15;   // X's fp16 planes and factors
   const int64_t wpb = BLOCK / kWave;
   int64_t blocks = (N + wpb - 1) / wpb;
-  const int64_t cap = (int64_t)num_cus * resident_blocks(kernel, BLOCK, lds, memo);
-  if (blocks > cap) blocks = cap;
+  size_t lds = x_lds;
+  // the copies move whole dwords of each wave's range: 4 | G keeps a range's ends on dwords
+  if (STAGE && (N >= ((int64_t)1 << 31) || (K / g) % 4 != 0 ||
+                (((uintptr_t)scales | (SYM ? (uintptr_t)0 : (uintptr_t)zeros)) & 3) != 0))
+    return hipErrorNotSupported;
+  // the grid is what is resident; with the copy, the LDS per block grows as the grid shrinks
+  for (;;) {
+    if (STAGE) {
+      const int64_t rmax = (N + blocks * wpb - 1) / (blocks * wpb);
+      lds = x_lds + (size_t)wpb * stage_bytes((uint32_t)rmax, (uint32_t)(K / g), SYM);
+      if (lds > 160 * 1024) return hipErrorNotSupported;
+    }
+    const int64_t cap = (int64_t)num_cus * resident_blocks(kernel, BLOCK, lds, memo);
+    if (blocks <= cap) break;
+    blocks = cap;
+  }
+  if (STAGE && blocks * wpb * kStageRows > N) return hipErrorNotSupported;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(BLOCK), lds, stream,
                      (const uint16_t*)X, M, N, (int)K, g, (const u32x4*)packed,
                      (const uint16_t*)scales, (const uint8_t*)zeros, (uint16_t*)Y);
@@ -424,11 +529,15 @@ hipError_t launch_mtj(const void* X, int M, int64_t N, int64_t K, int g, bool sy
                       int num_cus, hipStream_t stream) {
   const bool full = (K >> 5) == kWave * J;
   const bool share = K / g <= kWave;
-#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV)                                                        \
-  return launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, RING>(X, M, N, K, g, packed, scales, zeros, \
-                                                             Y, num_cus, stream)
-#define Q4_GEMV_SHARE(SYMV, FULLV)                                                           \
-  if (share) { Q4_GEMV_ONE(SYMV, FULLV, true); } else { Q4_GEMV_ONE(SYMV, FULLV, false); }
+#define Q4_GEMV_ONE(SYMV, FULLV, SHAREV, STAGEV)                                                 \
+  launch_one<MT, J, SYMV, BLOCK, FULLV, SHAREV, STAGEV, RING>(X, M, N, K, g, packed, scales, zeros, \
+                                                              Y, num_cus, stream)
+#define Q4_GEMV_SHARE(SYMV, FULLV)                                                       \
+  if (share) {                                                                           \
+    const hipError_t e = Q4_GEMV_ONE(SYMV, FULLV, true, true);                           \
+    return e == hipErrorNotSupported ? Q4_GEMV_ONE(SYMV, FULLV, true, false) : e;        \
+  }                                                                                      \
+  return Q4_GEMV_ONE(SYMV, FULLV, false, false);
   if (sym) {
     if (full) { Q4_GEMV_SHARE(true, true); } else { Q4_GEMV_SHARE(true, false); }
   } else {
