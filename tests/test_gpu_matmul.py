@@ -204,6 +204,35 @@ def test_gemv_many_rows_per_wave_exact_path(M):
         _check_every_element(Y, X_bits, qw, g, mode, "gemv-many-rows-exact", "gemv")
 
 
+@pytest.mark.parametrize("M,N,K,g", [(4, 8200, 4096, 64), (8, 8195, 2048, 32), (16, 8300, 4096, 128),
+                                     (3, 8209, 8192, 128), (12, 8250, 1024, 64), (6, 9000, 8192, 128),
+                                     (1, 8192, 512, 32), (4, 8200, 8192, 64)])
+def test_decode_many_row_blocks(M, N, K, g):
+    """Matrix-core decode on shapes with at least two 16-row blocks per workgroup on a 256-CU
+    device, where the workgroup copies each row block's scales and zero-points into LDS slots
+    shared by its waves (K = 8192 at g = 64 does not fit them and keeps the per-wave copies):
+    every element of Y, ragged N, both modes."""
+    assert decode_fits(M, N, K, g)
+    rng = np.random.default_rng(N + K + g + M)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        qw = orc.quantize_rtn_ref(W_bits, g, mode)
+        Y = _gpu_matmul(X_bits, _upload(*qw), g, mode, "decode")
+        _check_every_element(Y, X_bits, qw, g, mode, "decode-many-blocks", "decode")
+
+
+@pytest.mark.parametrize("M", [2, 5, 16])
+def test_decode_many_row_blocks_exact_path(M):
+    """X whose fp16 staging would lose bits (the bf16 exact path) with shared scale slots."""
+    N, K, g = 8300, 2048, 128
+    W_bits, X_bits = adversarial_layer(N, K, M, 36, seed=11 + M)
+    for mode in ("asym", "sym"):
+        qw = orc.quantize_rtn_ref(W_bits, g, mode)
+        Y = _gpu_matmul(X_bits, _upload(*qw), g, mode, "decode")
+        _check_every_element(Y, X_bits, qw, g, mode, "decode-many-blocks-exact", "decode")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K,g", [(100, 1536, 64), (300, 2048, 128), (33, 4096, 32), (129, 8192, 64),
                                    (50, 3072, 128), (17, 512, 32), (257, 4096, 128), (70, 6144, 128)])

@@ -23,10 +23,20 @@
 // Loads.  Each 1 KiB LDS-DMA instruction reads 4 rows x 256 contiguous bytes of codes
 // (requests of whole cache lines and more per row: as fast as contiguous streaming), written
 // to LDS with the 16-byte chunk c of row r at position (c ^ r) within its row, so that the
-// fragment reads of 16 rows at one chunk hit 16 distinct bank groups.  The fp16 scales and
-// uint8 zero-points of the stage come the same way, one dword per lane.  A wave keeps S stages
+// fragment reads of 16 rows at one chunk hit 16 distinct bank groups.  A wave keeps S stages
 // in flight and waits for the oldest with an explicit vmcnt: every global load of the main
 // loop is one of these LDS-DMA copies.
+// Scales and zero-points: each wave copies its groups of the stage's 16 rows into the stage
+// (one dword per lane, 16 rows x a few bytes: small scattered requests).  SH form, when a
+// workgroup has two row blocks or more and the LDS allows: a row block's scales and
+// zero-points are one contiguous range of each array (16 rows x K/g groups), and the
+// workgroup copies the whole range into an LDS slot shared by its waves, wave w the w-th of
+// WS equal pieces, instead.  The copies for a row block ride with the stage of the row block
+// before it, so the barrier that ends that row block (every wave has waited for its stage by
+// then) makes the whole range visible; S + 2 slots cover the row blocks in flight.  (70B-shaped
+// layer, M = 4 / 8 / 16: 28.1-28.8 / 29.8-30.1 / 33.8-34.1 -> 26.9 / 29.2-29.7 / 32.9-33.3 us;
+// with one row block per workgroup, as in the 4096 x 4096 layer, the first range's barrier
+// cost more than it saved: 8.7 -> 9.4 us.)
 //
 // Arithmetic (fast path, exact up to fp32 summation and the final bf16 rounding):
 //   * (q - z) is formed exactly in fp16: the nibble OR-ed into the mantissa of 1024.0, minus
@@ -125,8 +135,10 @@ __device__ __forceinline__ bf16x8 to_bf16(f16x8 h) {
   return r;
 }
 
-// Stage geometry of one wave: 16 rows of KR weights (codes), their scales and zero-points.
-template <int P, int NSL, int TK, bool SYM>
+// Stage geometry of one wave: 16 rows of KR weights (codes), and either its groups' scales
+// and zero-points of those rows or (SH) its piece of the next row block's (KR / g groups of
+// 16 rows: the range's WS-th part, copied to the shared slot).
+template <int P, int NSL, int TK, bool SYM, bool SH>
 struct Geo {
   static constexpr int MP = 16 / P;                  // token slots per part
   static constexpr int PW = NSL * 32;                // k per part
@@ -138,9 +150,9 @@ struct Geo {
   static constexpr int NSI = (8 * NG + 63) / 64;     // scale dword copies (64 dwords each)
   static constexpr int NZI = SYM ? 0 : (4 * NG + 63) / 64;
   static constexpr int L = NCI + NSI + NZI;          // vector memory operations per stage
-  static constexpr uint32_t SOFF = 16u * RBY;        // scales inside the stage
+  static constexpr uint32_t SOFF = 16u * RBY;        // scales inside the stage (not SH)
   static constexpr uint32_t ZOFF = SOFF + 256u * NSI;
-  static constexpr uint32_t STAGE = ZOFF + 256u * NZI;
+  static constexpr uint32_t STAGE = SH ? SOFF : ZOFF + 256u * NZI;   // LDS bytes of one stage
   static constexpr int DPT = TK / 32;                // dwords per lane per tile
   static constexpr int TPP = PW / TK;                // tiles per part
   static_assert(RBY % 256 == 0, "whole 256-byte segments per row");
@@ -149,12 +161,12 @@ struct Geo {
 };
 
 // At most 8 waves per workgroup: two waves per SIMD, 256 registers each (the X range takes 64).
-template <int P, int NSL, int TK, bool SYM>
+template <int P, int NSL, int TK, bool SYM, bool SH>
 __global__ __launch_bounds__(8 * 64) void decode_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, uint16_t* __restrict__ Y,
     int S) {
-  using Gm = Geo<P, NSL, TK, SYM>;
+  using Gm = Geo<P, NSL, TK, SYM, SH>;
   constexpr int MP = Gm::MP, DPT = Gm::DPT, KR = Gm::KR, NG = Gm::NG;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -168,7 +180,11 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   const int K0 = ((w + (int)blockIdx.x) % WS) * KR;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const uint32_t my_stages = lds0 + (uint32_t)(w * S) * Gm::STAGE;
-  const uint32_t red0 = lds0 + (uint32_t)(WS * S) * Gm::STAGE;
+  // SH: shared slots of a row block's scales (32 G bytes) then zero-points (16 G), S + 2 of them
+  const uint32_t slot_bytes = 32u * (uint32_t)G + (SYM ? 0u : 16u * (uint32_t)G);
+  const int NSLOT = SH ? S + 2 : 0;
+  const uint32_t sh0 = (uint32_t)(WS * S) * Gm::STAGE;                // offset in lds
+  const uint32_t red0 = lds0 + sh0 + (uint32_t)NSLOT * slot_bytes;
 
   // ---- X range -> registers: slot m = (part, token), slices s = (tile, dword) ----
   const int part = m / MP, tok = m % MP;
@@ -194,30 +210,61 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   uint32_t cv[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) cv[q] = (code_lane ^ (64u * (uint32_t)q)) + 4u * (uint32_t)q * rowbytes;
-  // scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2); zeros:
-  // dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
+  // not SH: scales: dword d = 64 q + l of the stage is dword d % (NG / 2) of row d / (NG / 2);
+  // zeros: dword d % (NG / 4) of row d / (NG / 4) (rows past 15 are padding and land past the
   // stage's 16 rows in LDS)
   uint32_t sv[Gm::NSI], zv[Gm::NZI > 0 ? Gm::NZI : 1];
+  if constexpr (!SH) {
 #pragma unroll
-  for (int q = 0; q < Gm::NSI; ++q)
-    sv[q] = (uint32_t)(q * (128 / NG) + lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
+    for (int q = 0; q < Gm::NSI; ++q)
+      sv[q] = (uint32_t)(q * (128 / NG) + lane / (NG / 2)) * (uint32_t)G * 2u + 4u * (uint32_t)(lane % (NG / 2));
 #pragma unroll
-  for (int q = 0; q < Gm::NZI; ++q)
-    zv[q] = (uint32_t)(q * (256 / NG) + lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
-  auto issue = [&](int slot, int rb) {
+    for (int q = 0; q < Gm::NZI; ++q)
+      zv[q] = (uint32_t)(q * (256 / NG) + lane / (NG / 4)) * (uint32_t)G + 4u * (uint32_t)(lane % (NG / 4));
+  }
+  // SH: scales and zero-points of row block rb into shared slot j: this wave's piece, 32 NG bytes
+  // of scales and 16 NG of zero-points at piece w of each range (lanes past the piece idle, so
+  // that no lane writes into another wave's piece; every copy keeps its first 16 lanes).
+  // Pieces past the end of the arrays read as 0 (resources end at the arrays' ends; none for
+  // rb >= NB, whose slot is never read: the copy is still issued, so that every stage holds L
+  // copies).
+  auto issue_sz = [&](int rb, int j) {
+    const uint32_t total = (uint32_t)N * (uint32_t)G;                // groups in the arrays
+    const uint32_t gp = (uint32_t)min(rb, NB) * 16u * (uint32_t)G + (uint32_t)(w * 16 * NG);   // piece start
+    const uint32_t left = gp < total ? total - gp : 0u;
+    const uint32_t dst = lds0 + sh0 + (uint32_t)j * slot_bytes;
+    const u32x4 rs = buffer_words(scales + (gp < total ? gp : 0u), min(left, 16u * (uint32_t)NG) * 2u);
+#pragma unroll
+    for (int q = 0; q < Gm::NSI; ++q)
+      if (256 * q + 4 * lane < 32 * NG) dma4(rs, 256u * (uint32_t)q + 4u * (uint32_t)lane, 0u, dst + (uint32_t)(w * 32 * NG + 256 * q));
+    if constexpr (!SYM) {
+      const u32x4 rz = buffer_words(zeros + (gp < total ? gp : 0u), min(left, 16u * (uint32_t)NG));
+#pragma unroll
+      for (int q = 0; q < Gm::NZI; ++q)
+        if (256 * q + 4 * lane < 16 * NG)
+          dma4(rz, 256u * (uint32_t)q + 4u * (uint32_t)lane, 0u, dst + 32u * (uint32_t)G + (uint32_t)(w * 16 * NG + 256 * q));
+    }
+  };
+  // stage j (row block rb, the j-th of this workgroup): codes, then the row block's scales and
+  // zero-points of this wave's groups (SH: the next row block's piece)
+  auto issue = [&](int slot, int rb, int j) {
     const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
     const uint32_t n0 = (uint32_t)rb * 16u;                          // rb < NB
-    const uint32_t g0 = n0 * (uint32_t)G + (uint32_t)(K0 / TK);      // first group of the range
     const u32x4 rw = buffer_words(packed + (size_t)n0 * rowbytes + (size_t)(K0 / 2),
                                   ((uint32_t)N - n0) * rowbytes - (uint32_t)(K0 / 2));
-    const u32x4 rs = buffer_words(scales + g0, ((uint32_t)N * (uint32_t)G - g0) * 2u);
-    const u32x4 rz = buffer_words(zeros + g0, SYM ? 0u : (uint32_t)N * (uint32_t)G - g0);
 #pragma unroll
     for (int i = 0; i < Gm::NCI; ++i) dma16(rw, cv[i & 3], 256u * (uint32_t)(i >> 2), st + 1024u * (uint32_t)i);
+    if constexpr (SH) {
+      issue_sz(rb + (int)gridDim.x, (j + 1) % NSLOT);
+    } else {
+      const uint32_t g0 = n0 * (uint32_t)G + (uint32_t)(K0 / TK);    // first group of the range
+      const u32x4 rs = buffer_words(scales + g0, ((uint32_t)N * (uint32_t)G - g0) * 2u);
+      const u32x4 rz = buffer_words(zeros + g0, SYM ? 0u : (uint32_t)N * (uint32_t)G - g0);
 #pragma unroll
-    for (int q = 0; q < Gm::NSI; ++q) dma4(rs, sv[q], 0u, st + Gm::SOFF + 256u * (uint32_t)q);
+      for (int q = 0; q < Gm::NSI; ++q) dma4(rs, sv[q], 0u, st + Gm::SOFF + 256u * (uint32_t)q);
 #pragma unroll
-    for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
+      for (int q = 0; q < Gm::NZI; ++q) dma4(rz, zv[q], 0u, st + Gm::ZOFF + 256u * (uint32_t)q);
+    }
   };
 
   // With two or four parts the first stage is requested right behind X (the conversion of X
@@ -227,8 +274,11 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   // 42.5 -> 28.3 / 30.0 / 37.8-39.1 us, config 3 9.9 -> 9.2 us)
   const int stride = gridDim.x;
   constexpr int EARLY = P == 1 ? 0 : 1;
+  // SH: the first row block's scales and zero-points ahead of its stage (loads complete in
+  // order)
+  if constexpr (SH && EARLY > 0) issue_sz((int)blockIdx.x, 0);
   for (int s = 0; s < min(S, EARLY); ++s)
-    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+    if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride, s);
 
   // The range of |x| is taken on the bf16 bit patterns (their order as unsigned 16-bit integers
   // is the order of the values), two at a time; the smallest nonzero one as the smallest of
@@ -260,8 +310,9 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   // overlaps their latency (M = 16: 35.0 -> 33.9 us; config 3 8.8 -> 8.7 us)
   if constexpr (P == 1) {
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SH) issue_sz((int)blockIdx.x, 0);
     for (int s = 0; s < S; ++s)
-      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride, s);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -292,7 +343,7 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
 
   if constexpr (P > 1)
     for (int s = EARLY; s < S; ++s)
-      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride);
+      if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride, s);
 
   // fragment reads: B column n = m (row of the block), quarter kq
   const int n = m;
@@ -306,7 +357,14 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
       const int slot = it % S;
       const int later = min(S - 1, (NB - 1 - rb) / stride);           // stages issued after this one
       wait_stages<Gm::L>(later);
+      // SH: the first row block's scales and zero-points came before any stage: once every
+      // wave has waited for its first stage they are all in LDS (later ones: the previous row
+      // block's closing barrier)
+      if (SH && it == 0) lds_barrier();
       const uint32_t st = my_stages + (uint32_t)slot * Gm::STAGE;
+      // this row block's scales and zero-points: row n's groups from the wave's first one
+      const uint32_t shs = sh0 + (uint32_t)(it % NSLOT) * slot_bytes;
+      const uint32_t gn = (uint32_t)(n * G + K0 / TK);
       // One part at a time: its accumulator collects the part's tiles, then the lanes whose D rows
       // belong to that part (4 kq / MP == p) keep it.  The tiles are generated at compile time
       // (a fold over an index sequence), so every X register index is a constant.
@@ -331,8 +389,14 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
         } else {
           dw[0] = *reinterpret_cast<const uint32_t*>(lds + off);
         }
-        const uint32_t sbits = *reinterpret_cast<const uint16_t*>(lds + (st - lds0) + Gm::SOFF + 2 * (n * NG + t));
-        const uint32_t z = SYM ? 8u : (uint32_t)lds[(st - lds0) + Gm::ZOFF + n * NG + t];
+        uint32_t sbits, z;
+        if constexpr (SH) {
+          sbits = *reinterpret_cast<const uint16_t*>(lds + shs + 2u * (gn + (uint32_t)t));
+          z = SYM ? 8u : (uint32_t)lds[shs + 32u * (uint32_t)G + gn + (uint32_t)t];
+        } else {
+          sbits = *reinterpret_cast<const uint16_t*>(lds + (st - lds0) + Gm::SOFF + 2 * (n * NG + t));
+          z = SYM ? 8u : (uint32_t)lds[(st - lds0) + Gm::ZOFF + n * NG + t];
+        }
         const f16x2 b1 = as_f16x2((0x6400u + z) * 0x00010001u);
         const f16x2 b16 = as_f16x2((0x6400u + 16u * z) * 0x00010001u);
         f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
@@ -355,7 +419,7 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
       for_each_index(tile, std::make_integer_sequence<int, P * Gm::TPP>{});
       // this slot's LDS reads are done: refill it with the row block S strides ahead
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (rb + S * stride < NB) issue(slot, rb + S * stride);
+      if (rb + S * stride < NB) issue(slot, rb + S * stride, it + S);
 
       // factor of output rows 4 kq + r (token slots of this lane's D fragment)
 #pragma unroll
@@ -387,21 +451,23 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   else run(std::false_type{});
 }
 
-// Launch geometry of a shape: parts P, slices NSL, waves WS and stages S.
+// Launch geometry of a shape: parts P, slices NSL, waves WS and stages S; sh: the shared
+// scale and zero-point slots.
 struct Plan {
   int P = 0, NSL = 0, WS = 0, S = 0;
+  bool sh = false;
   size_t lds = 0;
 };
 
 // Bytes of one stage and vector memory operations per stage (as Geo computes them).
-size_t stage_bytes(int P, int NSL, int g, bool sym, int* ops) {
+size_t stage_bytes(int P, int NSL, int g, bool sym, bool sh, int* ops) {
   const int KR = P * NSL * 32, NG = KR / g;
   const int NSI = (8 * NG + 63) / 64, NZI = sym ? 0 : (4 * NG + 63) / 64;
   *ops = 4 * (KR / 512) + NSI + NZI;
-  return (size_t)16 * (KR / 2) + 256u * NSI + 256u * NZI;
+  return (size_t)16 * (KR / 2) + (sh ? 0u : 256u * NSI + 256u * NZI);
 }
 
-Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym) {
+Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym, bool sh) {
   Plan pl;
   if (M < 1 || M > 16 || !(g == 32 || g == 64 || g == 128)) return pl;
   if (N * (K / 2) >= ((int64_t)1 << 32) || M * K * 2 >= ((int64_t)1 << 32)) return pl;
@@ -423,23 +489,29 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int g, bool sym) {
   const int64_t WS = K / KR;
   if (WS < 1 || WS > kMaxWaves) return pl;
   int ops = 0;
-  const size_t st = stage_bytes(P, NSL, g, sym, &ops);
+  const size_t st = stage_bytes(P, NSL, g, sym, sh, &ops);
   const size_t red = (size_t)2 * WS * kRedBytes;
-  int S = (int)((kLdsMax - red) / ((size_t)WS * st));
+  const size_t slot = sh ? (size_t)(K / g) * (sym ? 32 : 48) : 0;   // a row block's scales and zero-points
+  if (kLdsMax < red + 2 * slot) return pl;
+  int S = (int)((kLdsMax - red - 2 * slot) / ((size_t)WS * st + slot));   // S stages, S + 2 slots
   if (S > 4) S = 4;
   while (S > 2 && (S - 1) * ops > 63) --S;             // the stage waits fit the counter
   if (S < 2) return pl;
-  pl.P = P; pl.NSL = NSL; pl.WS = (int)WS; pl.S = S;
-  pl.lds = (size_t)WS * S * st + red;
+  pl.P = P; pl.NSL = NSL; pl.WS = (int)WS; pl.S = S; pl.sh = sh;
+  pl.lds = (size_t)WS * S * st + (size_t)(S + 2) * slot + red;
   return pl;
 }
 
 template <int P, int NSL, int TK, bool SYM>
 hipError_t launch_one(const Plan& pl, const void* X, int M, int64_t N, int64_t K, const void* packed,
                       const void* scales, const void* zeros, void* Y, int num_cus, hipStream_t stream) {
-  const auto kernel = decode_kernel<P, NSL, TK, SYM>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+  const auto kernel = pl.sh ? decode_kernel<P, NSL, TK, SYM, true> : decode_kernel<P, NSL, TK, SYM, false>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<P, NSL, TK, SYM, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax) != hipSuccess
+          ? hipErrorInvalidValue
+          : hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<P, NSL, TK, SYM, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
   if (attr != hipSuccess) return attr;
   const int64_t NB = (N + 15) / 16;
   const int64_t blocks = NB < num_cus ? NB : num_cus;
@@ -482,14 +554,17 @@ hipError_t launch_mode(const Plan& pl, int g, const void* X, int M, int64_t N, i
 }  // namespace
 
 bool decode_fits(int64_t M, int64_t N, int64_t K, int g) {
-  // the symmetric format needs fewer bytes per stage, so an asymmetric fit covers both
-  return plan_for(M, N, K, g, false).P != 0;
+  // the symmetric format needs fewer bytes per stage, so an asymmetric fit covers both; the
+  // shared slots are taken only where they fit as well
+  return plan_for(M, N, K, g, false, false).P != 0;
 }
 
 hipError_t launch_decode(const void* X, int M, int64_t N, int64_t K, int g, bool sym,
                          const void* packed, const void* scales, const void* zeros, void* Y,
                          int num_cus, hipStream_t stream) {
-  const Plan pl = plan_for(M, N, K, g, sym);
+  // shared scale slots when every workgroup has two row blocks or more and they fit
+  const Plan psh = (N + 15) / 16 >= 2 * (int64_t)num_cus ? plan_for(M, N, K, g, sym, true) : Plan{};
+  const Plan pl = psh.P != 0 ? psh : plan_for(M, N, K, g, sym, false);
   if (pl.P == 0) return hipErrorInvalidValue;
   return sym ? launch_mode<true>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream)
              : launch_mode<false>(pl, g, X, M, N, K, packed, scales, zeros, Y, num_cus, stream);
