@@ -353,7 +353,8 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
     inputs of that workload: W4A16 GEMV over enough distinct quantized copies that the
     Infinity Cache cannot serve them, HIP events around `reps` back-to-back launches through
     the C-ABI with their arguments marshalled once (at under 10 us per launch, the Python
-    binding's per-call cost would otherwise set the pace)."""
+    binding's per-call cost would otherwise set the pace).  Beside it, the same rotation read
+    by a plain streaming kernel: the practical ceiling at this size."""
     from synth import CONFIGS, make_layer
     import numpy as np
     c = CONFIGS[1]
@@ -382,10 +383,41 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     gbs = by / (ms * 1e-3) / 1e9
-    return {"workload": f"{c.name}, {copies} weight copies", "kernel": q4.select_kernel(1, c.N, c.K, c.g),
-            "ms": round(ms, 5), "bytes_per_launch": by,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    out = {"workload": f"{c.name}, {copies} weight copies", "kernel": q4.select_kernel(1, c.N, c.K, c.g),
+           "ms": round(ms, 5), "bytes_per_launch": by,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    # the practical ceiling at this size: a plain streaming read of each copy's packed codes,
+    # back to back over the same rotation (best of a few grid sizes)
+    import ctypes
+    from weight_only_int4_group_amd.build import BENCH_LIB
+    if os.path.exists(BENCH_LIB):
+        blib = ctypes.CDLL(BENCH_LIB)
+        blib.q4b_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+        blib.q4b_stream_read.restype = ctypes.c_int
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(cus * 64 * 4, dtype=torch.int32, device=dev)
+        nb = sets[0][0].numel()
+        best = None
+        for per_cu in (2, 4, 8, 16, 32):
+            run = [(p.data_ptr(), nb, sink.data_ptr(), cus * per_cu, st) for (p, _, _) in sets]
+            for r in range(reps):
+                blib.q4b_stream_read(*run[r % copies])
+            e0.record()
+            for r in range(reps):
+                blib.q4b_stream_read(*run[r % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            if best is None or t < best[0]:
+                best = (t, per_cu)
+        rgbs = nb / (best[0] * 1e-3) / 1e9
+        out["stream_read_same_size"] = {"GB/s": round(rgbs, 1), "frac": round(rgbs / HBM_PEAK_GBS, 4),
+                                        "us": round(best[0] * 1e3, 2), "bytes": nb, "blocks_per_cu": best[1],
+                                        "how": "libq4_bench stream_read over each copy's packed codes, "
+                                               "rotating as the GEMV does; best of 2-32 blocks per CU"}
+    return out
 
 
 def measure_decode_range(torch, q4, reps=300, min_bytes=700e6):
