@@ -13,8 +13,10 @@
 //     is issued at the start of step s.  Rows are XOR-swizzled in 16-byte chunks so that the
 //     MFMA fragment reads hit 16 different bank groups.
 //   * W: each wave owns 64 W rows; a lane loads the 32 codes (16 bytes) it needs per row and
-//     step, one step ahead, and dequantises them in registers straight into MFMA operands, so
-//     every weight of the tile is dequantised exactly once per block.
+//     step ahead of use (one step ahead in the 128-row tile; in the 256-row tile each 16-row
+//     block's codes are requested as soon as its register slot is free, most of two steps
+//     ahead), and dequantises them in registers straight into MFMA operands, so every weight
+//     of the tile is dequantised exactly once per block.
 //   * One barrier per step, after the step's loads have landed.
 // The k order inside a step is permuted identically for both operands (lane group q takes the
 // 32 contiguous k of its codes), which leaves each output sum unchanged.
@@ -354,6 +356,25 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     }
   };
 
+  // One 16-row block's codes (and, edge tiles, its scale and zero-point) of step kt into
+  // slot R: the large tile requests each block as soon as its codes in the slot are dead.
+  auto load_w_nb = [&](auto S, int kt, auto NBC) {
+    constexpr int R = decltype(S)::value;
+    constexpr int nb = decltype(NBC)::value;
+    const int ktc = min(kt, KT - 1);
+    const int gs = (ktc * kStepK) >> lg;
+    const int v = EDGE ? nb : 0;
+    const int rb = EDGE ? 0 : RPW * wave + 16 * nb;
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+      wq[R][nb][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rw, voff_w[v] + 16u * c, rb * (int)wrow + ktc * (kStepK * B / 8), 0));
+    if (REGSZ) {
+      ws[R][nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s[v], 2 * (rb * G + gs), 0);
+      wz[R][nb] = SYM ? kZsym : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, voff_z[v], rb * G + gs, 0);
+    }
+  };
+
   // Name the W registers of slot R (codes, and scales / zeros when they come by register):
   // the compiler then waits for those loads here, and for nothing issued after them.
   // (One asm statement per kind, so that the compiler emits one wait for the whole set.)
@@ -524,12 +545,18 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
         const bf16x8 b = bx[g % (XA + 1)];
         // Four slots, each one MFMA and then a little other work, so that the wave issues the
         // other work while the MFMA executes.  Slot 0: this group's LDS read two groups ahead
-        // and, in the first groups, one of the next step's loads (codes first, then one X
-        // copy per group, then the scale / zero words).
+        // and, in the first groups, one of the next step's copies (one X copy per group, then
+        // the scale / zero words); in groups 34..46, the codes of the step after next.
         mfma_acc(acc[0][mb], a[ks & 1][0], b);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (g + XA < NG) bx[(g + XA) % (XA + 1)] = xfrag(g + XA);
-        if constexpr (g == 0) load_w(Slot<R ^ 1>{}, kt + 1);
+        // block nb of slot R was last read in group 33 + 4 nb (sub-step 3 of this step): the
+        // block's codes of step kt + 2 are requested into it in group 34 + 4 nb, which gives
+        // them until group 47 of the next step (against groups 0 -> 47 of one step when a
+        // slot was refilled at the start of the step it feeds: 207 -> 202 us at g = 128, and
+        // 237 -> 201 us for 8-bit codes, whose loads are twice as large)
+        if constexpr (g >= 34 && g <= 46 && (g - 34) % 4 == 0)
+          load_w_nb(Slot<R>{}, kt + 2, std::integral_constant<int, (g - 34) / 4>{});
         if constexpr (g < kDmaOps) copy_x_piece(R ^ 1, kt + 1, g);
         if constexpr (g == kDmaOps) { if (!REGSZ) copy_sz(R ^ 1, kt + 1); }
         __builtin_amdgcn_sched_barrier(0);
@@ -585,6 +612,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     if (!REGSZ) copy_sz(0, 0);
     load_w(Slot<0>{}, 0);
     wait_codes(Slot<0>{});
+    load_w(Slot<1>{}, 1);                    // the codes of step 1 (slot 1), two steps ahead
     prep_scales(Slot<0>{}, 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -597,6 +625,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       step_large(Slot<1>{}, kt + 1);
     }
     if (kt < KT) step_large(Slot<0>{}, kt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last steps' look-ahead loads (unused)
     drain_mfma();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
