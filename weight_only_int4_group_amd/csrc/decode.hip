@@ -14,7 +14,10 @@
 // waves split K: wave w owns the K range [v KR, (v + 1) KR), v = (w + workgroup) mod WS.  A
 // wave keeps its X range in registers for the whole kernel (the A operand of every row block)
 // and streams its W range of each row block through LDS; the WS partial sums of a row block
-// meet in LDS in wave order.
+// meet in LDS in wave order.  With one part (M > 8) the X range arrives through the wave's own
+// stage area before any stage is requested: 1 KiB copies of whole lines, 16 tokens x 512 k at
+// a time, then one LDS read per slice (70B-shaped layer at M = 16: 32.9 -> 30.0 us; 4096 x
+// 4096: 8.7 -> 7.2 us), instead of lane loads that request every line four times.
 // With M <= 8 (or <= 4) tokens, the 16 token slots carry P = 2 (or 4) parts of the wave's
 // K range: slot m holds token m % (16 / P) of part m / (16 / P), and part p's weights go to
 // their own accumulator, whose rows of part p are the only ones kept.  So the same registers
@@ -99,6 +102,11 @@ __device__ __forceinline__ void lds_barrier() {
 // lane, lane i writing [lds + 4 i, + 4).  The address is the resource base + voff + soff.
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+// The same without the non-temporal hint, for X (which every workgroup reads).
+__device__ __forceinline__ void dma16x(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
                : "memory");
 }
 __device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
@@ -190,12 +198,41 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   const int part = m / MP, tok = m % MP;
   const __amdgpu_buffer_rsrc_t rx = buffer_over(X, (uint32_t)M * (uint32_t)K * 2u);
   u32x4 xr[NSL];
+  // One part (M > 8): X goes through the wave's own stage area, 16 slices (16 tokens x 512 k)
+  // at a time, by 1 KiB global -> LDS copies of whole lines (copy t: token t's 512 k, chunk c
+  // of it at position c ^ t, so that 16 tokens' reads of one chunk hit distinct banks), then
+  // one LDS read per slice.  Loaded straight into registers, each 16-byte lane load touches
+  // two lines per token and every line is requested by four instructions.
+  bool xlds = false;
+  if constexpr (P == 1 && NSL >= 16) xlds = (uint32_t)S * Gm::STAGE >= 16384u;   // wave-uniform
+  if (xlds) {
+    if constexpr (P == 1 && NSL >= 16) {
+      const u32x4 rxw = buffer_words(X, (uint32_t)M * (uint32_t)K * 2u);
 #pragma unroll
-  for (int s = 0; s < NSL; ++s) {
-    const int j = s / DPT, u = s % DPT;
-    const int k = K0 + part * Gm::PW + j * TK + kq * (TK / 4) + 8 * u;
-    xr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rx, 2u * ((uint32_t)tok * (uint32_t)K + (uint32_t)k), 0, 0));
+      for (int h = 0; h < NSL / 16; ++h) {
+        if (h > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the area's reads are done
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          dma16x(rxw, 2u * ((uint32_t)t * (uint32_t)K + (uint32_t)(K0 + 512 * h)) + 16u * (uint32_t)(lane ^ t), 0u,
+                 my_stages + 1024u * (uint32_t)t);
+        wait_vm<0>();
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+          const int j = s2 / DPT, u = s2 % DPT;
+          const int c = j * (TK / 8) + kq * (TK / 32) + u;                 // chunk of the 512 k
+          xr[16 * h + s2] = *reinterpret_cast<const u32x4*>(lds + (my_stages - lds0) + 1024u * (uint32_t)tok +
+                                                            16u * (uint32_t)(c ^ tok));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+      const int j = s / DPT, u = s % DPT;
+      const int k = K0 + part * Gm::PW + j * TK + kq * (TK / 4) + 8 * u;
+      xr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rx, 2u * ((uint32_t)tok * (uint32_t)K + (uint32_t)k), 0, 0));
+    }
   }
   // ---- stage copies ----
   // Each row block's copies go through resources based at its first row and this wave's K
@@ -310,6 +347,7 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   // overlaps their latency (M = 16: 35.0 -> 33.9 us; config 3 8.8 -> 8.7 us)
   if constexpr (P == 1) {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // X's reads of the stage area are done
     if constexpr (SH) issue_sz((int)blockIdx.x, 0);
     for (int s = 0; s < S; ++s)
       if ((int)blockIdx.x + s * stride < NB) issue(s, (int)blockIdx.x + s * stride, s);
