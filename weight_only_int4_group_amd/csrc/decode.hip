@@ -14,10 +14,10 @@
 // waves split K: wave w owns the K range [v KR, (v + 1) KR), v = (w + workgroup) mod WS.  A
 // wave keeps its X range in registers for the whole kernel (the A operand of every row block)
 // and streams its W range of each row block through LDS; the WS partial sums of a row block
-// meet in LDS in wave order.  With one part (M > 8) the X range arrives through the wave's own
-// stage area before any stage is requested: 1 KiB copies of whole lines, 16 tokens x 512 k at
-// a time, then one LDS read per slice (70B-shaped layer at M = 16: 32.9 -> 30.0 us; 4096 x
-// 4096: 8.7 -> 7.2 us), instead of lane loads that request every line four times.
+// meet in LDS in wave order.  The X range arrives through the wave's own stage area before any
+// stage is requested: 1 KiB copies of whole lines, then one LDS read per slice, instead of lane
+// loads that request every line four times (70B-shaped layer at M = 4 / 8 / 16: 27.2 / 29.1 /
+// 32.9 -> 25.8 / 26.6 / 30.0 us; 4096 x 4096 at M = 16: 8.7 -> 7.1 us).
 // With M <= 8 (or <= 4) tokens, the 16 token slots carry P = 2 (or 4) parts of the wave's
 // K range: slot m holds token m % (16 / P) of part m / (16 / P), and part p's weights go to
 // their own accumulator, whose rows of part p are the only ones kept.  So the same registers
@@ -198,32 +198,41 @@ __global__ __launch_bounds__(8 * 64) void decode_kernel(
   const int part = m / MP, tok = m % MP;
   const __amdgpu_buffer_rsrc_t rx = buffer_over(X, (uint32_t)M * (uint32_t)K * 2u);
   u32x4 xr[NSL];
-  // One part (M > 8): X goes through the wave's own stage area, 16 slices (16 tokens x 512 k)
-  // at a time, by 1 KiB global -> LDS copies of whole lines (copy t: token t's 512 k, chunk c
-  // of it at position c ^ t, so that 16 tokens' reads of one chunk hit distinct banks), then
-  // one LDS read per slice.  Loaded straight into registers, each 16-byte lane load touches
-  // two lines per token and every line is requested by four instructions.
+  // X goes through the wave's own stage area before it holds a stage: 1 KiB copies of whole
+  // lines, then one LDS read per slice.  The 16 token slots (part, token) of HS = min(NSL, 16)
+  // slices each, 64 HS bytes a slot, are copied at a time (a copy covers 1024 / (64 HS)
+  // slots; the chunk at position p of slot r's row holds chunk p ^ (r % 16) of its X, so that
+  // 16 slots' reads of one chunk hit distinct banks).  Loaded straight into registers, each
+  // 16-byte lane load would touch two lines per token and every line would be requested by four
+  // instructions.
+  constexpr int HS = NSL < 16 ? NSL : 16;               // slices per pass
+  constexpr uint32_t RB = 64u * HS;                      // bytes of one slot per pass
   bool xlds = false;
-  if constexpr (P == 1 && NSL >= 16) xlds = (uint32_t)S * Gm::STAGE >= 16384u;   // wave-uniform
+  if constexpr (HS >= 8) xlds = (uint32_t)S * Gm::STAGE >= 16u * RB;   // wave-uniform
   if (xlds) {
-    if constexpr (P == 1 && NSL >= 16) {
+    if constexpr (HS >= 8) {
       const u32x4 rxw = buffer_words(X, (uint32_t)M * (uint32_t)K * 2u);
 #pragma unroll
-      for (int h = 0; h < NSL / 16; ++h) {
+      for (int h = 0; h < NSL / HS; ++h) {
         if (h > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the area's reads are done
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          dma16x(rxw, 2u * ((uint32_t)t * (uint32_t)K + (uint32_t)(K0 + 512 * h)) + 16u * (uint32_t)(lane ^ t), 0u,
-                 my_stages + 1024u * (uint32_t)t);
+        for (int i = 0; i < (int)(16 * RB / 1024); ++i) {
+          const uint32_t at = 1024u * (uint32_t)i + 16u * (uint32_t)lane;   // this lane's bytes
+          const uint32_t r = at / RB, p = (at % RB) / 16u;                  // slot, chunk position
+          const uint32_t tk = r % (uint32_t)MP, pt = r / (uint32_t)MP;
+          dma16x(rxw, 2u * (tk * (uint32_t)K + (uint32_t)K0 + pt * (uint32_t)Gm::PW + (uint32_t)(HS * 32 * h)) +
+                          16u * (p ^ (r & 15u)), 0u, my_stages + 1024u * (uint32_t)i);
+        }
         wait_vm<0>();
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
+        for (int s2 = 0; s2 < HS; ++s2) {
           const int j = s2 / DPT, u = s2 % DPT;
-          const int c = j * (TK / 8) + kq * (TK / 32) + u;                 // chunk of the 512 k
-          xr[16 * h + s2] = *reinterpret_cast<const u32x4*>(lds + (my_stages - lds0) + 1024u * (uint32_t)tok +
-                                                            16u * (uint32_t)(c ^ tok));
+          const int c = j * (TK / 8) + kq * (TK / 32) + u;                 // chunk of the pass
+          xr[HS * h + s2] = *reinterpret_cast<const u32x4*>(lds + (my_stages - lds0) + RB * (uint32_t)m +
+                                                            16u * (uint32_t)(c ^ m));
         }
       }
+      if constexpr (P > 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // before the first stage
     }
   } else {
 #pragma unroll
