@@ -84,6 +84,21 @@ def read_traffic():
     return d.get("traffic_bytes_per_launch")
 
 
+def warm_up(torch, fn, seconds=0.025, batch=50):
+    """Untimed launches fn(0), fn(1), ... until `seconds` of wall time have passed (synchronising
+    every `batch` launches).  After a pause or a change of work the first 10-20 ms of launches run
+    slower while the clocks settle; every measurement below starts from that settled state."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -125,9 +140,7 @@ def measure_context(torch, q4, sets, X5, W5, w5, reps=10):
     from weight_only_int4_group_amd.build import BENCH_LIB
 
     def timed(fn, n):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        warm_up(torch, fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(n):
@@ -271,8 +284,7 @@ def measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5, copies=3, reps=30, w
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def timed(fn, n):
-        fn(0)
-        torch.cuda.synchronize()
+        warm_up(torch, fn)
         e0, e1 = ev(), ev()
         e0.record()
         for i in range(n):
@@ -329,8 +341,6 @@ def measure_w8(torch, q4, W4, X4, W4_bits, X4_bits, X5, W5, copies=3, reps=30, w
     w5 = q4.quantize_rtn8(W5, 128, "sym")
     Y5 = torch.empty((X5.shape[0], W5.shape[0]), dtype=torch.bfloat16, device=dev)
     gfn = lambda i: q4.matmul_w8_into(X5, *w5, 128, "sym", Y5)
-    for i in range(10):                    # the first launches after other work run slower
-        gfn(i)
     gms = timed(gfn, 20)
     tf = 2.0 * X5.shape[0] * W5.shape[0] * W5.shape[1] / (gms * 1e-3) / 1e12
     res["gemm_g128_M2048"] = {"ms": round(gms, 4), "roofline": {
@@ -375,9 +385,7 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
              Y.data_ptr(), st) for (p, s, z) in sets]
     for a in args:
         assert lib.q4_matmul(*a) == 0
-    for r in range(reps):                          # untimed: the same launches, back to back
-        lib.q4_matmul(*args[r % copies])
-    torch.cuda.synchronize()
+    warm_up(torch, lambda r: lib.q4_matmul(*args[r % copies]))   # untimed: the same launches
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for r in range(reps):
@@ -405,8 +413,7 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
         best = None
         for per_cu in (2, 4, 8, 16, 32):
             run = [(p.data_ptr(), nb, sink.data_ptr(), cus * per_cu, st) for (p, _, _) in sets]
-            for r in range(reps):
-                blib.q4b_stream_read(*run[r % copies])
+            warm_up(torch, lambda r: blib.q4b_stream_read(*run[r % copies]))
             e0.record()
             for r in range(reps):
                 blib.q4b_stream_read(*run[r % copies])
@@ -460,9 +467,7 @@ def measure_decode_range(torch, q4, reps=300, min_bytes=700e6):
                  Y.data_ptr(), st) for (p, s, z) in sets]
         for a in args:
             assert lib.q4_matmul(*a) == 0
-        for r in range(reps):                          # untimed: the same launches, back to back
-            lib.q4_matmul(*args[r % copies])
-        torch.cuda.synchronize()
+        warm_up(torch, lambda r: lib.q4_matmul(*args[r % copies]))   # untimed: the same launches
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for r in range(reps):
