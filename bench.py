@@ -433,7 +433,9 @@ def measure_gemv_7b(torch, q4, reps=200, min_bytes=700e6):
 def measure_decode_range(torch, q4, reps=300, min_bytes=700e6):
     """The M <= 16 decode workloads, each on its seeded synthetic inputs (synth recipe): config 1
     (tiny 128 x 256, M=1, a launch-latency case: time reported), config 3 (batched decode
-    4096 x 4096, M=16, sym), config 4 at M = 4 and 8 (70B-shaped MLP) and the 70B shape at M=16.
+    4096 x 4096, M=16, sym), config 4 at M = 4 and 8 (70B-shaped MLP) and the 70B shape at M=16;
+    beside them the 70B shape at M = 32 (the decode kernel in two 16-row launches) and 64 (the
+    GEMM), the batch sizes between decode and prefill.
     Each rotates over enough distinct quantized weight copies that the Infinity Cache cannot
     serve them; the kernel q4_matmul picks (Q4_KERNEL_AUTO) is launched `reps` times back to back
     through the C-ABI with its arguments marshalled once, between HIP events on the launch
@@ -448,8 +450,9 @@ def measure_decode_range(torch, q4, reps=300, min_bytes=700e6):
     import dataclasses
     c4 = CONFIGS[3]
     c4_16 = dataclasses.replace(c4, M_max=16)     # the config-4 recipe drawn with 16 rows of X
+    c4_64 = dataclasses.replace(c4, M_max=64)     # ... and with 64 (mid-range batches)
     cases = [("config1", CONFIGS[0], 1), ("config3", CONFIGS[2], 16), ("config4_m4", c4, 4),
-             ("config4_m8", c4, 8), ("70b_m16", c4_16, 16)]
+             ("config4_m8", c4, 8), ("70b_m16", c4_16, 16), ("70b_m32", c4_64, 32), ("70b_m64", c4_64, 64)]
     out = {}
     drawn = {}
     for key, c, M in cases:

@@ -63,12 +63,12 @@ typedef enum {
 typedef enum {
     Q4_KERNEL_AUTO = 0,    /* choose by M, N, K, g (see q4_select_kernel)                           */
     Q4_KERNEL_GEMV = 1,    /* decode GEMV, M <= 2: fp32 wave reduction of exact fp16 (q - z) dots  */
-    Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M (M >= 512 with K % 128
-                              == 0 and a power-of-two g: X staged in LDS, W dequantised in
-                              registers; otherwise W dequantised into LDS)                        */
-    Q4_KERNEL_DECODE = 3   /* decode, M <= 16: fp16 MFMA on exact (q - z) and exactly scaled X (bf16
-                              MFMA where X's range inside a K part exceeds fp16's), fp32 per-group
-                              scaling                                                             */
+    Q4_KERNEL_GEMM = 2,    /* bf16 MFMA GEMM on dequantised bf16 tiles, any M (K % 128 == 0 and a
+                              power-of-two g >= 32: X staged in LDS, W dequantised in registers;
+                              otherwise W dequantised into LDS)                                   */
+    Q4_KERNEL_DECODE = 3   /* decode, 16 rows of X per launch: fp16 MFMA on exact (q - z) and exactly
+                              scaled X (bf16 MFMA where X's range inside a K part exceeds fp16's),
+                              fp32 per-group scaling                                              */
 } q4_kernel_t;
 
 typedef enum {
@@ -231,8 +231,10 @@ int q4_awq_search_static(const void* X, int64_t M, const void* Yref, const void*
                          void* zeros, void* errors, void* best, void* stream);
 
 /* As q4_matmul, but with an explicit kernel choice (q4_kernel_t).  Q4_KERNEL_GEMV requires
- * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE requires 1 <= M <= 16,
- * g in {32, 64, 128}, N * K / 2 < 2^32, and K split into at most 8 equal ranges of KR
+ * M == 1 and K <= 16384, or M == 2 and K <= 4096.  Q4_KERNEL_DECODE runs M > 16 as launches
+ * of 16 rows of X and Y (the last one M mod 16 rows), each of which must fit the decode rule;
+ * for a launch of M <= 16 rows it requires g in {32, 64, 128}, N * K / 2 < 2^32, and K split
+ * into at most 8 equal ranges of KR
  * weights: KR = 32 P S with P = 4, 2 or 1 parts for M <= 4, <= 8 or <= 16, S = 16 slices (8
  * for g = 32 at M <= 8, and at M <= 4 for g = 64 or K a multiple of 1024 up to 8192), S
  * halved (down to P S = 16) while K is
@@ -247,8 +249,10 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
                      int32_t kernel, void* stream);
 
 /* The kernel Q4_KERNEL_AUTO picks for this shape (Q4_KERNEL_GEMV, Q4_KERNEL_DECODE or
- * Q4_KERNEL_GEMM), or a negative status for an invalid shape.  Pure host function, no HIP
- * call. */
+ * Q4_KERNEL_GEMM), or a negative status for an invalid shape: the GEMV for M == 1 (K <= 16384),
+ * else the decode kernel where it fits (M <= 16), else the GEMV for M == 2 (K <= 4096), else
+ * the decode kernel in 16-row launches for M <= 48 where every launch fits, else the GEMM.
+ * Pure host function, no HIP call. */
 int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g);
 
 /*

@@ -135,10 +135,16 @@ def test_select_kernel():
     assert q4.select_kernel(3, 4096, 1536, 64) == "decode"      # K = 3 x 512
     assert q4.select_kernel(2, 100, 96, 32) == "gemv"           # K not a multiple of 512
     assert q4.select_kernel(4, 100, 96, 32) == "gemm"
+    # above 16 rows: the decode kernel in 16-row launches up to 48 rows where every launch fits
+    assert q4.select_kernel(17, 28672, 8192, 128) == "decode"
+    assert q4.select_kernel(48, 4096, 4096, 128) == "decode"
+    assert q4.select_kernel(49, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel(32, 8192, 8192, 32) == "gemm"       # g = 32: 16 rows do not fit
+    assert q4.select_kernel(20, 4096, 8192, 32) == "gemm"       # nor the 4-row remainder
     assert q4.select_kernel(4, 100, 1024, 256) == "gemm"        # g above 128
     assert q4.select_kernel(4, 100, 480, 160) == "gemm"         # group straddles a 128 tile
     assert q4.select_kernel(4, 100, 480, 96) == "gemm"
-    assert q4.select_kernel(17, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel(17, 4096, 4096, 128) == "decode"     # 16 + 1 rows
     assert q4.select_kernel(2048, 8192, 8192, 128) == "gemm"
     with pytest.raises(q4.Q4Error):
         q4.select_kernel(1, 8192, 8192, 48)

@@ -39,12 +39,19 @@ def decode_fits(M, N, K, g, mode="asym"):
     return 2 * (K // KR) * stage + 2 * (K // KR) * 1024 <= 160 * 1024
 
 
+def decode_rows_fit(M, N, K, g):
+    """Whether Q4_KERNEL_DECODE runs M rows: launches of 16 rows, the last M mod 16, each fitting."""
+    if M <= 16:
+        return decode_fits(M, N, K, g)
+    return decode_fits(16, N, K, g) and (M % 16 == 0 or decode_fits(M % 16, N, K, g))
+
+
 def kernels_for(M, N, K, g):
     """Every kernel that can run this shape (mirrors the rules stated in include/q4.h)."""
     ks = ["auto", "gemm"]
     if (M == 1 and K <= 16384) or (M == 2 and K <= 4096):
         ks.append("gemv")
-    if decode_fits(M, N, K, g):
+    if decode_rows_fit(M, N, K, g):
         ks.append("decode")
     return tuple(ks)
 
@@ -243,6 +250,19 @@ def test_decode_shapes(M, N, K, g):
     X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
     for mode in ("asym", "sym"):
         _check_full(X_bits, W_bits, g, mode, "decode-shapes", kernels_for(M, N, K, g))
+
+
+@pytest.mark.parametrize("M", [17, 20, 32, 33, 48])
+@pytest.mark.parametrize("N,K,g", [(300, 2048, 128), (4096, 4096, 128), (129, 8192, 64), (70, 4096, 32)])
+def test_decode_in_row_chunks(M, N, K, g):
+    """M > 16 through the decode kernel in 16-row launches (and the choice auto makes), every
+    element against the oracle; the last launch takes M mod 16 rows."""
+    assert decode_rows_fit(M, N, K, g)
+    rng = np.random.default_rng(M * 31 + N + K + g)
+    W_bits = f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    X_bits = f64_to_bf16_bits(rng.normal(0, 1, (M, K)))
+    for mode in ("asym", "sym"):
+        _check_full(X_bits, W_bits, g, mode, "decode-row-chunks", kernels_for(M, N, K, g))
 
 
 @pytest.mark.parametrize("M,N,K,g", [(512, 64, 128, 128), (513, 300, 256, 32), (640, 256, 384, 128),

@@ -57,11 +57,25 @@ bool gemv_fits(int64_t M, int64_t K) {
   return (M == 1 && K <= q4::kGemvMaxK) || (M == 2 && K <= q4::kGemvMaxK2);
 }
 
+// Q4_KERNEL_DECODE above 16 rows runs as launches of 16 rows (the last one M mod 16): every
+// chunk's shape must fit the decode kernel.
+bool decode_rows_fit(int64_t M, int64_t N, int64_t K, int32_t g) {
+  if (M <= 16) return q4::decode_fits(M, N, K, g);
+  return q4::decode_fits(16, N, K, g) && (M % 16 == 0 || q4::decode_fits(M % 16, N, K, g));
+}
+
+// Up to this many rows Q4_KERNEL_AUTO takes the decode kernel in 16-row launches, each of which
+// reads W once: at M = 32 two launches take 14 us on a 4096 x 4096 layer and 59 us on the
+// 70B-shaped one (28672 x 8192), where the GEMM takes about 47 and 96 us at any M up to 64; on
+// the 70B-shaped layer a fourth launch (about 120 us) would be behind the GEMM.
+constexpr int64_t kDecodeMaxRows = 48;
+
 // Q4_KERNEL_AUTO: the decode kernels for small M, the GEMM otherwise.
 int auto_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
   if (M == 1 && gemv_fits(M, K)) return Q4_KERNEL_GEMV;
   if (q4::decode_fits(M, N, K, g)) return Q4_KERNEL_DECODE;
   if (gemv_fits(M, K)) return Q4_KERNEL_GEMV;
+  if (M <= kDecodeMaxRows && decode_rows_fit(M, N, K, g)) return Q4_KERNEL_DECODE;
   return Q4_KERNEL_GEMM;
 }
 
@@ -163,13 +177,21 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
   if (M == 0) return Q4_OK;
   if (kernel == Q4_KERNEL_AUTO) kernel = auto_kernel(M, N, K, g);
   if (kernel == Q4_KERNEL_GEMV && !gemv_fits(M, K)) return Q4_ERR_UNSUPPORTED;
-  if (kernel == Q4_KERNEL_DECODE && !q4::decode_fits(M, N, K, g)) return Q4_ERR_UNSUPPORTED;
+  if (kernel == Q4_KERNEL_DECODE && !decode_rows_fit(M, N, K, g)) return Q4_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool sym = mode == Q4_SYM;
   if (kernel == Q4_KERNEL_GEMV)
     return finish(q4::launch_gemv(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
-  if (kernel == Q4_KERNEL_DECODE)
-    return finish(q4::launch_decode(X, (int)M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
+  if (kernel == Q4_KERNEL_DECODE) {
+    // 16 rows of X and Y per launch (row-major: a chunk is a contiguous block of each)
+    for (int64_t r = 0; r < M; r += 16) {
+      const hipError_t e = q4::launch_decode(static_cast<const uint16_t*>(X) + r * K, (int)(M - r < 16 ? M - r : 16),
+                                             N, K, g, sym, packed, scales, zeros,
+                                             static_cast<uint16_t*>(Y) + r * N, num_cus(), s);
+      if (e != hipSuccess) return finish(e);
+    }
+    return Q4_OK;
+  }
   if (q4::prefill_fits(M, N, K, g))
     return finish(q4::launch_prefill(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
   return finish(q4::launch_gemm(X, M, N, K, g, sym, packed, scales, zeros, Y, num_cus(), s));
