@@ -251,8 +251,10 @@ int q4_matmul_kernel(const void* X, int64_t M, int64_t N, int64_t K, int32_t g, 
 /* The kernel Q4_KERNEL_AUTO picks for this shape (Q4_KERNEL_GEMV, Q4_KERNEL_DECODE or
  * Q4_KERNEL_GEMM), or a negative status for an invalid shape: the GEMV for M == 1 (K <= 16384),
  * else the decode kernel where it fits (M <= 16), else the GEMV for M == 2 (K <= 4096), else
- * the decode kernel in 16-row launches for M <= 48 where every launch fits, else the GEMM.
- * Pure host function, no HIP call. */
+ * the decode kernel in 16-row launches where every launch fits and M <= 16 n, n = the number of
+ * launches that take no longer than the GEMM by a cost model of MI355X (a launch 4.4 us plus
+ * 0.001 us per k plus N K (1/2 + 3/g) bytes at 4.5 TB/s, the GEMM 0.0117 us per k), clamped to
+ * 3 ... 6; else the GEMM.  Pure host function, no HIP call. */
 int q4_select_kernel(int64_t M, int64_t N, int64_t K, int32_t g);
 
 /*

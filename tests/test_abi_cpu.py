@@ -135,10 +135,18 @@ def test_select_kernel():
     assert q4.select_kernel(3, 4096, 1536, 64) == "decode"      # K = 3 x 512
     assert q4.select_kernel(2, 100, 96, 32) == "gemv"           # K not a multiple of 512
     assert q4.select_kernel(4, 100, 96, 32) == "gemm"
-    # above 16 rows: the decode kernel in 16-row launches up to 48 rows where every launch fits
+    # above 16 rows: the decode kernel in 16-row launches where every launch fits, up to 3 ... 6
+    # launches by the layer's size (28672 x 8192 and 11008 x 4096: 48 rows; 8192 x 8192 and
+    # 4096 x 4096: 64)
     assert q4.select_kernel(17, 28672, 8192, 128) == "decode"
-    assert q4.select_kernel(48, 4096, 4096, 128) == "decode"
-    assert q4.select_kernel(49, 4096, 4096, 128) == "gemm"
+    assert q4.select_kernel(48, 28672, 8192, 128) == "decode"
+    assert q4.select_kernel(49, 28672, 8192, 128) == "gemm"
+    assert q4.select_kernel(48, 11008, 4096, 128) == "decode"
+    assert q4.select_kernel(49, 11008, 4096, 128) == "gemm"
+    assert q4.select_kernel(64, 8192, 8192, 128) == "decode"
+    assert q4.select_kernel(65, 8192, 8192, 128) == "gemm"
+    assert q4.select_kernel(64, 4096, 4096, 128) == "decode"
+    assert q4.select_kernel(65, 4096, 4096, 128) == "gemm"
     assert q4.select_kernel(32, 8192, 8192, 32) == "gemm"       # g = 32: 16 rows do not fit
     assert q4.select_kernel(20, 4096, 8192, 32) == "gemm"       # nor the 4-row remainder
     assert q4.select_kernel(4, 100, 1024, 256) == "gemm"        # g above 128

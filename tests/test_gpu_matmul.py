@@ -252,7 +252,7 @@ def test_decode_shapes(M, N, K, g):
         _check_full(X_bits, W_bits, g, mode, "decode-shapes", kernels_for(M, N, K, g))
 
 
-@pytest.mark.parametrize("M", [17, 20, 32, 33, 48])
+@pytest.mark.parametrize("M", [17, 20, 32, 33, 48, 64, 95])
 @pytest.mark.parametrize("N,K,g", [(300, 2048, 128), (4096, 4096, 128), (129, 8192, 64), (70, 4096, 32)])
 def test_decode_in_row_chunks(M, N, K, g):
     """M > 16 through the decode kernel in 16-row launches (and the choice auto makes), every

@@ -64,18 +64,29 @@ bool decode_rows_fit(int64_t M, int64_t N, int64_t K, int32_t g) {
   return q4::decode_fits(16, N, K, g) && (M % 16 == 0 || q4::decode_fits(M % 16, N, K, g));
 }
 
-// Up to this many rows Q4_KERNEL_AUTO takes the decode kernel in 16-row launches, each of which
-// reads W once: at M = 32 two launches take 14 us on a 4096 x 4096 layer and 59 us on the
-// 70B-shaped one (28672 x 8192), where the GEMM takes about 47 and 96 us at any M up to 64; on
-// the 70B-shaped layer a fourth launch (about 120 us) would be behind the GEMM.
-constexpr int64_t kDecodeMaxRows = 48;
+// Up to how many rows Q4_KERNEL_AUTO takes the decode kernel in 16-row launches, each of which
+// reads W once, rather than the GEMM.  Below a few hundred rows the GEMM's time hardly depends
+// on M: its blocks walk all of K, about 0.0117 us per k on MI355X (47.5 us at K = 4096, 93-96 us
+// at K = 8192, M = 17 ... 384).  A decode launch is costed at 4.4 us, plus 0.001 us per k (its X
+// start-up), plus its weight bytes at 4.5 TB/s, which is at or above what was measured (7.1 us
+// for 4096 x 4096, 11.3 for 11008 x 4096, 16 for 8192 x 8192, 30 for 28672 x 8192).  So as many
+// launches as fit in the GEMM's time, at least three and at most six: 4096 x 4096 and 8192 x
+// 8192 at M = 64 take 28.4 and 63.8 us against 47.5 and 93.4 for the GEMM; 28672 x 8192 at
+// M = 32 / 48 59 / 90 us against 96.
+int64_t decode_max_rows(int64_t N, int64_t K, int32_t g) {
+  const double bytes = (double)N * (double)K * (0.5 + 3.0 / (double)g);
+  const double t_launch = 4.4 + 0.001 * (double)K + bytes / 4.5e6, t_gemm = 0.0117 * (double)K;   // us
+  int64_t n = (int64_t)(t_gemm / t_launch);
+  n = n < 3 ? 3 : (n > 6 ? 6 : n);
+  return 16 * n;
+}
 
 // Q4_KERNEL_AUTO: the decode kernels for small M, the GEMM otherwise.
 int auto_kernel(int64_t M, int64_t N, int64_t K, int32_t g) {
   if (M == 1 && gemv_fits(M, K)) return Q4_KERNEL_GEMV;
   if (q4::decode_fits(M, N, K, g)) return Q4_KERNEL_DECODE;
   if (gemv_fits(M, K)) return Q4_KERNEL_GEMV;
-  if (M <= kDecodeMaxRows && decode_rows_fit(M, N, K, g)) return Q4_KERNEL_DECODE;
+  if (M <= decode_max_rows(N, K, g) && decode_rows_fit(M, N, K, g)) return Q4_KERNEL_DECODE;
   return Q4_KERNEL_GEMM;
 }
 
