@@ -7,7 +7,8 @@
 // mixed-precision fma per weight and rounded once to bf16.
 //
 // Block = 4 waves, tile = 256 (or 128) rows of X x 256 rows of W, k walked in steps of 128;
-// shapes with too few such tiles to fill every compute unit take 128 x 128 tiles instead.
+// shapes with too few such tiles to fill every compute unit take 128 x 128 tiles instead, and
+// those with fewer than two of these per compute unit 128 x 64.
 //   * X: the block's 256 x 128 bf16 slice of each step is copied global -> LDS by the
 //     direct-to-LDS loads of gfx950 (no registers), double-buffered: the copy for step s + 1
 //     is issued at the start of step s.  Rows are XOR-swizzled in 16-byte chunks so that the
@@ -184,7 +185,8 @@ __device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int,
 // past M are clamped to row M - 1 and W rows past N read as 0 (their outputs are dropped).
 //
 // NBW: 16-row blocks of W per wave (4: 256-row W tiles; 2: 128-row tiles, for shapes whose
-// 256-row tiles would leave compute units idle).
+// 256-row tiles would leave compute units idle; 1: 64-row tiles, when 128-row tiles would not
+// give every compute unit two blocks, so that one block's loads overlap the other's work).
 // B: code width, 4 (W4A16) or 8 (W8A16).
 template <int TM, int NBW, bool SYM, bool EDGE, int B>
 __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel(
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     int edge_row, int vec_store) {
   static_assert(TM == kTileMSmall || TM == kTileMLarge, "tile of 128 or 256 X rows");
   constexpr int MB = TM / 16;                          // 16-row blocks of X
-  static_assert(NBW == 4 || (NBW == 2 && TM == kTileMSmall), "256-row W tiles, or 128-row with 128 X rows");
+  static_assert(NBW == 4 || ((NBW == 2 || NBW == 1) && TM == kTileMSmall), "256-row W tiles, or 128- or 64-row with 128 X rows");
   constexpr int NB = NBW;                              // 16-row blocks of W per wave
   constexpr int TN = 64 * NBW;                         // W rows per block
   constexpr int RPW = 16 * NBW;                        // W rows per wave
@@ -385,6 +387,10 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
     } else if constexpr (NB == 4) {
       asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][0][1]), "v"(wq[R][1][0]), "v"(wq[R][1][1]), "v"(wq[R][2][0]),
                    "v"(wq[R][2][1]), "v"(wq[R][3][0]), "v"(wq[R][3][1]));
+    } else if constexpr (NB == 1 && CW == 1) {
+      asm volatile("" ::"v"(wq[R][0][0]));
+    } else if constexpr (NB == 1) {
+      asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][0][1]));
     } else if constexpr (CW == 1) {
       asm volatile("" ::"v"(wq[R][0][0]), "v"(wq[R][1][0]));
     } else {
@@ -394,6 +400,9 @@ __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel
       if constexpr (NB == 4) {
         asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]), "v"(ws[R][2]), "v"(ws[R][3]));
         if constexpr (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]), "v"(wz[R][2]), "v"(wz[R][3]));
+      } else if constexpr (NB == 1) {
+        asm volatile("" ::"v"(ws[R][0]));
+        if constexpr (!SYM) asm volatile("" ::"v"(wz[R][0]));
       } else {
         asm volatile("" ::"v"(ws[R][0]), "v"(ws[R][1]));
         if constexpr (!SYM) asm volatile("" ::"v"(wz[R][0]), "v"(wz[R][1]));
@@ -700,6 +709,13 @@ hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, co
   const int64_t small_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + kTileN - 1) / kTileN);
   if (B == 4 && small_tiles >= 2 * (int64_t)num_cus)
     return launch_tm<kTileMSmall, 4, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
+  // Fewer 128 x 128 tiles than two per compute unit (small M: a block's time is its K loop, bound
+  // by its loads' latency): 128 x 64 tiles, twice as many blocks, two sharing a unit
+  // (70B-shaped layer M = 64 / 128: 96.8 / 102.6 -> 88.0 / 94.7 us; 8192^2 M = 128 / 256 / 384:
+  // 95.7 / 95.6 / 96.7 -> 71.0 / 71.5 / 79.9 us).
+  const int64_t half_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + 127) / 128);
+  if (half_tiles < 2 * (int64_t)num_cus)
+    return launch_tm<kTileMSmall, 1, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
   return launch_tm<kTileMSmall, 2, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
 }
 
