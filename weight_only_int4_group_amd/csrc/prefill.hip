@@ -8,7 +8,7 @@
 //
 // Block = 4 waves, tile = 256 (or 128) rows of X x 256 rows of W, k walked in steps of 128;
 // shapes with too few such tiles to fill every compute unit take 128 x 128 tiles instead, and
-// those with fewer than two of these per compute unit 128 x 64.
+// those with at most one of these per compute unit 128 x 64.
 //   * X: the block's 256 x 128 bf16 slice of each step is copied global -> LDS by the
 //     direct-to-LDS loads of gfx950 (no registers), double-buffered: the copy for step s + 1
 //     is issued at the start of step s.  Rows are XOR-swizzled in 16-byte chunks so that the
@@ -185,8 +185,8 @@ __device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int,
 // past M are clamped to row M - 1 and W rows past N read as 0 (their outputs are dropped).
 //
 // NBW: 16-row blocks of W per wave (4: 256-row W tiles; 2: 128-row tiles, for shapes whose
-// 256-row tiles would leave compute units idle; 1: 64-row tiles, when 128-row tiles would not
-// give every compute unit two blocks, so that one block's loads overlap the other's work).
+// 256-row tiles would leave compute units idle; 1: 64-row tiles, when 128-row tiles would give
+// a compute unit at most one block, so that two blocks' loads and work overlap).
 // B: code width, 4 (W4A16) or 8 (W8A16).
 template <int TM, int NBW, bool SYM, bool EDGE, int B>
 __global__ __launch_bounds__(256, TM == kTileMSmall ? 2 : 1) void prefill_kernel(
@@ -709,12 +709,14 @@ hipError_t launch_sym(const void* X, int64_t M, int64_t N, int64_t K, int lg, co
   const int64_t small_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + kTileN - 1) / kTileN);
   if (B == 4 && small_tiles >= 2 * (int64_t)num_cus)
     return launch_tm<kTileMSmall, 4, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
-  // Fewer 128 x 128 tiles than two per compute unit (small M: a block's time is its K loop, bound
-  // by its loads' latency): 128 x 64 tiles, twice as many blocks, two sharing a unit
-  // (70B-shaped layer M = 64 / 128: 96.8 / 102.6 -> 88.0 / 94.7 us; 8192^2 M = 128 / 256 / 384:
-  // 95.7 / 95.6 / 96.7 -> 71.0 / 71.5 / 79.9 us).
+  // At most one 128 x 128 tile per compute unit (small M: a block's time is its K loop, bound by
+  // its loads' latency): 128 x 64 tiles, twice as many blocks, two sharing a unit and all
+  // resident at once (70B-shaped layer M = 64 / 128: 96.8 / 102.6 -> 88.0 / 94.7 us; 8192^2
+  // M = 128 / 256 / 384 / 512: 95.7 / 95.6 / 96.7 / 96.8 -> 71.0 / 71.5 / 79.9 / 94.8 us).  With
+  // more, the 128 x 64 blocks would run in more than one round: 8192^2 M = 768 125.8 -> 160.7 us,
+  // the 70B-shaped layer M = 256 162.6 -> 185.7 us.
   const int64_t half_tiles = ((M + kTileMSmall - 1) / kTileMSmall) * ((N + 127) / 128);
-  if (half_tiles < 2 * (int64_t)num_cus)
+  if (half_tiles <= (int64_t)num_cus)
     return launch_tm<kTileMSmall, 1, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
   return launch_tm<kTileMSmall, 2, SYM, B>(X, M, N, K, lg, packed, scales, zeros, Y, stream);
 }
