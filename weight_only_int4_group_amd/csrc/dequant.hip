@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(
       const float sf = (float)__builtin_bit_cast(_Float16, k.s[j]);
       const float zf = SYM ? 8.0f : (float)k.z[j];
       const u32x4 v = convert8<Out>(w, sf, sf * zf);
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, 16 * (j * kWave + lane), 0, 0);
+      // streamed: every output byte is written once (70B-shaped weight: 112.2 -> 106.9 us)
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, 16 * (j * kWave + lane), 0, kBufferNT);
     }
   };
 
